@@ -1,0 +1,270 @@
+"""ISD / R-ISD / AR decoders: the per-slot state machine (oracle; test infrastructure only).
+
+What the pages fix (wiki note "Introspective Diffusion Language Models", *Key claims*
+and *Method*; Agentic Commons post, *How Introspective Strided Decoding Works*):
+one causal forward pass both proposes new tokens at MASK positions (distribution q)
+and re-scores the previously generated, still pending tokens under the anchor
+distribution p of the current pass; a pending token x is kept when u < p(x)/q(x);
+on the first rejection the block restarts from that position; position 1 is always
+accepted because of the logit shift; position k is accepted with probability
+p^(k-1); tokens per forward is (2 + p + ... + p^(N-2)) / (2 - p^(N-1)).
+
+Block layout (this build's reading; the only one consistent with the 2N-1 query rows
+of the pages' configurations, the TPF denominator 2 - p^(N-1) and the printed
+efficiency TPF^2 / queries-per-forward = 1.22 at N = 4, p = 0.9).  Per slot, with
+L = cached tokens and c = newest committed token (not yet cached):
+
+  A-state  rows [c, v_1 .. v_{N-1}, MASK x (N-1)] at positions L .. L+2N-2
+           for i = 1 .. N-1: p_i = softmax_T(row i-1);
+             Accept(v_i, p_i, q_i, u(slot,t,L+i,0)) -> commit v_i
+             else commit Resid(p_i, q_i, u(slot,t,L+i,1)); L += i; go to B; stop
+           all accepted: z_1 = Cat(softmax_T(row N-1), u(slot,t,L+N,1)), commit it;
+             proposals z_{j+1} from row N-1+j (j = 1..N-1) with u(slot,t,L+N+j,1);
+             L += N; stay in A with pending z_2 .. z_N
+  B-state  rows [c, MASK x (N-1)] at positions L .. L+N-1
+           z_1 from row 0 with u(slot,t,L+1,1), committed; proposals z_{j+1} from row j
+           with u(slot,t,L+1+j,1); L += 1; go to A
+  after every pass the cache keeps positions < L (MASK and rejected rows never persist)
+
+Proposals: 'sample' draws z ~ q = softmax_T(row); 'argmax' takes z = argmax(row) and
+q := delta_z (so acceptance is u < p(z) and the residual is p with z removed).
+T = 0 is greedy: every decision is an argmax (accept iff v_i == argmax p_i).
+N = 1 is plain AR decoding.  R-ISD is the same machine with the LoRA active on MASK
+rows.  A slot stops after exactly max_new generated tokens (the prefill's token
+counts); extra tokens of the last pass are dropped.
+"""
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import philox, sampler
+from .model import empty_cache, extend_cache
+from .paged_kv import PagePool
+
+STATE_A, STATE_B, STATE_DONE = "A", "B", "DONE"
+
+
+@dataclass
+class SlotState:
+    slot: int
+    committed: list                 # prompt + generated tokens
+    prompt_len: int
+    L: int                          # cached tokens
+    c: int                          # newest committed token (uncached)
+    pending: list = field(default_factory=list)
+    pending_q: list = field(default_factory=list)   # (w float32 [V], S) or None (delta q)
+    t: int = 1
+    state: str = STATE_B
+    max_new: int = 0
+    n_gen: int = 0
+    cache: list = None
+
+    @property
+    def generated(self):
+        return self.committed[self.prompt_len:]
+
+
+@dataclass
+class Decision:
+    kind: str        # 'accept', 'resid', 'z1', 'propose'
+    position: int
+    token: int
+    margin: float    # distance to the nearest flip (see sampler); inf when none applies
+    accepted: bool = True
+
+
+@dataclass
+class StepRecord:
+    slot: int
+    state: str
+    ids: list
+    positions: list
+    tokens: list
+    n_accept: int
+    decisions: list
+    logits: np.ndarray = None
+
+
+class Decoder:
+    def __init__(self, model, N, temperature, propose="sample", seed=1,
+                 page_size=16, n_pages=1 << 20, keep_logits=False):
+        assert N >= 1
+        self.m = model
+        self.spec = model.spec
+        self.N = int(N)
+        self.T = float(temperature)
+        self.propose = propose
+        self.seed = int(seed)
+        self.pool = PagePool(n_pages, page_size)
+        self.slots = {}
+        self.keep_logits = keep_logits
+        self.use_lora = model.lora is not None
+
+    # ---- decisions -------------------------------------------------------
+    def _u(self, slot, t, pos, purpose):
+        return philox.uniform(self.seed, slot, t, pos, purpose)
+
+    def _draw(self, logits, u):
+        """Sample (or argmax when T = 0) from softmax_T(logits): (token, margin)."""
+        if self.T == 0.0:
+            return sampler.argmax(logits), sampler.top2_gap(logits)
+        w, _, _ = sampler.weights_T(logits, self.T)
+        return sampler.cat(w, u)
+
+    def _propose(self, logits, u):
+        """(token, q-record, margin) for a MASK row."""
+        if self.T == 0.0:
+            return sampler.argmax(logits), None, sampler.top2_gap(logits)
+        if self.propose == "argmax":
+            return sampler.argmax(logits), None, sampler.top2_gap(logits)
+        w, S, _ = sampler.weights_T(logits, self.T)
+        j, margin = sampler.cat(w, u)
+        return j, (w, S), margin
+
+    # ---- prefill ---------------------------------------------------------
+    def prefill(self, slots, prompts, max_new):
+        """AR prefill of each prompt; returns the first generated token per slot."""
+        out = []
+        for slot, prompt, mx in zip(slots, prompts, max_new):
+            prompt = [int(x) for x in prompt]
+            L0 = len(prompt)
+            self.pool.truncate(slot, 0)
+            self.pool.reserve(slot, L0)
+            logits, kv = self.m.forward(prompt, np.arange(L0), empty_cache(self.spec))
+            z1, _ = self._draw(logits[-1], self._u(slot, 0, L0, philox.PURPOSE_DRAW))
+            st = SlotState(slot=slot, committed=prompt + [z1], prompt_len=L0, L=L0, c=z1,
+                           t=1, state=STATE_B, max_new=int(mx), n_gen=1,
+                           cache=extend_cache(empty_cache(self.spec), kv, L0))
+            if st.n_gen >= st.max_new:
+                st.state = STATE_DONE
+                self.pool.truncate(slot, 0)
+            self.slots[slot] = st
+            out.append(z1)
+        return out
+
+    # ---- one pass --------------------------------------------------------
+    def rows_of(self, st):
+        N, MASK = self.N, self.spec.mask_id
+        if st.state == STATE_A:
+            ids = [st.c] + list(st.pending) + [MASK] * (N - 1)
+        else:
+            ids = [st.c] + [MASK] * (N - 1)
+        is_mask = np.array([i == MASK for i in ids])
+        return ids, is_mask
+
+    def step(self):
+        """One ISD pass over every live slot (ascending slot order). Returns {slot: StepRecord}."""
+        live = sorted(s for s, st in self.slots.items() if st.state in (STATE_A, STATE_B))
+        rows = {}
+        for s in live:
+            st = self.slots[s]
+            ids, is_mask = self.rows_of(st)
+            rows[s] = (ids, is_mask)
+            self.pool.reserve(s, st.L + len(ids))
+        recs = {}
+        for s in live:
+            recs[s] = self._step_slot(self.slots[s], *rows[s])
+        for s in live:
+            st = self.slots[s]
+            self.pool.truncate(s, st.L if st.state != STATE_DONE else 0)
+        return recs
+
+    def _step_slot(self, st, ids, is_mask):
+        N, t, L, slot = self.N, st.t, st.L, st.slot
+        pos = L + np.arange(len(ids))
+        logits, kv = self.m.forward(ids, pos, st.cache, is_mask=is_mask if self.use_lora else None)
+        dec = []
+        tokens = []
+        n_acc = 0
+        state_before = st.state
+        if st.state == STATE_A:
+            rejected = False
+            for i in range(1, N):
+                v = st.pending[i - 1]
+                row = logits[i - 1]
+                if self.T == 0.0:
+                    a = sampler.argmax(row)
+                    ok, margin = (v == a), sampler.top2_gap(row)
+                else:
+                    w, S, _ = sampler.weights_T(row, self.T)
+                    px = float(w[v]) / S
+                    qrec = st.pending_q[i - 1]
+                    qx = 1.0 if qrec is None else float(qrec[0][v]) / qrec[1]
+                    ok, margin = sampler.accept(px, qx, self._u(slot, t, L + i, philox.PURPOSE_ACCEPT))
+                dec.append(Decision("accept", L + i, v, margin, ok))
+                if ok:
+                    tokens.append(v)
+                    n_acc += 1
+                    continue
+                # first rejection: residual resample at position L+i, restart from there
+                if self.T == 0.0:
+                    r, rm = sampler.argmax(row), sampler.top2_gap(row)
+                else:
+                    p = w.astype(np.float64) / S
+                    if qrec is None:
+                        q = np.zeros_like(p)
+                        q[v] = 1.0
+                    else:
+                        q = qrec[0].astype(np.float64) / qrec[1]
+                    r, rm = sampler.resid_draw(p, q, self._u(slot, t, L + i, philox.PURPOSE_DRAW))
+                dec.append(Decision("resid", L + i, r, rm))
+                tokens.append(r)
+                rejected = True
+                new_L, new_c = L + i, r
+                new_state, new_pending, new_q = STATE_B, [], []
+                break
+            if not rejected:
+                z1, m1 = self._draw(logits[N - 1], self._u(slot, t, L + N, philox.PURPOSE_DRAW))
+                dec.append(Decision("z1", L + N, z1, m1))
+                tokens.append(z1)
+                new_pending, new_q = [], []
+                for j in range(1, N):
+                    z, qrec, mz = self._propose(logits[N - 1 + j],
+                                                self._u(slot, t, L + N + j, philox.PURPOSE_DRAW))
+                    dec.append(Decision("propose", L + N + j, z, mz))
+                    new_pending.append(z)
+                    new_q.append(qrec)
+                new_L, new_c, new_state = L + N, z1, STATE_A
+        else:
+            z1, m1 = self._draw(logits[0], self._u(slot, t, L + 1, philox.PURPOSE_DRAW))
+            dec.append(Decision("z1", L + 1, z1, m1))
+            tokens.append(z1)
+            new_pending, new_q = [], []
+            for j in range(1, N):
+                z, qrec, mz = self._propose(logits[j], self._u(slot, t, L + 1 + j, philox.PURPOSE_DRAW))
+                dec.append(Decision("propose", L + 1 + j, z, mz))
+                new_pending.append(z)
+                new_q.append(qrec)
+            new_L, new_c, new_state = L + 1, z1, STATE_A
+
+        # the KV of c and of the accepted pending tokens persists; the rest is rolled back
+        keep = new_L - L
+        st.cache = extend_cache(st.cache, kv, keep)
+        room = st.max_new - st.n_gen
+        tokens = tokens[:room]
+        st.committed.extend(tokens)
+        st.n_gen += len(tokens)
+        st.L, st.c, st.t = new_L, new_c, t + 1
+        st.pending, st.pending_q, st.state = new_pending, new_q, new_state
+        if st.n_gen >= st.max_new:
+            st.state = STATE_DONE
+            st.pending, st.pending_q = [], []
+        return StepRecord(slot, state_before, list(ids), list(pos), tokens, n_acc, dec,
+                          logits if self.keep_logits else None)
+
+    def run(self, max_steps=1 << 30):
+        steps = 0
+        while steps < max_steps and any(st.state != STATE_DONE for st in self.slots.values()):
+            self.step()
+            steps += 1
+        return steps
+
+
+def ar_greedy_reference(model, prompt, n_new):
+    """Plain AR greedy decoding by full recomputation (no cache, no blocks): the
+    definition the ISD greedy decoder must reproduce."""
+    seq = [int(x) for x in prompt]
+    for _ in range(n_new):
+        logits, _ = model.forward(seq, np.arange(len(seq)), empty_cache(model.spec))
+        seq.append(sampler.argmax(logits[-1]))
+    return seq[len(prompt):]
