@@ -1,0 +1,252 @@
+/*
+ * isd.h - C ABI of the MI355X (gfx950) Introspective Strided Decoding library (libisd.so).
+ *
+ * Introspective Strided Decoding (ISD) is the decode step of a diffusion language model
+ * whose attention stays strictly causal: one forward pass proposes new tokens at MASK
+ * positions (distribution q) and re-scores the previously proposed, still pending tokens
+ * under the anchor distribution p of the same pass; a pending token x is kept when
+ * u < p(x)/q(x), and on the first rejection the block restarts from that position
+ * (Bud's Wiki note "Introspective Diffusion Language Models", sections Key claims and
+ * Method; Agentic Commons post of the same title, section "How Introspective Strided
+ * Decoding Works").  R-ISD adds a rank-r LoRA that is active only at MASK positions, so
+ * verify positions keep the base weights and the output equals the base AR model's
+ * (wiki note, Key claims; GeekNews summaries, section Lossless R-ISD).
+ *
+ * Conventions for every call:
+ *  - Pointers named "device" are device (HBM) addresses on the current HIP device,
+ *    "host" are host addresses.  The library allocates NO device memory: weights, the KV
+ *    pool, the workspace and all outputs belong to the caller and must stay valid for the
+ *    lifetime of the context.  isd_release frees host metadata only.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Calls enqueue
+ *    work on it and return; outputs are valid once the stream has completed that work.
+ *    A context is not thread-safe; use one stream per context.
+ *  - Host-side validation failures return a negative isd_status synchronously and enqueue
+ *    nothing.  Device-side conditions (non-finite logits) are recorded per slot in
+ *    isd_slot.status; isd_get_status() reads the sticky context status (it synchronizes
+ *    the stream).
+ *  - Matrices are row-major.  "act" is the activation/storage type of the context:
+ *    bfloat16 (ISD_BF16) or float (ISD_F32).  Weight matrices are stored out x in
+ *    (y = x W^T).
+ */
+#ifndef ISD_H
+#define ISD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ISD_MAX_STRIDE 8          /* largest supported stride N */
+
+typedef enum {
+  ISD_OK = 0,
+  ISD_E_ARG = -1,        /* NULL pointer, bad enum value, out-of-range scalar */
+  ISD_E_SHAPE = -2,      /* model/config shape the kernels do not support */
+  ISD_E_CAPACITY = -3,   /* KV page pool, prefill row budget or batch too small */
+  ISD_E_STATE = -4,      /* call not valid in the context's current state */
+  ISD_E_HIP = -5,        /* a HIP runtime call failed */
+  ISD_E_NONFINITE = -6   /* non-finite logits were seen by the sampler (sticky) */
+} isd_status;
+
+enum { ISD_F32 = 0, ISD_BF16 = 1 };
+enum { ISD_PROPOSE_SAMPLE = 0, ISD_PROPOSE_ARGMAX = 1 };
+enum { ISD_SLOT_EMPTY = 0, ISD_SLOT_A = 1, ISD_SLOT_B = 2, ISD_SLOT_DONE = 3 };
+
+/* Model + decoding configuration.
+ * Model: pre-norm causal decoder (RMSNorm, RoPE rotate-half with base rope_base, grouped
+ * query attention, SwiGLU FFN, untied LM head, no biases).  The MASK token id is `vocab`
+ * and indexes row `vocab` of the (vocab+1)-row embedding table.
+ * Decoding: stride_n = N (1 = plain AR); temperature 0 = greedy; `propose` selects how the
+ * MASK rows propose (sample from q, or argmax with q := delta); seed keys the Philox4x32-10
+ * stream u(slot, t, position, purpose). */
+typedef struct {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ffn, vocab;
+  float rope_base, rms_eps;
+  int32_t dtype;               /* ISD_F32 | ISD_BF16 */
+  int32_t stride_n;            /* 1 .. ISD_MAX_STRIDE */
+  int32_t page_size;           /* tokens per KV page: 16 */
+  int32_t max_batch;           /* number of slots */
+  int32_t max_seq_len;         /* prompt + generated tokens of any slot */
+  int32_t n_pages;             /* pages in the KV pool */
+  int32_t max_prefill_tokens;  /* largest sum of prompt lengths of one isd_prefill call */
+  int32_t lora_rank;           /* 0 = ISD, >0 = R-ISD gated LoRA of that rank (multiple of 64) */
+  int32_t propose;             /* ISD_PROPOSE_SAMPLE | ISD_PROPOSE_ARGMAX */
+  float temperature;           /* >= 0 */
+  uint64_t seed;
+} isd_config;
+
+/* Device pointers of the weights (act type).  The per-layer fields are HOST arrays of
+ * n_layers device pointers; they are copied by isd_init.
+ *   embed [vocab+1, d]      final_norm [d]        lm_head [vocab, d]
+ *   attn_norm[l] [d]        wqkv[l] [(Hq+2Hkv)*hd, d] (q rows, then k, then v)
+ *   wo[l] [d, Hq*hd]        ffn_norm[l] [d]
+ *   wg[l], wu[l] [F, d]     wd[l] [d, F]
+ *   lora_a[l*7+m] [r, d_in_m], lora_b[l*7+m] [d_out_m, r] for m = q,k,v,o,g,u,d
+ *   (HOST arrays of n_layers*7 device pointers; NULL when lora_rank == 0). */
+typedef struct {
+  const void* embed;
+  const void* final_norm;
+  const void* lm_head;
+  const void* const* attn_norm;
+  const void* const* wqkv;
+  const void* const* wo;
+  const void* const* ffn_norm;
+  const void* const* wg;
+  const void* const* wu;
+  const void* const* wd;
+  const void* const* lora_a;
+  const void* const* lora_b;
+} isd_weights;
+
+typedef struct {
+  size_t kv_pool_bytes;    /* K pool then V pool, every layer */
+  size_t workspace_bytes;  /* activations, logits, sampler state, page tables, slots */
+} isd_sizes;
+
+/* Per-slot device state (array of max_batch in the workspace; layout fixed, 128 bytes). */
+typedef struct {
+  int32_t state;                         /* ISD_SLOT_* */
+  int32_t L;                             /* cached tokens (positions 0 .. L-1 in the pages) */
+  int32_t c;                             /* newest committed token, not yet cached */
+  int32_t t;                             /* pass counter of the Philox stream (prefill = 0) */
+  int32_t n_gen, max_new;                /* generated tokens so far / stop after max_new */
+  int32_t n_pages;                       /* pages in this slot's page table */
+  int32_t status;                        /* 0 or ISD_E_NONFINITE */
+  int32_t pending[ISD_MAX_STRIDE - 1];   /* v_1 .. v_{N-1} awaiting verification (state A) */
+  int32_t q_row[ISD_MAX_STRIDE - 1];     /* logits row (previous pass) that proposed pending[i];
+                                            -1: delta q (argmax proposal) */
+  int32_t passes, accepted, verified, committed;   /* cumulative counters */
+  int32_t pad[2];
+} isd_slot;
+
+typedef struct isd_ctx isd_ctx;
+
+/* Device addresses of the context's internal buffers (for tests and benchmarks). */
+typedef struct {
+  isd_slot* slots;          /* [max_batch] */
+  int32_t* page_table;      /* [max_batch, max_pages_per_slot] */
+  int32_t max_pages_per_slot;
+  int32_t* free_stack;      /* [n_pages], entries 0 .. n_free-1 */
+  int32_t* n_free;          /* [1] */
+  float* logits;            /* logits of the last pass: [max_batch * (2N-1), vocab] fp32;
+                               row b*(2N-1)+i is row i of slot b's block */
+  int32_t rows_per_slot;    /* 2N-1 */
+  int32_t* row_token;       /* [max_batch*(2N-1)] input token of each row of the last pass */
+  int32_t* row_pos;         /* [max_batch*(2N-1)] position (-1 for a dead row) */
+  void* k_pool;             /* [n_layers][n_pages][Hkv][P][hd] act */
+  void* v_pool;             /* [n_layers][n_pages][Hkv][hd][P] act (transposed within a page) */
+  void* attn_out;           /* last layer's attention output of the last pass [rows, Hq*hd] act */
+} isd_buffers;
+
+/* Create a context.  With kv_pool == workspace == NULL only `sizes` is filled (size query)
+ * and *out is set to NULL.  Otherwise kv_pool/workspace must hold at least the queried
+ * sizes (256-byte aligned) and set-up kernels (free stack, slot reset, RoPE tables) are
+ * enqueued on `stream`.  Errors: ISD_E_ARG (NULL cfg/w/sizes/out, bad enum), ISD_E_SHAPE
+ * (unsupported dims: head_dim must be 128 for bf16 and <= 256 for f32, Hq a multiple of
+ * Hkv, d/F/qkv widths multiples of 64 for bf16), ISD_E_HIP. */
+isd_status isd_init(const isd_config* cfg, const isd_weights* w, void* kv_pool, void* workspace,
+                    isd_sizes* sizes, isd_ctx** out, void* stream);
+
+/* Prefill n slots with their prompts (an ordinary causal AR prefill, the pages' "AR-compatible
+ * serving"), sample each slot's first token from the last prompt row with
+ * u(slot, 0, prompt_len, 1), and put the slot in state B (DONE if max_new <= 1).
+ *   slots      host [n]   distinct slot ids in [0, max_batch)
+ *   prompt_ids device [offsets[n]] int32 tokens in [0, vocab), prompts packed back to back
+ *   offsets    host [n+1] prompt i is prompt_ids[offsets[i] .. offsets[i+1]), length >= 1
+ *   max_new    host [n]   tokens to generate (>= 1), including the first token
+ *   first_tok  device [n] int32 out: the first generated token of each slot
+ * Pages: in call order each slot frees its old pages then takes ceil(len/P) pages.
+ * Admission: ceil((len + max_new + 2N)/P) pages are reserved per slot so that isd_step can
+ * never run out; ISD_E_CAPACITY when the reservations exceed the pool, when offsets[n] >
+ * max_prefill_tokens or len + max_new + 2N > max_seq_len.  ISD_E_ARG on bad slots/lengths. */
+isd_status isd_prefill(isd_ctx* ctx, int32_t n, const int32_t* slots, const int32_t* prompt_ids,
+                       const int32_t* offsets, const int32_t* max_new, int32_t* first_tok,
+                       void* stream);
+
+/* One ISD pass over every live slot (state A or B): assemble the block rows from device
+ * state, reserve KV pages, run the causal forward (LoRA on MASK rows when lora_rank > 0),
+ * verify / accept / resample / propose, and roll the KV cache back to the committed length.
+ *   tokens   device [max_batch, N] int32 out: tokens committed this pass (-1 padded)
+ *   n_commit device [max_batch]    int32 out: number of tokens committed this pass
+ *   n_accept device [max_batch]    int32 out: pending tokens accepted this pass
+ * Slots that are EMPTY or DONE commit nothing.  No host synchronization happens inside.
+ * Errors: ISD_E_STATE if no slot was ever prefilled, ISD_E_ARG on NULL outputs. */
+isd_status isd_step(isd_ctx* ctx, int32_t* tokens, int32_t* n_commit, int32_t* n_accept,
+                    void* stream);
+
+/* Device addresses of internal buffers (see isd_buffers). */
+isd_status isd_get_buffers(const isd_ctx* ctx, isd_buffers* out);
+
+/* Synchronize `stream` and return the sticky device status (ISD_OK or ISD_E_NONFINITE). */
+isd_status isd_get_status(isd_ctx* ctx, void* stream);
+
+/* Free the host-side context. */
+isd_status isd_release(isd_ctx* ctx);
+
+/* ---------------------------------------------------------------------------------------
+ * Kernel-level entry points (used by the attention + acceptance microbench).
+ * ------------------------------------------------------------------------------------- */
+
+/* Paged causal attention of blocks of query rows (wiki note, TL;DR: attention stays strictly
+ * causal; the block's own keys are read from the pages, as a paged-only kernel does).
+ *   q          device [B, R, Hq, hd] bf16, query rows after RoPE; row i of sequence b sits
+ *              at position ctx_len[b] - q_len[b] + i
+ *   k_pool     device [n_pages, Hkv, P, hd] bf16;  v_pool device [n_pages, Hkv, hd, P] bf16
+ *   page_table device [B, max_pages] int32;  ctx_len, q_len device [B] int32
+ *              (keys 0 .. ctx_len-1 are in the pages; q_len <= R)
+ *   out        device [B, R, Hq, hd] bf16 (rows >= q_len are written as zeros)
+ *   workspace  device, at least isd_attn_workspace_bytes(...) bytes
+ * head_dim must be 128, page_size 16, Hq/Hkv * R <= 64.  Errors: ISD_E_ARG, ISD_E_SHAPE. */
+typedef struct {
+  int32_t batch, rows, n_q_heads, n_kv_heads, head_dim, page_size, max_pages, max_ctx;
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* page_table;
+  const int32_t* ctx_len;
+  const int32_t* q_len;
+  void* out;
+  void* workspace;
+} isd_attn_args;
+
+size_t isd_attn_workspace_bytes(const isd_attn_args* a);
+isd_status isd_attn_paged(const isd_attn_args* a, void* stream);
+
+/* The fused vocabulary-wide acceptance step for a batch of slots, as inside isd_step
+ * (wiki note, Method: accept when u < p(x)/q(x); Agentic Commons, "How Introspective
+ * Strided Decoding Works": speculative-sampling rule; residual draw from
+ * normalize(max(0, p - q)) on the first rejection).
+ *   slots      device [B] isd_slot, in/out (state machine as in isd_step; L, c, t advance)
+ *   logits     device [B, R, V] fp32, the current pass (R = 2N-1 rows per slot)
+ *   q_logits   device [B*R', V] fp32 rows named by slots[b].q_row (the previous pass),
+ *              may be NULL in argmax mode
+ *   q_rows     number of rows of q_logits (bounds check of q_row)
+ *   tokens/n_commit/n_accept  device outputs as in isd_step
+ *   workspace  device, at least isd_sample_workspace_bytes(B, R, V, q_rows) bytes
+ * The slot ids used in the Philox counters are the array indices b.  Page tables are not
+ * touched.  Errors: ISD_E_ARG. */
+typedef struct {
+  int32_t batch, stride_n, vocab, propose, q_rows;
+  float temperature;
+  uint64_t seed;
+  isd_slot* slots;
+  const float* logits;
+  const float* q_logits;
+  int32_t* tokens;
+  int32_t* n_commit;
+  int32_t* n_accept;
+  void* workspace;
+} isd_sample_args;
+
+size_t isd_sample_workspace_bytes(int32_t batch, int32_t rows, int32_t vocab, int32_t q_rows);
+isd_status isd_sample(const isd_sample_args* a, void* stream);
+
+/* Library version string. */
+const char* isd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ISD_H */

@@ -85,6 +85,99 @@ class StepRecord:
     logits: np.ndarray = None
 
 
+@dataclass
+class Outcome:
+    tokens: list
+    n_accept: int
+    decisions: list
+    new_L: int
+    new_c: int
+    new_state: str
+    new_pending: list
+    new_q: list
+
+
+def draw(logits, u, T):
+    """Sample (or argmax when T = 0) from softmax_T(logits): (token, margin)."""
+    if T == 0.0:
+        return sampler.argmax(logits), sampler.top2_gap(logits)
+    w, _, _ = sampler.weights_T(logits, T)
+    return sampler.cat(w, u)
+
+
+def propose_token(logits, u, T, propose):
+    """(token, q-record, margin) for a MASK row; q-record None means q = delta(token)."""
+    if T == 0.0 or propose == "argmax":
+        return sampler.argmax(logits), None, sampler.top2_gap(logits)
+    w, S, _ = sampler.weights_T(logits, T)
+    j, margin = sampler.cat(w, u)
+    return j, (w, S), margin
+
+
+def decide(state, L, t, slot, pending, pending_q, logits, N, T, propose, seed):
+    """The decisions of one pass of one slot, given the pass's logits rows.
+
+    state 'A': rows [c, v_1 .. v_{N-1}, MASK x (N-1)]; 'B': rows [c, MASK x (N-1)].
+    pending_q[i] is (w, S) of the MASK row that proposed pending[i], or None (delta q).
+    Returns an Outcome (tokens committed in order, accepted count, decisions with margins,
+    and the slot's next L, c, state, pending tokens and their q records).
+    """
+    u = lambda pos, purpose: philox.uniform(seed, slot, t, pos, purpose)
+    dec, tokens = [], []
+    n_acc = 0
+    if state == STATE_A:
+        for i in range(1, N):
+            v = pending[i - 1]
+            row = logits[i - 1]
+            qrec = pending_q[i - 1] if pending_q else None
+            if T == 0.0:
+                ok, margin = (v == sampler.argmax(row)), sampler.top2_gap(row)
+            else:
+                w, S, _ = sampler.weights_T(row, T)
+                px = float(w[v]) / S
+                qx = 1.0 if qrec is None else float(qrec[0][v]) / qrec[1]
+                ok, margin = sampler.accept(px, qx, u(L + i, philox.PURPOSE_ACCEPT))
+            dec.append(Decision("accept", L + i, v, margin, ok))
+            if ok:
+                tokens.append(v)
+                n_acc += 1
+                continue
+            # first rejection: residual resample at position L+i, restart from there
+            if T == 0.0:
+                r, rm = sampler.argmax(row), sampler.top2_gap(row)
+            else:
+                p = w.astype(np.float64) / S
+                if qrec is None:
+                    q = np.zeros_like(p)
+                    q[v] = 1.0
+                else:
+                    q = qrec[0].astype(np.float64) / qrec[1]
+                r, rm = sampler.resid_draw(p, q, u(L + i, philox.PURPOSE_DRAW))
+            dec.append(Decision("resid", L + i, r, rm))
+            tokens.append(r)
+            return Outcome(tokens, n_acc, dec, L + i, r, STATE_B, [], [])
+        z1, m1 = draw(logits[N - 1], u(L + N, philox.PURPOSE_DRAW), T)
+        dec.append(Decision("z1", L + N, z1, m1))
+        tokens.append(z1)
+        new_pending, new_q = [], []
+        for j in range(1, N):
+            z, qrec, mz = propose_token(logits[N - 1 + j], u(L + N + j, philox.PURPOSE_DRAW), T, propose)
+            dec.append(Decision("propose", L + N + j, z, mz))
+            new_pending.append(z)
+            new_q.append(qrec)
+        return Outcome(tokens, n_acc, dec, L + N, z1, STATE_A, new_pending, new_q)
+    z1, m1 = draw(logits[0], u(L + 1, philox.PURPOSE_DRAW), T)
+    dec.append(Decision("z1", L + 1, z1, m1))
+    tokens.append(z1)
+    new_pending, new_q = [], []
+    for j in range(1, N):
+        z, qrec, mz = propose_token(logits[j], u(L + 1 + j, philox.PURPOSE_DRAW), T, propose)
+        dec.append(Decision("propose", L + 1 + j, z, mz))
+        new_pending.append(z)
+        new_q.append(qrec)
+    return Outcome(tokens, n_acc, dec, L + 1, z1, STATE_A, new_pending, new_q)
+
+
 class Decoder:
     def __init__(self, model, N, temperature, propose="sample", seed=1,
                  page_size=16, n_pages=1 << 20, keep_logits=False):
@@ -100,36 +193,27 @@ class Decoder:
         self.keep_logits = keep_logits
         self.use_lora = model.lora is not None
 
-    # ---- decisions -------------------------------------------------------
     def _u(self, slot, t, pos, purpose):
         return philox.uniform(self.seed, slot, t, pos, purpose)
 
     def _draw(self, logits, u):
-        """Sample (or argmax when T = 0) from softmax_T(logits): (token, margin)."""
-        if self.T == 0.0:
-            return sampler.argmax(logits), sampler.top2_gap(logits)
-        w, _, _ = sampler.weights_T(logits, self.T)
-        return sampler.cat(w, u)
-
-    def _propose(self, logits, u):
-        """(token, q-record, margin) for a MASK row."""
-        if self.T == 0.0:
-            return sampler.argmax(logits), None, sampler.top2_gap(logits)
-        if self.propose == "argmax":
-            return sampler.argmax(logits), None, sampler.top2_gap(logits)
-        w, S, _ = sampler.weights_T(logits, self.T)
-        j, margin = sampler.cat(w, u)
-        return j, (w, S), margin
+        return draw(logits, u, self.T)
 
     # ---- prefill ---------------------------------------------------------
     def prefill(self, slots, prompts, max_new):
-        """AR prefill of each prompt; returns the first generated token per slot."""
+        """AR prefill of each prompt; returns the first generated token per slot.
+
+        Page order: first, slot by slot in call order, free the slot's old pages and
+        reserve the prompt's; then forward and draw; last, free the pages of slots that
+        are already finished (max_new <= 1), in call order.
+        """
         out = []
+        for slot, prompt in zip(slots, prompts):
+            self.pool.truncate(slot, 0)
+            self.pool.reserve(slot, len(prompt))
         for slot, prompt, mx in zip(slots, prompts, max_new):
             prompt = [int(x) for x in prompt]
             L0 = len(prompt)
-            self.pool.truncate(slot, 0)
-            self.pool.reserve(slot, L0)
             logits, kv = self.m.forward(prompt, np.arange(L0), empty_cache(self.spec))
             z1, _ = self._draw(logits[-1], self._u(slot, 0, L0, philox.PURPOSE_DRAW))
             st = SlotState(slot=slot, committed=prompt + [z1], prompt_len=L0, L=L0, c=z1,
@@ -137,9 +221,11 @@ class Decoder:
                            cache=extend_cache(empty_cache(self.spec), kv, L0))
             if st.n_gen >= st.max_new:
                 st.state = STATE_DONE
-                self.pool.truncate(slot, 0)
             self.slots[slot] = st
             out.append(z1)
+        for slot in slots:
+            if self.slots[slot].state == STATE_DONE:
+                self.pool.truncate(slot, 0)
         return out
 
     # ---- one pass --------------------------------------------------------
@@ -173,69 +259,11 @@ class Decoder:
         N, t, L, slot = self.N, st.t, st.L, st.slot
         pos = L + np.arange(len(ids))
         logits, kv = self.m.forward(ids, pos, st.cache, is_mask=is_mask if self.use_lora else None)
-        dec = []
-        tokens = []
-        n_acc = 0
         state_before = st.state
-        if st.state == STATE_A:
-            rejected = False
-            for i in range(1, N):
-                v = st.pending[i - 1]
-                row = logits[i - 1]
-                if self.T == 0.0:
-                    a = sampler.argmax(row)
-                    ok, margin = (v == a), sampler.top2_gap(row)
-                else:
-                    w, S, _ = sampler.weights_T(row, self.T)
-                    px = float(w[v]) / S
-                    qrec = st.pending_q[i - 1]
-                    qx = 1.0 if qrec is None else float(qrec[0][v]) / qrec[1]
-                    ok, margin = sampler.accept(px, qx, self._u(slot, t, L + i, philox.PURPOSE_ACCEPT))
-                dec.append(Decision("accept", L + i, v, margin, ok))
-                if ok:
-                    tokens.append(v)
-                    n_acc += 1
-                    continue
-                # first rejection: residual resample at position L+i, restart from there
-                if self.T == 0.0:
-                    r, rm = sampler.argmax(row), sampler.top2_gap(row)
-                else:
-                    p = w.astype(np.float64) / S
-                    if qrec is None:
-                        q = np.zeros_like(p)
-                        q[v] = 1.0
-                    else:
-                        q = qrec[0].astype(np.float64) / qrec[1]
-                    r, rm = sampler.resid_draw(p, q, self._u(slot, t, L + i, philox.PURPOSE_DRAW))
-                dec.append(Decision("resid", L + i, r, rm))
-                tokens.append(r)
-                rejected = True
-                new_L, new_c = L + i, r
-                new_state, new_pending, new_q = STATE_B, [], []
-                break
-            if not rejected:
-                z1, m1 = self._draw(logits[N - 1], self._u(slot, t, L + N, philox.PURPOSE_DRAW))
-                dec.append(Decision("z1", L + N, z1, m1))
-                tokens.append(z1)
-                new_pending, new_q = [], []
-                for j in range(1, N):
-                    z, qrec, mz = self._propose(logits[N - 1 + j],
-                                                self._u(slot, t, L + N + j, philox.PURPOSE_DRAW))
-                    dec.append(Decision("propose", L + N + j, z, mz))
-                    new_pending.append(z)
-                    new_q.append(qrec)
-                new_L, new_c, new_state = L + N, z1, STATE_A
-        else:
-            z1, m1 = self._draw(logits[0], self._u(slot, t, L + 1, philox.PURPOSE_DRAW))
-            dec.append(Decision("z1", L + 1, z1, m1))
-            tokens.append(z1)
-            new_pending, new_q = [], []
-            for j in range(1, N):
-                z, qrec, mz = self._propose(logits[j], self._u(slot, t, L + 1 + j, philox.PURPOSE_DRAW))
-                dec.append(Decision("propose", L + 1 + j, z, mz))
-                new_pending.append(z)
-                new_q.append(qrec)
-            new_L, new_c, new_state = L + 1, z1, STATE_A
+        out = decide(st.state, L, t, slot, st.pending, st.pending_q, logits, N, self.T, self.propose, self.seed)
+        tokens, n_acc, dec = out.tokens, out.n_accept, out.decisions
+        new_L, new_c, new_state = out.new_L, out.new_c, out.new_state
+        new_pending, new_q = out.new_pending, out.new_q
 
         # the KV of c and of the accepted pending tokens persists; the rest is rolled back
         keep = new_L - L

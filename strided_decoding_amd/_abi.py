@@ -1,0 +1,118 @@
+"""ctypes mirror of include/isd.h and the loader of libisd.so.
+
+The library is required: importing this module on a machine without the built
+libisd.so raises, there is no fallback implementation.
+"""
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libisd.so")
+
+ISD_MAX_STRIDE = 8
+ISD_OK, ISD_E_ARG, ISD_E_SHAPE, ISD_E_CAPACITY, ISD_E_STATE, ISD_E_HIP, ISD_E_NONFINITE = 0, -1, -2, -3, -4, -5, -6
+STATUS_NAMES = {0: "ISD_OK", -1: "ISD_E_ARG", -2: "ISD_E_SHAPE", -3: "ISD_E_CAPACITY", -4: "ISD_E_STATE",
+                -5: "ISD_E_HIP", -6: "ISD_E_NONFINITE"}
+ISD_F32, ISD_BF16 = 0, 1
+ISD_PROPOSE_SAMPLE, ISD_PROPOSE_ARGMAX = 0, 1
+ISD_SLOT_EMPTY, ISD_SLOT_A, ISD_SLOT_B, ISD_SLOT_DONE = 0, 1, 2, 3
+
+# symbols the header declares (checked by the CPU test-suite)
+EXPORTS = ("isd_init", "isd_prefill", "isd_step", "isd_get_buffers", "isd_get_status", "isd_release",
+           "isd_attn_workspace_bytes", "isd_attn_paged", "isd_sample_workspace_bytes", "isd_sample",
+           "isd_version")
+
+
+class IsdError(RuntimeError):
+    def __init__(self, where, code):
+        super().__init__(f"{where} failed: {STATUS_NAMES.get(code, code)}")
+        self.code = code
+
+
+class Config(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("d_model", C.c_int32), ("n_q_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("d_ffn", C.c_int32), ("vocab", C.c_int32),
+                ("rope_base", C.c_float), ("rms_eps", C.c_float), ("dtype", C.c_int32), ("stride_n", C.c_int32),
+                ("page_size", C.c_int32), ("max_batch", C.c_int32), ("max_seq_len", C.c_int32),
+                ("n_pages", C.c_int32), ("max_prefill_tokens", C.c_int32), ("lora_rank", C.c_int32),
+                ("propose", C.c_int32), ("temperature", C.c_float), ("seed", C.c_uint64)]
+
+
+PP = C.POINTER(C.c_void_p)
+
+
+class Weights(C.Structure):
+    _fields_ = [("embed", C.c_void_p), ("final_norm", C.c_void_p), ("lm_head", C.c_void_p),
+                ("attn_norm", PP), ("wqkv", PP), ("wo", PP), ("ffn_norm", PP), ("wg", PP), ("wu", PP),
+                ("wd", PP), ("lora_a", PP), ("lora_b", PP)]
+
+
+class Sizes(C.Structure):
+    _fields_ = [("kv_pool_bytes", C.c_size_t), ("workspace_bytes", C.c_size_t)]
+
+
+SLOT_INTS = 32   # isd_slot is 32 int32 words
+SLOT_FIELDS = ["state", "L", "c", "t", "n_gen", "max_new", "n_pages", "status"] + \
+    [f"pending{i}" for i in range(ISD_MAX_STRIDE - 1)] + [f"q_row{i}" for i in range(ISD_MAX_STRIDE - 1)] + \
+    ["passes", "accepted", "verified", "committed", "pad0", "pad1"]
+
+
+class Buffers(C.Structure):
+    _fields_ = [("slots", C.c_void_p), ("page_table", C.c_void_p), ("max_pages_per_slot", C.c_int32),
+                ("free_stack", C.c_void_p), ("n_free", C.c_void_p), ("logits", C.c_void_p),
+                ("rows_per_slot", C.c_int32), ("row_token", C.c_void_p), ("row_pos", C.c_void_p),
+                ("k_pool", C.c_void_p), ("v_pool", C.c_void_p), ("attn_out", C.c_void_p)]
+
+
+class AttnArgs(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("rows", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("page_size", C.c_int32), ("max_pages", C.c_int32),
+                ("max_ctx", C.c_int32), ("q", C.c_void_p), ("k_pool", C.c_void_p), ("v_pool", C.c_void_p),
+                ("page_table", C.c_void_p), ("ctx_len", C.c_void_p), ("q_len", C.c_void_p), ("out", C.c_void_p),
+                ("workspace", C.c_void_p)]
+
+
+class SampleArgs(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("stride_n", C.c_int32), ("vocab", C.c_int32), ("propose", C.c_int32),
+                ("q_rows", C.c_int32), ("temperature", C.c_float), ("seed", C.c_uint64), ("slots", C.c_void_p),
+                ("logits", C.c_void_p), ("q_logits", C.c_void_p), ("tokens", C.c_void_p),
+                ("n_commit", C.c_void_p), ("n_accept", C.c_void_p), ("workspace", C.c_void_p)]
+
+
+_lib = None
+
+
+def load(path=LIB_PATH):
+    """Load libisd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m strided_decoding_amd.build` "
+                          "(hipcc, gfx950); there is no fallback implementation")
+    lib = C.CDLL(path)
+    lib.isd_init.argtypes = [C.POINTER(Config), C.POINTER(Weights), C.c_void_p, C.c_void_p, C.POINTER(Sizes),
+                             C.POINTER(C.c_void_p), C.c_void_p]
+    lib.isd_prefill.argtypes = [C.c_void_p, C.c_int32, C.POINTER(C.c_int32), C.c_void_p, C.POINTER(C.c_int32),
+                                C.POINTER(C.c_int32), C.c_void_p, C.c_void_p]
+    lib.isd_step.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+    lib.isd_get_buffers.argtypes = [C.c_void_p, C.POINTER(Buffers)]
+    lib.isd_get_status.argtypes = [C.c_void_p, C.c_void_p]
+    lib.isd_release.argtypes = [C.c_void_p]
+    lib.isd_attn_workspace_bytes.argtypes = [C.POINTER(AttnArgs)]
+    lib.isd_attn_workspace_bytes.restype = C.c_size_t
+    lib.isd_attn_paged.argtypes = [C.POINTER(AttnArgs), C.c_void_p]
+    lib.isd_sample_workspace_bytes.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_int32]
+    lib.isd_sample_workspace_bytes.restype = C.c_size_t
+    lib.isd_sample.argtypes = [C.POINTER(SampleArgs), C.c_void_p]
+    lib.isd_version.restype = C.c_char_p
+    for f in ("isd_init", "isd_prefill", "isd_step", "isd_get_buffers", "isd_get_status", "isd_release",
+              "isd_attn_paged", "isd_sample"):
+        getattr(lib, f).restype = C.c_int
+    _lib = lib
+    return lib
+
+
+def check(where, code):
+    if code != ISD_OK:
+        raise IsdError(where, code)

@@ -1,0 +1,250 @@
+// Shared device helpers and internal structures of libisd (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/isd.h"
+
+#define ISD_DEV __device__ __forceinline__
+
+// ---------------------------------------------------------------------------------------
+// bfloat16 stored as raw bits.  Conversion to float is exact; float -> bf16 rounds to
+// nearest-even (NaN kept quiet).
+struct bf16 {
+  uint16_t u;
+};
+
+ISD_DEV float to_f(float x) { return x; }
+ISD_DEV float to_f(bf16 x) { return __uint_as_float((uint32_t)x.u << 16); }
+
+template <typename T>
+ISD_DEV T from_f(float f);
+template <>
+ISD_DEV float from_f<float>(float f) { return f; }
+template <>
+ISD_DEV bf16 from_f<bf16>(float f) {
+  uint32_t u = __float_as_uint(f);
+  bf16 r;
+  if ((u & 0x7fffffffu) > 0x7f800000u) {
+    r.u = (uint16_t)((u >> 16) | 0x40u);
+  } else {
+    u += 0x7fffu + ((u >> 16) & 1u);
+    r.u = (uint16_t)(u >> 16);
+  }
+  return r;
+}
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;   // MFMA operand (8 bf16)
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;     // 16x16 MFMA accumulator
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;  // 16-byte load unit
+
+ISD_DEV bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// D = A * B + C for one 16x16x32 bf16 tile.  Lane l holds A row (l%16), B column (l%16),
+// each with 8 k-values in slots 8*(l/16) .. 8*(l/16)+7 (any fixed k permutation shared by
+// A and B gives the same product); D lane l, register r is row 4*(l/16)+r, column l%16.
+ISD_DEV f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------------------
+// Wave (64-lane) reductions.
+ISD_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+ISD_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+ISD_DEV double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): one round maps (c0,c1,c2,c3) under key
+// (k0,k1) to (hi(M1 c2)^c1^k0, lo(M1 c2), hi(M0 c0)^c3^k1, lo(M0 c0)); the key is bumped by
+// the Weyl constants between rounds.
+ISD_DEV void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
+    const uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+  }
+}
+
+// u(slot, t, position, purpose) = ((word0 >> 8) + 1/2) * 2^-24, an odd multiple of 2^-25 in
+// (0, 1), exact in double.  purpose 0 = acceptance test, 1 = categorical draw.
+ISD_DEV double philox_uniform(uint64_t seed, uint32_t slot, uint32_t t, uint32_t pos, uint32_t purpose) {
+  uint32_t c[4] = {slot, t, pos, purpose};
+  philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+  return ((double)(c[0] >> 8) + 0.5) * 0x1p-24;
+}
+
+// ---------------------------------------------------------------------------------------
+// Internal structures shared by the runtime and the kernels.
+
+// One attention work item: nq consecutive query positions pos0 .. pos0+nq-1 of `slot`,
+// stored in activation rows row0 .. row0+nq-1.
+struct AttnItem {
+  int32_t slot, row0, nq, pos0;
+};
+
+// Per-row, per-chunk statistics of a logits row: max m_c, lowest argmax, and
+// s_c = sum_j exp((l_j - m_c)/T) over the chunk (double).
+struct ChunkStat {
+  float m;
+  int32_t arg;
+  double s;
+};
+
+constexpr int kStatChunk = 4096;        // logits per statistics chunk
+constexpr int kAttnSplit = 256;         // keys per split-context partial (multiple of 32)
+
+enum EpiMode : int { EPI_STORE = 0, EPI_STORE_F32 = 1, EPI_RESID = 2, EPI_SWIGLU = 3 };
+
+struct GemmArgs {
+  const void* A;             // [*, lda] act; row of output row m is a_rows ? a_rows[m] : m
+  const int32_t* a_rows;     // optional gather (entries < 0 read as zero rows)
+  int lda;
+  const void* B0;            // [N, ldb] act (out x in)
+  const void* B1;            // second operand for EPI_SWIGLU (up projection)
+  int ldb;
+  int M, N, K;
+  int epi;
+  void* C;                   // EPI_STORE / EPI_SWIGLU: act [M, ldc]; EPI_STORE_F32: float
+  int ldc;
+  float* R;                  // EPI_RESID: float residual [M, ldr], R += A B^T
+  int ldr;
+  const float* delta;        // optional LoRA delta rows [*, ldd] added before the epilogue
+  const int32_t* delta_row;  // [M] delta row of output row m or -1
+  int ldd;
+  int delta_off2;            // EPI_SWIGLU: column offset of the up-projection delta
+};
+
+// ---------------------------------------------------------------------------------------
+// Kernel launchers (defined in the .hip files).
+namespace isd {
+
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  const void* q;             // [rows, Hq*hd] act (after RoPE)
+  const void* k_pool;        // layer base: [n_pages, Hkv, P, hd]
+  const void* v_pool;        // layer base: [n_pages, Hkv, hd, P]
+  const int32_t* page_table; // [slots, max_pages]
+  int max_pages;
+  const AttnItem* items;
+  int n_items;               // grid size (items beyond the live count have nq = 0)
+  const int32_t* ctx_len;    // [slots] keys in the pages
+  int Hq, Hkv, hd, P;
+  int ncb;                   // 16-column query blocks per item (2 or 4): nq * Hq/Hkv <= 16 * ncb
+  int split;                 // keys per split (0: one pass writes `out` directly)
+  int max_splits;
+  float* part_o;             // [max_splits, part_rows, Hq, hd]
+  float* part_ml;            // [max_splits, part_rows, Hq, 2]
+  int part_rows;
+  void* out;                 // [rows, Hq*hd] act
+  const int32_t* row_pos;    // [rows] position or -1 (combine, f32 path)
+  const int32_t* row_slot;   // [rows] slot (f32 path)
+  int n_rows;
+};
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_combine_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
+
+template <typename T>
+hipError_t launch_embed(const int32_t* tok, const T* table, float* X, int rows, int d, int mask_id, hipStream_t s);
+template <typename T>
+hipError_t launch_rmsnorm(const float* X, const T* g, T* Y, int rows, int d, float eps, hipStream_t s);
+
+struct RopeAppendArgs {
+  const void* qkv;           // [rows, (Hq+2Hkv)*hd] act
+  void* q_out;               // [rows, Hq*hd] act
+  void* k_pool;              // layer base
+  void* v_pool;
+  const int32_t* page_table;
+  int max_pages;
+  const int32_t* row_pos;    // -1: dead row (no cache write, zero q)
+  const int32_t* row_slot;
+  const float* cos_t;        // [max_pos, hd/2]
+  const float* sin_t;
+  int rows, Hq, Hkv, hd, P;
+};
+template <typename T>
+hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s);
+hipError_t launch_rope_tables(float* cos_t, float* sin_t, int max_pos, int hd, float base, hipStream_t s);
+
+struct StepMeta {            // device buffers of the block / page machinery
+  isd_slot* slots;
+  int32_t* page_table;
+  int max_pages;
+  int32_t* free_stack;
+  int32_t* n_free;
+  int32_t* row_tok;
+  int32_t* row_pos;
+  int32_t* row_slot;
+  int32_t* delta_row;        // [rows] LoRA delta row or -1
+  int32_t* mask_rows;        // [max_batch*(N-1)] row of each MASK row or -1
+  int32_t* ctx_len;          // [max_batch]
+  AttnItem* items;
+  int items_per_slot, q_max;   // decode: attention items per slot, query positions per item
+  int max_batch, N, P, mask_id;
+  int32_t* last_rows;        // prefill: last row of each prompt
+};
+hipError_t launch_init_state(const StepMeta& m, int n_pages, hipStream_t s);
+hipError_t launch_assemble(const StepMeta& m, hipStream_t s);
+hipError_t launch_attn_setup(AttnItem* items, int32_t* row_pos, int32_t* row_slot, const int32_t* ctx_len,
+                             const int32_t* q_len, int batch, int rows, hipStream_t s);
+hipError_t launch_truncate(const StepMeta& m, const int32_t* order, int n, hipStream_t s);
+
+constexpr int kMaxPrefillSlots = 256;
+struct PrefillCall {
+  int n;
+  int32_t slot[kMaxPrefillSlots];
+  int32_t off[kMaxPrefillSlots + 1];
+  int32_t max_new[kMaxPrefillSlots];
+  int32_t item_off[kMaxPrefillSlots + 1];   // first attention item of each prompt
+};
+hipError_t launch_prefill_setup(const StepMeta& m, const PrefillCall& c, const int32_t* prompt_ids,
+                                int q_tile, int32_t* order_out, hipStream_t s);
+
+struct SampleArgs {
+  isd_slot* slots;
+  int n_slots;
+  const int32_t* slot_ids;   // optional: slot index of work item i (prefill); NULL = i
+  int N, V, propose;
+  float T;
+  uint64_t seed;
+  const float* logits;       // current rows
+  int rows_per_slot;         // R (decode) or 1 (prefill)
+  const ChunkStat* stats;    // [rows, n_chunks]
+  const float* q_logits;     // previous pass rows
+  const ChunkStat* q_stats;
+  int q_rows;
+  int n_chunks;
+  int32_t* tokens;           // [n_slots, N]
+  int32_t* n_commit;
+  int32_t* n_accept;
+  int prefill;               // 1: draw the first token only (t = 0, position L)
+  int32_t* first_tok;        // prefill output [n_slots]
+};
+hipError_t launch_row_stats(const float* logits, int rows, int V, float T, ChunkStat* stats, hipStream_t s);
+hipError_t launch_decide(const SampleArgs& a, hipStream_t s);
+
+}  // namespace isd

@@ -1,0 +1,686 @@
+// Host runtime of libisd: configuration checks, workspace carve-up, the per-pass launch
+// sequence, and the C ABI declared in include/isd.h.
+//
+// One ISD pass (isd_step):
+//   assemble (rows + page reservation) -> embed -> per layer {RMSNorm -> QKV GEMM (+LoRA on
+//   MASK rows) -> RoPE + KV append -> paged attention (+ split combine) -> O GEMM + residual
+//   -> RMSNorm -> gate/up GEMM + SwiGLU -> down GEMM + residual} -> final RMSNorm -> LM head
+//   -> row statistics -> decide -> truncate.
+// Everything is enqueued on the caller's stream; no host synchronization happens.
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "isd_common.h"
+
+using namespace isd;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  template <typename T>
+  T* take(size_t n) {
+    off = align_up(off);
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += n * sizeof(T);
+    return p;
+  }
+};
+
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+struct isd_ctx {
+  isd_config cfg{};
+  bool bf;                // activations are bf16
+  size_t act;             // bytes per activation element
+  int R, qd, kd, qkvw;
+  int max_pages, max_rows, max_dec_rows, n_chunks, max_splits, items_per_slot, q_max, ncb, q_tile;
+  int max_items, n_mask, delta_w;
+  // weights
+  const void *embed = nullptr, *final_norm = nullptr, *lm_head = nullptr;
+  std::vector<const void*> attn_norm, wqkv, wo, ffn_norm, wg, wu, wd, lora_a, lora_b;
+  // pools
+  char* k_pool = nullptr;
+  char* v_pool = nullptr;
+  size_t kv_layer_bytes = 0;
+  // workspace regions
+  isd_slot* slots = nullptr;
+  int32_t *page_table = nullptr, *free_stack = nullptr, *n_free = nullptr;
+  int32_t *row_tok = nullptr, *row_pos = nullptr, *row_slot = nullptr, *delta_row = nullptr;
+  int32_t *mask_rows = nullptr, *ctx_len = nullptr, *last_rows = nullptr, *order = nullptr;
+  AttnItem* items = nullptr;
+  float* X = nullptr;
+  void *Xn = nullptr, *QKV = nullptr, *Qr = nullptr, *O = nullptr, *H = nullptr;
+  float *part_o = nullptr, *part_ml = nullptr;
+  float* logits[2] = {nullptr, nullptr};
+  ChunkStat* stats[2] = {nullptr, nullptr};
+  float *cos_t = nullptr, *sin_t = nullptr;
+  void* lora_s = nullptr;
+  float* lora_delta = nullptr;
+  int cur = 0;            // logits buffer the next pass writes
+  bool prefilled = false;
+  std::vector<long long> reserved;   // admission reservation per slot (pages)
+  long long reserved_total = 0;
+  isd_status sticky = ISD_OK;
+};
+
+namespace {
+
+isd_status check_config(const isd_config* c) {
+  if (!c) return ISD_E_ARG;
+  if (c->dtype != ISD_F32 && c->dtype != ISD_BF16) return ISD_E_ARG;
+  if (c->propose != ISD_PROPOSE_SAMPLE && c->propose != ISD_PROPOSE_ARGMAX) return ISD_E_ARG;
+  if (!(c->temperature >= 0.f)) return ISD_E_ARG;
+  if (c->stride_n < 1 || c->stride_n > ISD_MAX_STRIDE) return ISD_E_ARG;
+  if (c->n_layers < 1 || c->d_model < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 2 ||
+      c->d_ffn < 1 || c->vocab < 2 || c->max_batch < 1 || c->max_seq_len < 1 || c->n_pages < 1 ||
+      c->max_prefill_tokens < 1 || c->lora_rank < 0 || !(c->rms_eps > 0.f) || !(c->rope_base > 0.f))
+    return ISD_E_ARG;
+  if (c->page_size != 16) return ISD_E_SHAPE;
+  if (c->n_q_heads % c->n_kv_heads) return ISD_E_SHAPE;
+  if (c->head_dim % 2) return ISD_E_SHAPE;
+  if (c->vocab > kStatChunk * 256) return ISD_E_SHAPE;
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (c->dtype == ISD_BF16) {
+    if (c->head_dim != 128) return ISD_E_SHAPE;
+    if (G > 8) return ISD_E_SHAPE;
+    if (c->d_model % 64 || c->d_ffn % 64 || (c->n_q_heads * c->head_dim) % 64) return ISD_E_SHAPE;
+    if (c->lora_rank % 64) return ISD_E_SHAPE;
+  } else {
+    if (c->head_dim > 256) return ISD_E_SHAPE;
+  }
+  return ISD_OK;
+}
+
+// Carve the workspace (base == nullptr: size only).
+size_t carve(isd_ctx& x, char* base) {
+  const isd_config& c = x.cfg;
+  Carver cv{base};
+  const int B = c.max_batch, d = c.d_model, V = c.vocab, F = c.d_ffn;
+  x.slots = cv.take<isd_slot>(B);
+  x.page_table = cv.take<int32_t>((size_t)B * x.max_pages);
+  x.free_stack = cv.take<int32_t>(c.n_pages);
+  x.n_free = cv.take<int32_t>(64);
+  x.row_tok = cv.take<int32_t>(x.max_rows);
+  x.row_pos = cv.take<int32_t>(x.max_rows);
+  x.row_slot = cv.take<int32_t>(x.max_rows);
+  x.delta_row = cv.take<int32_t>(x.max_rows);
+  x.mask_rows = cv.take<int32_t>(std::max(1, x.n_mask));
+  x.ctx_len = cv.take<int32_t>(B);
+  x.last_rows = cv.take<int32_t>(B);
+  x.order = cv.take<int32_t>(B);
+  x.items = cv.take<AttnItem>(x.max_items);
+  x.X = cv.take<float>((size_t)x.max_rows * d);
+  x.Xn = cv.take<char>((size_t)x.max_rows * d * x.act);
+  x.QKV = cv.take<char>((size_t)x.max_rows * x.qkvw * x.act);
+  x.Qr = cv.take<char>((size_t)x.max_rows * x.qd * x.act);
+  x.O = cv.take<char>((size_t)x.max_rows * x.qd * x.act);
+  x.H = cv.take<char>((size_t)x.max_rows * F * x.act);
+  if (x.bf) {
+    x.part_o = cv.take<float>((size_t)x.max_splits * x.max_dec_rows * x.qd);
+    x.part_ml = cv.take<float>((size_t)x.max_splits * x.max_dec_rows * c.n_q_heads * 2);
+  }
+  for (int i = 0; i < 2; ++i) {
+    x.logits[i] = cv.take<float>((size_t)x.max_dec_rows * V);
+    x.stats[i] = cv.take<ChunkStat>((size_t)x.max_dec_rows * x.n_chunks);
+  }
+  const int max_pos = c.max_seq_len + 2 * c.stride_n;
+  x.cos_t = cv.take<float>((size_t)max_pos * (c.head_dim / 2));
+  x.sin_t = cv.take<float>((size_t)max_pos * (c.head_dim / 2));
+  if (c.lora_rank > 0) {
+    x.lora_s = cv.take<char>((size_t)std::max(1, x.n_mask) * 3 * c.lora_rank * x.act);
+    x.lora_delta = cv.take<float>((size_t)std::max(1, x.n_mask) * x.delta_w);
+  }
+  return align_up(cv.off);
+}
+
+void derive(isd_ctx& x) {
+  const isd_config& c = x.cfg;
+  x.bf = c.dtype == ISD_BF16;
+  x.act = x.bf ? 2 : 4;
+  x.R = 2 * c.stride_n - 1;
+  x.qd = c.n_q_heads * c.head_dim;
+  x.kd = c.n_kv_heads * c.head_dim;
+  x.qkvw = x.qd + 2 * x.kd;
+  x.max_pages = cdiv(c.max_seq_len + 2 * c.stride_n, c.page_size);
+  x.max_dec_rows = c.max_batch * x.R;
+  x.max_rows = std::max(x.max_dec_rows, c.max_prefill_tokens);
+  x.n_chunks = cdiv(c.vocab, kStatChunk);
+  x.max_splits = cdiv(c.max_seq_len + 2 * c.stride_n, kAttnSplit);
+  const int G = c.n_q_heads / c.n_kv_heads;
+  x.ncb = (x.R * G <= 32) ? 2 : 4;
+  x.q_max = std::max(1, 16 * x.ncb / G);
+  x.items_per_slot = cdiv(x.R, x.q_max);
+  x.q_tile = x.q_max;
+  x.max_items = std::max(c.max_batch * x.items_per_slot, cdiv(c.max_prefill_tokens, x.q_tile) + c.max_batch);
+  x.n_mask = c.max_batch * (c.stride_n - 1);
+  x.delta_w = std::max(std::max(x.qkvw, 2 * c.d_ffn), c.d_model);
+  x.kv_layer_bytes = (size_t)c.n_pages * x.kd * c.page_size * x.act;
+}
+
+StepMeta meta(isd_ctx& x) {
+  StepMeta m{};
+  m.slots = x.slots;
+  m.page_table = x.page_table;
+  m.max_pages = x.max_pages;
+  m.free_stack = x.free_stack;
+  m.n_free = x.n_free;
+  m.row_tok = x.row_tok;
+  m.row_pos = x.row_pos;
+  m.row_slot = x.row_slot;
+  m.delta_row = x.delta_row;
+  m.mask_rows = x.mask_rows;
+  m.ctx_len = x.ctx_len;
+  m.items = x.items;
+  m.items_per_slot = x.items_per_slot;
+  m.q_max = x.q_max;
+  m.max_batch = x.cfg.max_batch;
+  m.N = x.cfg.stride_n;
+  m.P = x.cfg.page_size;
+  m.mask_id = x.cfg.vocab;
+  m.last_rows = x.last_rows;
+  return m;
+}
+
+#define HIP_OK(expr)                       \
+  do {                                     \
+    if ((expr) != hipSuccess) return ISD_E_HIP; \
+  } while (0)
+
+hipError_t gemm(const isd_ctx& x, const GemmArgs& g, hipStream_t s) {
+  return x.bf ? launch_gemm_bf16(g, s) : launch_gemm_f32(g, s);
+}
+
+GemmArgs gargs(const void* A, int lda, const void* B0, int ldb, int M, int N, int K, int epi) {
+  GemmArgs g{};
+  g.A = A;
+  g.lda = lda;
+  g.B0 = B0;
+  g.ldb = ldb;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.epi = epi;
+  return g;
+}
+
+// LoRA of one target on the MASK rows: S[:, so:so+r] = X[mask_rows] A^T; delta[:, do:do+n] = S B^T.
+isd_status lora_target(isd_ctx& x, int layer, int tgt, const void* Xsrc, int ldx, int k_in, int n_out, int s_off,
+                       int d_off, hipStream_t s) {
+  const int r = x.cfg.lora_rank, M = x.n_mask;
+  const void* A = x.lora_a[(size_t)layer * 7 + tgt];
+  const void* Bm = x.lora_b[(size_t)layer * 7 + tgt];
+  GemmArgs g = gargs(Xsrc, ldx, A, k_in, M, r, k_in, EPI_STORE);
+  g.a_rows = x.mask_rows;
+  g.C = (char*)x.lora_s + (size_t)s_off * x.act;
+  g.ldc = 3 * r;
+  HIP_OK(gemm(x, g, s));
+  GemmArgs e = gargs((const char*)x.lora_s + (size_t)s_off * x.act, 3 * r, Bm, r, M, n_out, r, EPI_STORE_F32);
+  e.C = x.lora_delta + d_off;
+  e.ldc = x.delta_w;
+  HIP_OK(gemm(x, e, s));
+  return ISD_OK;
+}
+
+void with_delta(const isd_ctx& x, GemmArgs& g, bool on) {
+  if (!on) return;
+  g.delta = x.lora_delta;
+  g.delta_row = x.delta_row;
+  g.ldd = x.delta_w;
+}
+
+// The transformer body over M rows.  decode: split-context attention over the decode items;
+// prefill: one pass per item.  lm_rows: rows fed to the LM head (gather list or null = all).
+isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* lm_rows, int lm_M, bool lora,
+                   hipStream_t s) {
+  const isd_config& c = x.cfg;
+  const int d = c.d_model, F = c.d_ffn, Hq = c.n_q_heads, Hkv = c.n_kv_heads, hd = c.head_dim;
+  if (x.bf) HIP_OK(launch_embed<bf16>(x.row_tok, (const bf16*)x.embed, x.X, M, d, c.vocab, s));
+  else HIP_OK(launch_embed<float>(x.row_tok, (const float*)x.embed, x.X, M, d, c.vocab, s));
+  for (int l = 0; l < c.n_layers; ++l) {
+    char* kl = x.k_pool + (size_t)l * x.kv_layer_bytes;
+    char* vl = x.v_pool + (size_t)l * x.kv_layer_bytes;
+    // attention block
+    if (x.bf) HIP_OK(launch_rmsnorm<bf16>(x.X, (const bf16*)x.attn_norm[l], (bf16*)x.Xn, M, d, c.rms_eps, s));
+    else HIP_OK(launch_rmsnorm<float>(x.X, (const float*)x.attn_norm[l], (float*)x.Xn, M, d, c.rms_eps, s));
+    if (lora) {
+      const int r = c.lora_rank;
+      const char* wq = nullptr;
+      (void)wq;
+      isd_status st;
+      if ((st = lora_target(x, l, 0, x.Xn, d, d, x.qd, 0, 0, s)) != ISD_OK) return st;
+      if ((st = lora_target(x, l, 1, x.Xn, d, d, x.kd, r, x.qd, s)) != ISD_OK) return st;
+      if ((st = lora_target(x, l, 2, x.Xn, d, d, x.kd, 2 * r, x.qd + x.kd, s)) != ISD_OK) return st;
+    }
+    {
+      GemmArgs g = gargs(x.Xn, d, x.wqkv[l], d, M, x.qkvw, d, EPI_STORE);
+      g.C = x.QKV;
+      g.ldc = x.qkvw;
+      with_delta(x, g, lora);
+      HIP_OK(gemm(x, g, s));
+    }
+    {
+      RopeAppendArgs ra{};
+      ra.qkv = x.QKV;
+      ra.q_out = x.Qr;
+      ra.k_pool = kl;
+      ra.v_pool = vl;
+      ra.page_table = x.page_table;
+      ra.max_pages = x.max_pages;
+      ra.row_pos = x.row_pos;
+      ra.row_slot = x.row_slot;
+      ra.cos_t = x.cos_t;
+      ra.sin_t = x.sin_t;
+      ra.rows = M;
+      ra.Hq = Hq;
+      ra.Hkv = Hkv;
+      ra.hd = hd;
+      ra.P = c.page_size;
+      if (x.bf) HIP_OK(launch_rope_append<bf16>(ra, s));
+      else HIP_OK(launch_rope_append<float>(ra, s));
+    }
+    {
+      AttnArgs aa{};
+      aa.q = x.Qr;
+      aa.k_pool = kl;
+      aa.v_pool = vl;
+      aa.page_table = x.page_table;
+      aa.max_pages = x.max_pages;
+      aa.items = x.items;
+      aa.n_items = n_items;
+      aa.ctx_len = x.ctx_len;
+      aa.Hq = Hq;
+      aa.Hkv = Hkv;
+      aa.hd = hd;
+      aa.P = c.page_size;
+      aa.ncb = x.ncb;
+      aa.out = x.O;
+      aa.row_pos = x.row_pos;
+      aa.row_slot = x.row_slot;
+      aa.n_rows = M;
+      if (!x.bf) {
+        HIP_OK(launch_attn_f32(aa, s));
+      } else if (decode) {
+        aa.split = kAttnSplit;
+        aa.max_splits = x.max_splits;
+        aa.part_o = x.part_o;
+        aa.part_ml = x.part_ml;
+        aa.part_rows = x.max_dec_rows;
+        HIP_OK(launch_attn_bf16(aa, s));
+        HIP_OK(launch_attn_combine_bf16(aa, s));
+      } else {
+        aa.split = 0;
+        HIP_OK(launch_attn_bf16(aa, s));
+      }
+    }
+    if (lora) {
+      isd_status st = lora_target(x, l, 3, x.O, x.qd, x.qd, d, 0, 0, s);
+      if (st != ISD_OK) return st;
+    }
+    {
+      GemmArgs g = gargs(x.O, x.qd, x.wo[l], x.qd, M, d, x.qd, EPI_RESID);
+      g.R = x.X;
+      g.ldr = d;
+      with_delta(x, g, lora);
+      HIP_OK(gemm(x, g, s));
+    }
+    // FFN block
+    if (x.bf) HIP_OK(launch_rmsnorm<bf16>(x.X, (const bf16*)x.ffn_norm[l], (bf16*)x.Xn, M, d, c.rms_eps, s));
+    else HIP_OK(launch_rmsnorm<float>(x.X, (const float*)x.ffn_norm[l], (float*)x.Xn, M, d, c.rms_eps, s));
+    if (lora) {
+      const int r = c.lora_rank;
+      isd_status st;
+      if ((st = lora_target(x, l, 4, x.Xn, d, d, F, 0, 0, s)) != ISD_OK) return st;
+      if ((st = lora_target(x, l, 5, x.Xn, d, d, F, r, F, s)) != ISD_OK) return st;
+    }
+    {
+      GemmArgs g = gargs(x.Xn, d, x.wg[l], d, M, F, d, EPI_SWIGLU);
+      g.B1 = x.wu[l];
+      g.C = x.H;
+      g.ldc = F;
+      with_delta(x, g, lora);
+      g.delta_off2 = F;
+      HIP_OK(gemm(x, g, s));
+    }
+    if (lora) {
+      isd_status st = lora_target(x, l, 6, x.H, F, F, d, 0, 0, s);
+      if (st != ISD_OK) return st;
+    }
+    {
+      GemmArgs g = gargs(x.H, F, x.wd[l], F, M, d, F, EPI_RESID);
+      g.R = x.X;
+      g.ldr = d;
+      with_delta(x, g, lora);
+      HIP_OK(gemm(x, g, s));
+    }
+  }
+  if (x.bf) HIP_OK(launch_rmsnorm<bf16>(x.X, (const bf16*)x.final_norm, (bf16*)x.Xn, M, d, c.rms_eps, s));
+  else HIP_OK(launch_rmsnorm<float>(x.X, (const float*)x.final_norm, (float*)x.Xn, M, d, c.rms_eps, s));
+  GemmArgs g = gargs(x.Xn, d, x.lm_head, d, lm_M, c.vocab, d, EPI_STORE_F32);
+  g.a_rows = lm_rows;
+  g.C = x.logits[x.cur];
+  g.ldc = c.vocab;
+  HIP_OK(gemm(x, g, s));
+  return ISD_OK;
+}
+
+SampleArgs sargs(isd_ctx& x) {
+  SampleArgs a{};
+  a.slots = x.slots;
+  a.N = x.cfg.stride_n;
+  a.V = x.cfg.vocab;
+  a.propose = x.cfg.propose;
+  a.T = x.cfg.temperature;
+  a.seed = x.cfg.seed;
+  a.n_chunks = x.n_chunks;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* isd_version(void) { return "isd-mi355x 0.1 (gfx950)"; }
+
+isd_status isd_init(const isd_config* cfg, const isd_weights* w, void* kv_pool, void* workspace, isd_sizes* sizes,
+                    isd_ctx** out, void* stream) {
+  if (!cfg || !sizes || !out) return ISD_E_ARG;
+  *out = nullptr;
+  isd_status st = check_config(cfg);
+  if (st != ISD_OK) return st;
+  isd_ctx probe;
+  probe.cfg = *cfg;
+  derive(probe);
+  sizes->kv_pool_bytes = 2 * (size_t)cfg->n_layers * probe.kv_layer_bytes;
+  sizes->workspace_bytes = carve(probe, nullptr);
+  if (!kv_pool && !workspace) return ISD_OK;
+  if (!kv_pool || !workspace || !w) return ISD_E_ARG;
+  if (((uintptr_t)kv_pool % kAlign) || ((uintptr_t)workspace % kAlign)) return ISD_E_ARG;
+  const int L = cfg->n_layers;
+  if (!w->embed || !w->final_norm || !w->lm_head || !w->attn_norm || !w->wqkv || !w->wo || !w->ffn_norm ||
+      !w->wg || !w->wu || !w->wd)
+    return ISD_E_ARG;
+  if (cfg->lora_rank > 0 && (!w->lora_a || !w->lora_b)) return ISD_E_ARG;
+  isd_ctx* x = new (std::nothrow) isd_ctx();
+  if (!x) return ISD_E_ARG;
+  x->cfg = *cfg;
+  derive(*x);
+  carve(*x, (char*)workspace);
+  x->embed = w->embed;
+  x->final_norm = w->final_norm;
+  x->lm_head = w->lm_head;
+  x->attn_norm.assign(w->attn_norm, w->attn_norm + L);
+  x->wqkv.assign(w->wqkv, w->wqkv + L);
+  x->wo.assign(w->wo, w->wo + L);
+  x->ffn_norm.assign(w->ffn_norm, w->ffn_norm + L);
+  x->wg.assign(w->wg, w->wg + L);
+  x->wu.assign(w->wu, w->wu + L);
+  x->wd.assign(w->wd, w->wd + L);
+  for (int l = 0; l < L; ++l)
+    if (!x->attn_norm[l] || !x->wqkv[l] || !x->wo[l] || !x->ffn_norm[l] || !x->wg[l] || !x->wu[l] || !x->wd[l]) {
+      delete x;
+      return ISD_E_ARG;
+    }
+  if (cfg->lora_rank > 0) {
+    x->lora_a.assign(w->lora_a, w->lora_a + (size_t)L * 7);
+    x->lora_b.assign(w->lora_b, w->lora_b + (size_t)L * 7);
+    for (size_t i = 0; i < x->lora_a.size(); ++i)
+      if (!x->lora_a[i] || !x->lora_b[i]) {
+        delete x;
+        return ISD_E_ARG;
+      }
+  }
+  x->k_pool = (char*)kv_pool;
+  x->v_pool = (char*)kv_pool + (size_t)L * x->kv_layer_bytes;
+  x->reserved.assign(cfg->max_batch, 0);
+  hipStream_t s = (hipStream_t)stream;
+  StepMeta m = meta(*x);
+  if (launch_init_state(m, cfg->n_pages, s) != hipSuccess ||
+      launch_rope_tables(x->cos_t, x->sin_t, cfg->max_seq_len + 2 * cfg->stride_n, cfg->head_dim, cfg->rope_base, s) !=
+          hipSuccess) {
+    delete x;
+    return ISD_E_HIP;
+  }
+  *out = x;
+  return ISD_OK;
+}
+
+isd_status isd_prefill(isd_ctx* x, int32_t n, const int32_t* slots, const int32_t* prompt_ids, const int32_t* offsets,
+                       const int32_t* max_new, int32_t* first_tok, void* stream) {
+  if (!x || !slots || !prompt_ids || !offsets || !max_new || !first_tok) return ISD_E_ARG;
+  const isd_config& c = x->cfg;
+  if (n < 1 || n > c.max_batch || n > kMaxPrefillSlots) return ISD_E_ARG;
+  if (offsets[0] != 0) return ISD_E_ARG;
+  std::vector<char> seen(c.max_batch, 0);
+  long long new_total = x->reserved_total;
+  PrefillCall call{};
+  call.n = n;
+  call.off[0] = 0;
+  call.item_off[0] = 0;
+  for (int i = 0; i < n; ++i) {
+    const int b = slots[i];
+    if (b < 0 || b >= c.max_batch || seen[b]) return ISD_E_ARG;
+    seen[b] = 1;
+    const int len = offsets[i + 1] - offsets[i];
+    if (len < 1 || max_new[i] < 1) return ISD_E_ARG;
+    if ((long long)len + max_new[i] + 2 * c.stride_n > c.max_seq_len) return ISD_E_CAPACITY;
+    const long long res = cdiv(len + max_new[i] + 2 * c.stride_n, c.page_size);
+    new_total += res - x->reserved[b];
+    call.slot[i] = b;
+    call.off[i + 1] = offsets[i + 1];
+    call.max_new[i] = max_new[i];
+    call.item_off[i + 1] = call.item_off[i] + cdiv(len, x->q_tile);
+  }
+  const int M = offsets[n];
+  if (M > c.max_prefill_tokens) return ISD_E_CAPACITY;
+  if (new_total > c.n_pages) return ISD_E_CAPACITY;
+  if (call.item_off[n] > x->max_items) return ISD_E_CAPACITY;
+  for (int i = 0; i < n; ++i) {
+    const int b = slots[i];
+    const int len = offsets[i + 1] - offsets[i];
+    const long long res = cdiv(len + max_new[i] + 2 * c.stride_n, c.page_size);
+    x->reserved_total += res - x->reserved[b];
+    x->reserved[b] = res;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  StepMeta m = meta(*x);
+  HIP_OK(launch_prefill_setup(m, call, prompt_ids, x->q_tile, x->order, s));
+  isd_status st = forward(*x, M, call.item_off[n], /*decode=*/false, x->last_rows, n, /*lora=*/false, s);
+  if (st != ISD_OK) return st;
+  HIP_OK(launch_row_stats(x->logits[x->cur], n, c.vocab, c.temperature, x->stats[x->cur], s));
+  SampleArgs a = sargs(*x);
+  a.n_slots = n;
+  a.slot_ids = x->order;
+  a.logits = x->logits[x->cur];
+  a.rows_per_slot = 1;
+  a.stats = x->stats[x->cur];
+  a.prefill = 1;
+  a.first_tok = first_tok;
+  HIP_OK(launch_decide(a, s));
+  HIP_OK(launch_truncate(m, x->order, n, s));
+  x->prefilled = true;
+  return ISD_OK;
+}
+
+isd_status isd_step(isd_ctx* x, int32_t* tokens, int32_t* n_commit, int32_t* n_accept, void* stream) {
+  if (!x || !tokens || !n_commit || !n_accept) return ISD_E_ARG;
+  if (!x->prefilled) return ISD_E_STATE;
+  const isd_config& c = x->cfg;
+  hipStream_t s = (hipStream_t)stream;
+  StepMeta m = meta(*x);
+  HIP_OK(launch_assemble(m, s));
+  const int M = x->max_dec_rows;
+  isd_status st = forward(*x, M, c.max_batch * x->items_per_slot, /*decode=*/true, nullptr, M,
+                          /*lora=*/c.lora_rank > 0 && c.stride_n > 1, s);
+  if (st != ISD_OK) return st;
+  const int cur = x->cur, prev = cur ^ 1;
+  HIP_OK(launch_row_stats(x->logits[cur], M, c.vocab, c.temperature, x->stats[cur], s));
+  SampleArgs a = sargs(*x);
+  a.n_slots = c.max_batch;
+  a.logits = x->logits[cur];
+  a.rows_per_slot = x->R;
+  a.stats = x->stats[cur];
+  a.q_logits = x->logits[prev];
+  a.q_stats = x->stats[prev];
+  a.q_rows = M;
+  a.tokens = tokens;
+  a.n_commit = n_commit;
+  a.n_accept = n_accept;
+  HIP_OK(launch_decide(a, s));
+  HIP_OK(launch_truncate(m, nullptr, c.max_batch, s));
+  x->cur = prev;
+  return ISD_OK;
+}
+
+isd_status isd_get_buffers(const isd_ctx* x, isd_buffers* out) {
+  if (!x || !out) return ISD_E_ARG;
+  out->slots = x->slots;
+  out->page_table = x->page_table;
+  out->max_pages_per_slot = x->max_pages;
+  out->free_stack = x->free_stack;
+  out->n_free = x->n_free;
+  out->logits = x->logits[x->cur ^ 1];
+  out->rows_per_slot = x->R;
+  out->row_token = x->row_tok;
+  out->row_pos = x->row_pos;
+  out->k_pool = x->k_pool;
+  out->v_pool = x->v_pool;
+  out->attn_out = x->O;
+  return ISD_OK;
+}
+
+isd_status isd_get_status(isd_ctx* x, void* stream) {
+  if (!x) return ISD_E_ARG;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return ISD_E_HIP;
+  std::vector<isd_slot> h(x->cfg.max_batch);
+  if (hipMemcpy(h.data(), x->slots, h.size() * sizeof(isd_slot), hipMemcpyDeviceToHost) != hipSuccess)
+    return ISD_E_HIP;
+  for (const auto& sl : h)
+    if (sl.status == ISD_E_NONFINITE) x->sticky = ISD_E_NONFINITE;
+  return x->sticky;
+}
+
+isd_status isd_release(isd_ctx* x) {
+  if (!x) return ISD_E_ARG;
+  delete x;
+  return ISD_OK;
+}
+
+size_t isd_attn_workspace_bytes(const isd_attn_args* a) {
+  if (!a) return 0;
+  const int splits = cdiv(std::max(1, a->max_ctx), kAttnSplit);
+  const size_t rows = (size_t)a->batch * a->rows;
+  size_t off = 0;
+  off = align_up(off + a->batch * sizeof(AttnItem));
+  off = align_up(off + rows * 4);
+  off = align_up(off + rows * 4);
+  off = align_up(off + (size_t)splits * rows * a->n_q_heads * a->head_dim * 4);
+  off = align_up(off + (size_t)splits * rows * a->n_q_heads * 2 * 4);
+  return off;
+}
+
+isd_status isd_attn_paged(const isd_attn_args* a, void* stream) {
+  if (!a || !a->q || !a->k_pool || !a->v_pool || !a->page_table || !a->ctx_len || !a->q_len || !a->out ||
+      !a->workspace)
+    return ISD_E_ARG;
+  if (a->batch < 1 || a->rows < 1 || a->n_kv_heads < 1 || a->n_q_heads % a->n_kv_heads || a->max_ctx < 1)
+    return ISD_E_ARG;
+  const int G = a->n_q_heads / a->n_kv_heads;
+  if (a->head_dim != 128 || a->page_size != 16 || G * a->rows > 64) return ISD_E_SHAPE;
+  const int splits = cdiv(a->max_ctx, kAttnSplit);
+  const size_t rows = (size_t)a->batch * a->rows;
+  char* w = (char*)a->workspace;
+  size_t off = 0;
+  AttnItem* items = (AttnItem*)(w + off);
+  off = align_up(off + a->batch * sizeof(AttnItem));
+  int32_t* row_pos = (int32_t*)(w + off);
+  off = align_up(off + rows * 4);
+  int32_t* row_slot = (int32_t*)(w + off);
+  off = align_up(off + rows * 4);
+  float* part_o = (float*)(w + off);
+  off = align_up(off + (size_t)splits * rows * a->n_q_heads * a->head_dim * 4);
+  float* part_ml = (float*)(w + off);
+  hipStream_t s = (hipStream_t)stream;
+  HIP_OK(launch_attn_setup(items, row_pos, row_slot, a->ctx_len, a->q_len, a->batch, a->rows, s));
+  AttnArgs aa{};
+  aa.q = a->q;
+  aa.k_pool = a->k_pool;
+  aa.v_pool = a->v_pool;
+  aa.page_table = a->page_table;
+  aa.max_pages = a->max_pages;
+  aa.items = items;
+  aa.n_items = a->batch;
+  aa.ctx_len = a->ctx_len;
+  aa.Hq = a->n_q_heads;
+  aa.Hkv = a->n_kv_heads;
+  aa.hd = a->head_dim;
+  aa.P = a->page_size;
+  aa.ncb = G * a->rows <= 32 ? 2 : 4;
+  aa.split = kAttnSplit;
+  aa.max_splits = splits;
+  aa.part_o = part_o;
+  aa.part_ml = part_ml;
+  aa.part_rows = (int)rows;
+  aa.out = a->out;
+  aa.row_pos = row_pos;
+  aa.row_slot = row_slot;
+  aa.n_rows = (int)rows;
+  HIP_OK(launch_attn_bf16(aa, s));
+  HIP_OK(launch_attn_combine_bf16(aa, s));
+  return ISD_OK;
+}
+
+size_t isd_sample_workspace_bytes(int32_t batch, int32_t rows, int32_t vocab, int32_t q_rows) {
+  const int nc = cdiv(vocab, kStatChunk);
+  return align_up((size_t)batch * rows * nc * sizeof(ChunkStat)) +
+         align_up((size_t)std::max(1, q_rows) * nc * sizeof(ChunkStat));
+}
+
+isd_status isd_sample(const isd_sample_args* a, void* stream) {
+  if (!a || !a->slots || !a->logits || !a->tokens || !a->n_commit || !a->n_accept || !a->workspace)
+    return ISD_E_ARG;
+  if (a->batch < 1 || a->stride_n < 1 || a->stride_n > ISD_MAX_STRIDE || a->vocab < 2 ||
+      a->vocab > kStatChunk * 256 || !(a->temperature >= 0.f))
+    return ISD_E_ARG;
+  if (a->propose != ISD_PROPOSE_SAMPLE && a->propose != ISD_PROPOSE_ARGMAX) return ISD_E_ARG;
+  if (a->propose == ISD_PROPOSE_SAMPLE && a->temperature > 0.f && (!a->q_logits || a->q_rows < 1)) return ISD_E_ARG;
+  const int R = 2 * a->stride_n - 1, nc = cdiv(a->vocab, kStatChunk);
+  char* w = (char*)a->workspace;
+  ChunkStat* st = (ChunkStat*)w;
+  ChunkStat* qst = (ChunkStat*)(w + align_up((size_t)a->batch * R * nc * sizeof(ChunkStat)));
+  hipStream_t s = (hipStream_t)stream;
+  HIP_OK(launch_row_stats(a->logits, a->batch * R, a->vocab, a->temperature, st, s));
+  if (a->q_logits && a->q_rows > 0)
+    HIP_OK(launch_row_stats(a->q_logits, a->q_rows, a->vocab, a->temperature, qst, s));
+  SampleArgs sa{};
+  sa.slots = a->slots;
+  sa.n_slots = a->batch;
+  sa.N = a->stride_n;
+  sa.V = a->vocab;
+  sa.propose = a->propose;
+  sa.T = a->temperature;
+  sa.seed = a->seed;
+  sa.logits = a->logits;
+  sa.rows_per_slot = R;
+  sa.stats = st;
+  sa.q_logits = a->q_logits;
+  sa.q_stats = qst;
+  sa.q_rows = a->q_rows;
+  sa.n_chunks = nc;
+  sa.tokens = a->tokens;
+  sa.n_commit = a->n_commit;
+  sa.n_accept = a->n_accept;
+  HIP_OK(launch_decide(sa, s));
+  return ISD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,353 @@
+// Block assembly, KV page reserve / append / truncate, and the elementwise glue of a pass
+// (embedding gather, RMSNorm, RoPE).
+//
+// Block layout per slot (R = 2N-1 row slots, L cached tokens, c newest committed token):
+//   state A: [c, v_1 .. v_{N-1}, MASK x (N-1)] at positions L .. L+2N-2
+//   state B: [c, MASK x (N-1)]                 at positions L .. L+N-1
+// Pages: a LIFO free stack (top = n_free-1).  A pass first reserves, slot by slot in
+// ascending order, the pages positions L .. L+q_len-1 need; after the decisions every slot,
+// in ascending order, frees the pages beyond ceil(L'/P), ascending logical order.  Both
+// orders come from block-wide prefix sums, so the page tables are a deterministic function
+// of the slot states.
+#include "isd_common.h"
+
+namespace isd {
+namespace {
+
+// Exclusive prefix sum over a 256-thread block; *total receives the block sum.
+__device__ int block_excl_scan(int v, int* sh, int* total) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int t = tid >= off ? sh[tid - off] : 0;
+    __syncthreads();
+    sh[tid] += t;
+    __syncthreads();
+  }
+  const int incl = sh[tid];
+  *total = sh[255];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(256) void assemble_kernel(StepMeta m) {
+  __shared__ int sh[256];
+  __shared__ int s_nfree;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_nfree = *m.n_free;
+  __syncthreads();
+  const int N = m.N, R = 2 * N - 1, P = m.P;
+  int popped = 0;
+  for (int g0 = 0; g0 < m.max_batch; g0 += 256) {
+    const int b = g0 + tid;
+    const bool valid = b < m.max_batch;
+    isd_slot* st = valid ? &m.slots[b] : nullptr;
+    const int state = valid ? st->state : ISD_SLOT_EMPTY;
+    const int L = valid ? st->L : 0;
+    const int q_len = state == ISD_SLOT_A ? R : (state == ISD_SLOT_B ? N : 0);
+    const int have = valid ? st->n_pages : 0;
+    int need = 0;
+    if (q_len > 0) need = max(0, (L + q_len + P - 1) / P - have);
+    int total;
+    const int off = block_excl_scan(need, sh, &total);
+    if (valid) {
+      int32_t* pt = m.page_table + (size_t)b * m.max_pages;
+      for (int k = 0; k < need; ++k) {
+        const int idx = s_nfree - 1 - (popped + off + k);
+        pt[have + k] = idx >= 0 ? m.free_stack[idx] : -1;
+        if (idx < 0) st->status = ISD_E_CAPACITY;
+      }
+      st->n_pages = have + need;
+      // rows
+      for (int i = 0; i < R; ++i) {
+        const int r = b * R + i;
+        int tok = m.mask_id, pos = -1;
+        if (i < q_len) {
+          pos = L + i;
+          if (i == 0) tok = st->c;
+          else if (state == ISD_SLOT_A && i < N) tok = st->pending[i - 1];
+        }
+        m.row_tok[r] = tok;
+        m.row_pos[r] = pos;
+        m.row_slot[r] = b;
+        m.delta_row[r] = -1;
+      }
+      for (int j = 0; j < N - 1; ++j) {
+        int r = -1;
+        if (state == ISD_SLOT_A) r = b * R + N + j;
+        else if (state == ISD_SLOT_B) r = b * R + 1 + j;
+        m.mask_rows[b * (N - 1) + j] = r;
+        if (r >= 0) m.delta_row[r] = b * (N - 1) + j;
+      }
+      for (int k = 0; k < m.items_per_slot; ++k) {
+        AttnItem it;
+        it.slot = b;
+        it.row0 = b * R + k * m.q_max;
+        it.nq = max(0, min(m.q_max, q_len - k * m.q_max));
+        it.pos0 = L + k * m.q_max;
+        m.items[b * m.items_per_slot + k] = it;
+      }
+      m.ctx_len[b] = L + q_len;
+    }
+    popped += total;
+  }
+  __syncthreads();
+  if (tid == 0) *m.n_free = s_nfree - popped;
+}
+
+// Free the pages beyond ceil(L/P) (all pages of a finished or empty slot), slots taken in
+// the given order (NULL = ascending), pushing in ascending logical page order.
+__global__ __launch_bounds__(256) void truncate_kernel(StepMeta m, const int32_t* order, int n) {
+  __shared__ int sh[256];
+  __shared__ int s_nfree;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_nfree = *m.n_free;
+  __syncthreads();
+  int pushed = 0;
+  for (int g0 = 0; g0 < n; g0 += 256) {
+    const int i = g0 + tid;
+    const bool valid = i < n;
+    const int b = valid ? (order ? order[i] : i) : 0;
+    int frees = 0, keep = 0, have = 0;
+    if (valid) {
+      const isd_slot& st = m.slots[b];
+      have = st.n_pages;
+      keep = (st.state == ISD_SLOT_A || st.state == ISD_SLOT_B) ? (st.L + m.P - 1) / m.P : 0;
+      frees = max(0, have - keep);
+    }
+    int total;
+    const int off = block_excl_scan(frees, sh, &total);
+    if (valid && frees > 0) {
+      int32_t* pt = m.page_table + (size_t)b * m.max_pages;
+      for (int k = 0; k < frees; ++k) {
+        m.free_stack[s_nfree + pushed + off + k] = pt[keep + k];
+        pt[keep + k] = -1;
+      }
+      m.slots[b].n_pages = keep;
+    }
+    pushed += total;
+  }
+  __syncthreads();
+  if (tid == 0) *m.n_free = s_nfree + pushed;
+}
+
+// Prefill set-up: slot by slot in call order, free the slot's old pages and take the
+// prompt's pages; reset the slot; write row metadata and the attention items.
+__global__ __launch_bounds__(256) void prefill_setup_kernel(StepMeta m, PrefillCall c, const int32_t* prompt_ids,
+                                                            int q_tile, int32_t* order_out) {
+  __shared__ int s_nfree;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_nfree = *m.n_free;
+  __syncthreads();
+  for (int i = 0; i < c.n; ++i) {
+    const int b = c.slot[i];
+    const int len = c.off[i + 1] - c.off[i];
+    isd_slot* st = &m.slots[b];
+    int32_t* pt = m.page_table + (size_t)b * m.max_pages;
+    const int old = st->n_pages;
+    for (int k = tid; k < old; k += 256) m.free_stack[s_nfree + k] = pt[k];
+    __syncthreads();
+    if (tid == 0) s_nfree += old;
+    __syncthreads();
+    const int np = (len + m.P - 1) / m.P;
+    for (int k = tid; k < np; k += 256) {
+      const int idx = s_nfree - 1 - k;
+      pt[k] = idx >= 0 ? m.free_stack[idx] : -1;
+    }
+    for (int k = np + tid; k < m.max_pages; k += 256) pt[k] = -1;
+    __syncthreads();
+    if (tid == 0) {
+      const int stat = s_nfree < np ? ISD_E_CAPACITY : 0;
+      s_nfree -= np;
+      st->state = ISD_SLOT_B;
+      st->L = len;
+      st->c = 0;
+      st->t = 0;
+      st->n_gen = 0;
+      st->max_new = c.max_new[i];
+      st->n_pages = np;
+      st->status = stat;
+      for (int j = 0; j < ISD_MAX_STRIDE - 1; ++j) {
+        st->pending[j] = -1;
+        st->q_row[j] = -1;
+      }
+      st->passes = st->accepted = st->verified = st->committed = 0;
+      m.ctx_len[b] = len;
+      m.last_rows[i] = c.off[i + 1] - 1;
+      order_out[i] = b;
+    }
+    for (int r = c.off[i] + tid; r < c.off[i + 1]; r += 256) {
+      m.row_tok[r] = prompt_ids[r];
+      m.row_pos[r] = r - c.off[i];
+      m.row_slot[r] = b;
+      m.delta_row[r] = -1;
+    }
+    const int nit = (len + q_tile - 1) / q_tile;
+    for (int k = tid; k < nit; k += 256) {
+      AttnItem it;
+      it.slot = b;
+      it.row0 = c.off[i] + k * q_tile;
+      it.nq = min(q_tile, len - k * q_tile);
+      it.pos0 = k * q_tile;
+      m.items[c.item_off[i] + k] = it;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) *m.n_free = s_nfree;
+}
+
+// Token ids outside [0, vocab] (vocab = MASK) read the MASK row.
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* tok, const T* table, float* X, int d, int mask_id) {
+  const int r = blockIdx.x;
+  int id = tok[r];
+  if (id < 0 || id > mask_id) id = mask_id;
+  const T* src = table + (size_t)id * d;
+  float* dst = X + (size_t)r * d;
+  for (int i = threadIdx.x; i < d; i += 256) dst[i] = to_f(src[i]);
+}
+
+// y = g * x / sqrt(mean(x^2) + eps), one block per row, fixed-order reduction.
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* X, const T* g, T* Y, int d, float eps) {
+  __shared__ float sh[4];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const float* x = X + (size_t)r * d;
+  float ss = 0.f;
+  for (int i = tid; i < d; i += 256) ss += x[i] * x[i];
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) sh[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+  const float denom = sqrtf(tot / (float)d + eps);
+  T* y = Y + (size_t)r * d;
+  for (int i = tid; i < d; i += 256) y[i] = from_f<T>((x[i] / denom) * to_f(g[i]));
+}
+
+// RoPE (rotate-half) on q and k, write q to q_out and k, v into the slot's pages at `pos`.
+// K page layout [Hkv][P][hd]; V page layout [Hkv][hd][P].
+template <typename T>
+__global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
+  const int r = blockIdx.x;
+  const int pos = a.row_pos[r];
+  const int hd = a.hd, half = hd / 2, P = a.P;
+  const int qd = a.Hq * hd, kd = a.Hkv * hd;
+  const T* src = (const T*)a.qkv + (size_t)r * (qd + 2 * kd);
+  T* qo = (T*)a.q_out + (size_t)r * qd;
+  if (pos < 0) {
+    for (int i = threadIdx.x; i < qd; i += 256) qo[i] = from_f<T>(0.f);
+    return;
+  }
+  const float* cs = a.cos_t + (size_t)pos * half;
+  const float* sn = a.sin_t + (size_t)pos * half;
+  const int slot = a.row_slot[r];
+  const int page = a.page_table[(size_t)slot * a.max_pages + pos / P];
+  const int tok = pos % P;
+  T* kp = (T*)a.k_pool;
+  T* vp = (T*)a.v_pool;
+  const int pairs_q = a.Hq * half, pairs_k = a.Hkv * half;
+  for (int i = threadIdx.x; i < pairs_q + pairs_k; i += 256) {
+    const bool isq = i < pairs_q;
+    const int j = isq ? i : i - pairs_q;
+    const int h = j / half, e = j % half;
+    const T* x = src + (isq ? 0 : qd) + (size_t)h * hd;
+    const float x1 = to_f(x[e]), x2 = to_f(x[e + half]);
+    const float c = cs[e], s = sn[e];
+    const float y1 = x1 * c - x2 * s, y2 = x2 * c + x1 * s;
+    if (isq) {
+      qo[h * hd + e] = from_f<T>(y1);
+      qo[h * hd + e + half] = from_f<T>(y2);
+    } else {
+      T* kr = kp + (((size_t)page * a.Hkv + h) * P + tok) * hd;
+      kr[e] = from_f<T>(y1);
+      kr[e + half] = from_f<T>(y2);
+    }
+  }
+  for (int i = threadIdx.x; i < kd; i += 256) {
+    const int h = i / hd, d = i % hd;
+    vp[(((size_t)page * a.Hkv + h) * hd + d) * P + tok] = src[qd + kd + i];
+  }
+}
+
+// cos/sin of pos * base^(-2i/hd), computed in double and rounded to float.
+__global__ void rope_tables_kernel(float* cos_t, float* sin_t, int max_pos, int hd, double base) {
+  const int half = hd / 2;
+  const size_t n = (size_t)max_pos * half;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (size_t)gridDim.x * blockDim.x) {
+    const int pos = (int)(idx / half), i = (int)(idx % half);
+    const double inv = pow(base, -2.0 * (double)i / (double)hd);
+    const double ang = (double)pos * inv;
+    cos_t[idx] = (float)cos(ang);
+    sin_t[idx] = (float)sin(ang);
+  }
+}
+
+// Context set-up: every slot EMPTY, page tables -1, free stack popping 0, 1, 2, ... first.
+__global__ void init_state_kernel(StepMeta m, int n_pages) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const size_t t0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (size_t i = t0; i < (size_t)n_pages; i += stride) m.free_stack[i] = n_pages - 1 - (int)i;
+  for (size_t i = t0; i < (size_t)m.max_batch * m.max_pages; i += stride) m.page_table[i] = -1;
+  int32_t* sw = (int32_t*)m.slots;
+  for (size_t i = t0; i < (size_t)m.max_batch * (sizeof(isd_slot) / 4); i += stride) sw[i] = 0;
+  if (t0 == 0) *m.n_free = n_pages;
+}
+
+}  // namespace
+
+hipError_t launch_init_state(const StepMeta& m, int n_pages, hipStream_t s) {
+  hipLaunchKernelGGL(init_state_kernel, dim3(256), dim3(256), 0, s, m, n_pages);
+  return hipGetLastError();
+}
+
+hipError_t launch_assemble(const StepMeta& m, hipStream_t s) {
+  hipLaunchKernelGGL(assemble_kernel, dim3(1), dim3(256), 0, s, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_truncate(const StepMeta& m, const int32_t* order, int n, hipStream_t s) {
+  hipLaunchKernelGGL(truncate_kernel, dim3(1), dim3(256), 0, s, m, order, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_setup(const StepMeta& m, const PrefillCall& c, const int32_t* prompt_ids, int q_tile,
+                                int32_t* order_out, hipStream_t s) {
+  hipLaunchKernelGGL(prefill_setup_kernel, dim3(1), dim3(256), 0, s, m, c, prompt_ids, q_tile, order_out);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_embed(const int32_t* tok, const T* table, float* X, int rows, int d, int mask_id, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(embed_kernel<T>, dim3(rows), dim3(256), 0, s, tok, table, X, d, mask_id);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_rmsnorm(const float* X, const T* g, T* Y, int rows, int d, float eps, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_kernel<T>, dim3(rows), dim3(256), 0, s, X, g, Y, d, eps);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_append_kernel<T>, dim3(a.rows), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_tables(float* cos_t, float* sin_t, int max_pos, int hd, float base, hipStream_t s) {
+  hipLaunchKernelGGL(rope_tables_kernel, dim3(256), dim3(256), 0, s, cos_t, sin_t, max_pos, hd, (double)base);
+  return hipGetLastError();
+}
+
+template hipError_t launch_embed<float>(const int32_t*, const float*, float*, int, int, int, hipStream_t);
+template hipError_t launch_embed<bf16>(const int32_t*, const bf16*, float*, int, int, int, hipStream_t);
+template hipError_t launch_rmsnorm<float>(const float*, const float*, float*, int, int, float, hipStream_t);
+template hipError_t launch_rmsnorm<bf16>(const float*, const bf16*, bf16*, int, int, float, hipStream_t);
+template hipError_t launch_rope_append<float>(const RopeAppendArgs&, hipStream_t);
+template hipError_t launch_rope_append<bf16>(const RopeAppendArgs&, hipStream_t);
+
+}  // namespace isd

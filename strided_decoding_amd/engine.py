@@ -1,0 +1,216 @@
+"""Thin Python front of libisd: torch provides device memory and streams, every step of
+the decode path runs in the library's HIP kernels.
+"""
+import ctypes as C
+
+import numpy as np
+import torch
+
+from . import _abi as A
+
+LORA_ORDER = ("q", "k", "v", "o", "g", "u", "d")
+
+
+def _dt(dtype):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def to_device(a, dtype, device):
+    """numpy float32 array or uint16 bf16-bit array -> contiguous device tensor of `dtype`."""
+    if isinstance(a, torch.Tensor):
+        return a.to(device=device, dtype=_dt(dtype)).contiguous()
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(a.astype(np.float32))
+    return t.to(device=device, dtype=_dt(dtype)).contiguous()
+
+
+class Engine:
+    """One decoding context: weights, KV pool and workspace resident on `device`.
+
+    shape: isd_inputs.ModelShape; weights / lora: nested like isd_inputs.weights_numpy /
+    lora_numpy (numpy or torch tensors).
+    """
+
+    def __init__(self, shape, weights, *, stride, temperature, propose="sample", seed=1, max_batch=1,
+                 max_seq_len=256, n_pages=None, max_prefill_tokens=None, lora=None, page_size=16,
+                 device="cuda:0", stream=None):
+        self.lib = A.load()
+        self.shape = shape
+        self.device = torch.device(device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        dt = shape.dtype
+        self.N = stride
+        self.R = 2 * stride - 1
+        self.max_batch = max_batch
+        lora_rank = 0 if lora is None else int(lora[0]["q"][0].shape[0])
+        if n_pages is None:
+            n_pages = max_batch * (-(-(max_seq_len + 2 * stride) // page_size))
+        if max_prefill_tokens is None:
+            max_prefill_tokens = max_batch * max_seq_len
+        cfg = A.Config(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                       shape.d_ffn, shape.vocab, shape.rope_base, shape.rms_eps,
+                       A.ISD_BF16 if dt == "bf16" else A.ISD_F32, stride, page_size, max_batch, max_seq_len,
+                       n_pages, max_prefill_tokens, lora_rank,
+                       A.ISD_PROPOSE_ARGMAX if propose == "argmax" else A.ISD_PROPOSE_SAMPLE,
+                       float(temperature), int(seed))
+        self.cfg = cfg
+        # weights (kept alive by this object)
+        dev = self.device
+        self.w = {k: to_device(weights[k], dt, dev) for k in ("embed", "final_norm", "lm_head")}
+        self.wl = [{k: to_device(v, dt, dev) for k, v in layer.items()} for layer in weights["layers"]]
+        self.lora = None
+        if lora is not None:
+            self.lora = [{m: (to_device(layer[m][0], dt, dev), to_device(layer[m][1], dt, dev))
+                          for m in LORA_ORDER} for layer in lora]
+
+        def arr(name):
+            return (C.c_void_p * len(self.wl))(*[t[name].data_ptr() for t in self.wl])
+
+        self._arrs = {n: arr(n) for n in ("attn_norm", "wqkv", "wo", "ffn_norm", "wg", "wu", "wd")}
+        la = lb = None
+        if self.lora is not None:
+            la = (C.c_void_p * (7 * len(self.lora)))(*[l[m][0].data_ptr() for l in self.lora for m in LORA_ORDER])
+            lb = (C.c_void_p * (7 * len(self.lora)))(*[l[m][1].data_ptr() for l in self.lora for m in LORA_ORDER])
+        self._la, self._lb = la, lb
+        cast = lambda x: C.cast(x, A.PP) if x is not None else None
+        self.cw = A.Weights(self.w["embed"].data_ptr(), self.w["final_norm"].data_ptr(),
+                            self.w["lm_head"].data_ptr(), *[cast(self._arrs[n]) for n in
+                                                            ("attn_norm", "wqkv", "wo", "ffn_norm", "wg", "wu", "wd")],
+                            cast(la), cast(lb))
+        sizes = A.Sizes()
+        ctx = C.c_void_p()
+        A.check("isd_init(size query)", self.lib.isd_init(C.byref(cfg), C.byref(self.cw), None, None,
+                                                          C.byref(sizes), C.byref(ctx), None))
+        self.sizes = (sizes.kv_pool_bytes, sizes.workspace_bytes)
+        self.kv_pool = torch.empty(sizes.kv_pool_bytes, dtype=torch.uint8, device=dev)
+        self.workspace = torch.empty(sizes.workspace_bytes, dtype=torch.uint8, device=dev)
+        A.check("isd_init", self.lib.isd_init(C.byref(cfg), C.byref(self.cw), self.kv_pool.data_ptr(),
+                                              self.workspace.data_ptr(), C.byref(sizes), C.byref(ctx),
+                                              self._s()))
+        self.ctx = ctx
+        self.tokens = torch.full((max_batch, stride), -1, dtype=torch.int32, device=dev)
+        self.n_commit = torch.zeros(max_batch, dtype=torch.int32, device=dev)
+        self.n_accept = torch.zeros(max_batch, dtype=torch.int32, device=dev)
+        b = A.Buffers()
+        A.check("isd_get_buffers", self.lib.isd_get_buffers(self.ctx, C.byref(b)))
+        self._buf = b
+
+    def _s(self):
+        return C.c_void_p(self.stream.cuda_stream)
+
+    def __del__(self):
+        try:
+            if getattr(self, "ctx", None) is not None and self.ctx.value:
+                self.lib.isd_release(self.ctx)
+                self.ctx = None
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------------ calls
+    def prefill(self, slots, prompts, max_new):
+        n = len(slots)
+        lens = [len(p) for p in prompts]
+        offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        ids = torch.from_numpy(np.concatenate([np.asarray(p, np.int32) for p in prompts])).to(self.device)
+        self._prompt_ids = ids
+        first = torch.empty(n, dtype=torch.int32, device=self.device)
+        cs = (C.c_int32 * n)(*slots)
+        co = (C.c_int32 * (n + 1))(*offs.tolist())
+        cm = (C.c_int32 * n)(*max_new)
+        A.check("isd_prefill", self.lib.isd_prefill(self.ctx, n, cs, ids.data_ptr(), co, cm, first.data_ptr(),
+                                                    self._s()))
+        return first
+
+    def step(self):
+        A.check("isd_step", self.lib.isd_step(self.ctx, self.tokens.data_ptr(), self.n_commit.data_ptr(),
+                                              self.n_accept.data_ptr(), self._s()))
+        return self.tokens, self.n_commit, self.n_accept
+
+    def status(self):
+        return self.lib.isd_get_status(self.ctx, self._s())
+
+    # ------------------------------------------------------------------ views
+    def _view(self, ptr, nbytes, dtype, shape):
+        off = ptr - self.workspace.data_ptr()
+        return self.workspace[off:off + nbytes].view(dtype).view(shape)
+
+    def slots_view(self):
+        return self._view(self._buf.slots, self.max_batch * A.SLOT_INTS * 4, torch.int32,
+                          (self.max_batch, A.SLOT_INTS))
+
+    def slots_host(self):
+        """Per-slot state as a list of dicts (synchronizes)."""
+        torch.cuda.synchronize(self.device)
+        a = self.slots_view().cpu().numpy()
+        return [dict(zip(A.SLOT_FIELDS, row.tolist())) for row in a]
+
+    def page_table(self):
+        mp = self._buf.max_pages_per_slot
+        return self._view(self._buf.page_table, self.max_batch * mp * 4, torch.int32, (self.max_batch, mp))
+
+    def free_stack(self):
+        n = int(self._view(self._buf.n_free, 4, torch.int32, (1,)).item())
+        return self._view(self._buf.free_stack, self.cfg.n_pages * 4, torch.int32, (self.cfg.n_pages,))[:n]
+
+    def logits(self):
+        """Logits of the last decode pass [max_batch, 2N-1, V] (float32)."""
+        V = self.shape.vocab
+        rows = self.max_batch * self.R
+        return self._view(self._buf.logits, rows * V * 4, torch.float32, (self.max_batch, self.R, V))
+
+    def rows(self):
+        n = self.max_batch * self.R
+        tok = self._view(self._buf.row_token, n * 4, torch.int32, (self.max_batch, self.R))
+        pos = self._view(self._buf.row_pos, n * 4, torch.int32, (self.max_batch, self.R))
+        return tok, pos
+
+    def kv_pools(self):
+        """(K, V) pools: K [L, n_pages, Hkv, P, hd], V [L, n_pages, Hkv, hd, P] (act dtype)."""
+        s = self.shape
+        dt = _dt(s.dtype)
+        el = self.kv_pool.numel() // 2
+        kp = self.kv_pool[:el].view(dt).view(s.n_layers, self.cfg.n_pages, s.n_kv_heads, self.cfg.page_size,
+                                              s.head_dim)
+        vp = self.kv_pool[el:].view(dt).view(s.n_layers, self.cfg.n_pages, s.n_kv_heads, s.head_dim,
+                                              self.cfg.page_size)
+        return kp, vp
+
+
+def attn_paged(q, k_pool, v_pool, page_table, ctx_len, q_len, n_kv_heads, out=None, workspace=None, stream=None):
+    """Kernel-level paged attention (see isd_attn_paged).  q [B, R, Hq, hd] bf16 on device."""
+    lib = A.load()
+    B, R, Hq, hd = q.shape
+    P = k_pool.shape[2]
+    args = A.AttnArgs(B, R, Hq, n_kv_heads, hd, P, page_table.shape[1], int(ctx_len.max().item()),
+                      q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), page_table.data_ptr(),
+                      ctx_len.data_ptr(), q_len.data_ptr(), 0, 0)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = torch.empty(lib.isd_attn_workspace_bytes(C.byref(args)), dtype=torch.uint8, device=q.device)
+    args.out = out.data_ptr()
+    args.workspace = workspace.data_ptr()
+    stream = stream if stream is not None else torch.cuda.current_stream(q.device)
+    A.check("isd_attn_paged", lib.isd_attn_paged(C.byref(args), C.c_void_p(stream.cuda_stream)))
+    return out, workspace, args
+
+
+def sample(slots, logits, q_logits, stride, temperature, propose, seed, tokens, n_commit, n_accept,
+           workspace=None, stream=None):
+    """Kernel-level acceptance step (see isd_sample).  slots: int32 [B, 32] device tensor (in/out)."""
+    lib = A.load()
+    B, R, V = logits.shape
+    q_rows = 0 if q_logits is None else q_logits.shape[0]
+    if workspace is None:
+        workspace = torch.empty(lib.isd_sample_workspace_bytes(B, R, V, q_rows), dtype=torch.uint8,
+                                device=logits.device)
+    args = A.SampleArgs(B, stride, V, A.ISD_PROPOSE_ARGMAX if propose == "argmax" else A.ISD_PROPOSE_SAMPLE,
+                        q_rows, float(temperature), int(seed), slots.data_ptr(), logits.data_ptr(),
+                        0 if q_logits is None else q_logits.data_ptr(), tokens.data_ptr(), n_commit.data_ptr(),
+                        n_accept.data_ptr(), workspace.data_ptr())
+    stream = stream if stream is not None else torch.cuda.current_stream(logits.device)
+    A.check("isd_sample", lib.isd_sample(C.byref(args), C.c_void_p(stream.cuda_stream)))
+    return workspace

@@ -1,0 +1,173 @@
+"""GPU parity of whole decode passes through the C ABI (isd_prefill / isd_step).
+
+Teacher-forced: before every pass the oracle holds the GPU's slot state (committed
+tokens, pending tokens, L, state), runs its own forward and decisions, the two are
+compared, and the oracle then adopts the GPU's resulting state.
+  * fp32 path (tiny model): logits max-abs <= 1e-4; the decisions the oracle takes on its
+    own logits must equal the GPU's, except near-ties (acceptance |u - min(1,p/q)| < 1e-3,
+    categorical draw within 1e-5 of an interval edge relative to the mass), counted.
+  * bf16 path: logits ||gpu - oracle||_inf <= 2e-2 ||oracle||_inf per row; the decisions
+    are checked on the GPU's own logits (both sides decide in the same precision).
+Page tables and the free stack are compared bit-exactly with the oracle's allocator while
+every slot is in lock-step.
+"""
+import numpy as np
+import pytest
+import torch
+
+import isd_inputs as I
+from oracle import isd as OI
+from oracle import model as M
+from oracle import philox, sampler
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+ACC_TAU, CAT_TAU = 1e-3, 1e-5
+STATE_NAME = {1: "A", 2: "B", 3: "DONE", 0: "EMPTY"}
+
+
+def spec_of(s):
+    return M.Spec(s.n_layers, s.d_model, s.n_q_heads, s.n_kv_heads, s.head_dim, s.d_ffn, s.vocab, s.rope_base,
+                  s.rms_eps)
+
+
+def make_engine(shape, w, N, T, propose, B, max_seq, lora=None, seed=1, n_pages=None):
+    from strided_decoding_amd import Engine
+    return Engine(shape, w, stride=N, temperature=T, propose=propose, seed=seed, max_batch=B,
+                  max_seq_len=max_seq, lora=lora, n_pages=n_pages)
+
+
+def _near(decisions, T):
+    return any((d.kind == "accept" and d.margin < ACC_TAU) or (d.kind != "accept" and T > 0 and d.margin < CAT_TAU)
+               for d in decisions)
+
+
+def _adopt(dec, model, b, g, committed, rec_logits, R, N, T, propose):
+    """Make the oracle slot equal the GPU's state (cache rebuilt when L differs)."""
+    st = dec.slots[b]
+    st.committed = list(committed)
+    st.n_gen = len(committed) - st.prompt_len
+    st.c = g["c"]
+    st.t = g["t"]
+    st.state = STATE_NAME[g["state"]]
+    st.pending, st.pending_q = [], []
+    if st.state == "A":
+        for j in range(N - 1):
+            st.pending.append(g[f"pending{j}"])
+            qr = g[f"q_row{j}"]
+            if qr >= 0 and T > 0 and propose == "sample":
+                st.pending_q.append(sampler.weights_T(rec_logits[qr - b * R], T)[:2])
+            else:
+                st.pending_q.append(None)
+    if g["L"] != st.L:
+        st.L = g["L"]
+        _, kv = model.forward(st.committed[:st.L], np.arange(st.L), M.empty_cache(model.spec))
+        st.cache = M.extend_cache(M.empty_cache(model.spec), kv, st.L)
+    if st.state == "DONE":
+        dec.pool.truncate(b, 0)
+
+
+def teacher_forced(shape, w, N, T, propose, prompts, max_new, steps, lora=None, on_gpu_logits=False,
+                   logits_tol=1e-4, rel=False):
+    B = len(prompts)
+    max_seq = max(len(p) for p in prompts) + max(max_new) + 2 * N + 2
+    eng = make_engine(shape, w, N, T, propose, B, max_seq, lora=lora)
+    model = M.Model(spec_of(shape), w, lora)
+    dec = OI.Decoder(model, N, T, propose=propose, seed=1, page_size=16, n_pages=eng.cfg.n_pages,
+                     keep_logits=True)
+    slots = list(range(B))
+    print(f"e2e {shape.name} N={N} T={T} {propose} B={B}", flush=True)
+    first = eng.prefill(slots, prompts, max_new).cpu().numpy()
+    ofirst = dec.prefill(slots, prompts, max_new)
+    near, lockstep = 0, True
+    committed = [[int(x) for x in p] + [int(first[b])] for b, p in enumerate(prompts)]
+    for b in range(B):
+        if first[b] != ofirst[b]:
+            logits, _ = model.forward(prompts[b], np.arange(len(prompts[b])), M.empty_cache(model.spec))
+            _, m = OI.draw(logits[-1], philox.uniform(1, b, 0, len(prompts[b]), 1), T)
+            assert T > 0 and m < CAT_TAU, ("first token differs", b, m)
+            near += 1
+            lockstep = False
+            dec.slots[b].committed[-1] = int(first[b])
+            dec.slots[b].c = int(first[b])
+    R = 2 * N - 1
+    n_steps, max_err = 0, 0.0
+    for _ in range(steps):
+        if all(st.state == "DONE" for st in dec.slots.values()):
+            break
+        snap = {b: (dec.slots[b].state, dec.slots[b].L, dec.slots[b].t, list(dec.slots[b].pending),
+                    list(dec.slots[b].pending_q)) for b in slots}
+        tok, nc, na = eng.step()
+        recs = dec.step()
+        n_steps += 1
+        torch.cuda.synchronize()
+        g_tok, g_nc, g_na = tok.cpu().numpy(), nc.cpu().numpy(), na.cpu().numpy()
+        g_logits = eng.logits().cpu().numpy()
+        gs = eng.slots_host()
+        for b in slots:
+            if b not in recs:
+                assert g_nc[b] == 0
+                continue
+            rec = recs[b]
+            nrows = len(rec.ids)
+            ol, gl = rec.logits, g_logits[b, :nrows]
+            if rel:
+                err = float((np.abs(gl - ol).max(axis=1) / np.maximum(np.abs(ol).max(axis=1), 1e-6)).max())
+            else:
+                err = float(np.abs(gl - ol).max())
+            assert err <= logits_tol, (b, err)
+            max_err = max(max_err, err)
+            if on_gpu_logits:
+                state, L, t, pend, pq = snap[b]
+                out = OI.decide(state, L, t, b, pend, pq, gl, N, T, propose, 1)
+                room = max_new[b] - (len(committed[b]) - len(prompts[b]))
+                decisions, otoks, onacc = out.decisions, out.tokens[:room], out.n_accept
+            else:
+                decisions, otoks, onacc = rec.decisions, rec.tokens, rec.n_accept
+            gt = [int(x) for x in g_tok[b, :g_nc[b]]]
+            if gt != list(otoks) or g_na[b] != onacc:
+                assert _near(decisions, T), (b, gt, otoks, [(d.kind, d.token, d.margin) for d in decisions])
+                near += 1
+                lockstep = False
+            committed[b] += gt
+        if lockstep:
+            pt = eng.page_table().cpu().numpy()
+            for b in slots:
+                np.testing.assert_array_equal(pt[b], dec.pool.table_array(b, pt.shape[1]))
+            np.testing.assert_array_equal(eng.free_stack().cpu().numpy(), np.array(dec.pool.stack, np.int32))
+        for b in slots:
+            if b in recs:
+                q_src = g_logits[b] if on_gpu_logits else recs[b].logits
+                _adopt(dec, model, b, gs[b], committed[b], q_src, R, N, T, propose)
+    print(f"steps={n_steps} near_ties={near} max_logit_err={max_err:.3g}", flush=True)
+    return eng, dec, committed, near
+
+
+def test_tiny_fp32_end_to_end():
+    wl = I.TINY_E2E
+    w = I.weights_numpy(wl.model)
+    prompts = list(I.prompts(wl.batch, wl.prompt_len, wl.model.vocab))
+    eng, dec, committed, near = teacher_forced(wl.model, w, wl.stride, wl.temperature, wl.propose, prompts,
+                                               [wl.max_new] * wl.batch, steps=64)
+    for b in range(wl.batch):
+        assert len(committed[b]) - wl.prompt_len == wl.max_new
+    assert near <= 6
+    st = eng.slots_host()
+    assert all(s["state"] == 3 for s in st[:wl.batch])
+    assert int(eng.free_stack().numel()) == eng.cfg.n_pages
+
+
+@pytest.mark.parametrize("N,T,propose", [(3, 1.0, "argmax"), (4, 0.0, "argmax"), (1, 1.0, "sample")])
+def test_tiny_fp32_variants(N, T, propose):
+    shape = I.ModelShape("tiny-gqa", 2, 128, 4, 2, 32, 256, 512, "f32")
+    w = I.weights_numpy(shape, seed=4, scale=8.0)
+    prompts = I.ragged_prompts([5, 17, 33], shape.vocab, seed=6)
+    teacher_forced(shape, w, N, T, propose, prompts, [20, 9, 15], steps=40)
+
+
+def test_small_bf16_end_to_end():
+    shape = I.SMALL_BF16
+    w = I.weights_numpy(shape, seed=0, scale=20.0)
+    prompts = I.ragged_prompts([40, 7, 130, 19], shape.vocab, seed=3)
+    teacher_forced(shape, w, 4, 1.0, "sample", prompts, [12, 20, 8, 16], steps=14, logits_tol=2e-2, rel=True,
+                   on_gpu_logits=True)
