@@ -118,7 +118,7 @@ typedef struct {
   int32_t q_row[ISD_MAX_STRIDE - 1];     /* logits row (previous pass) that proposed pending[i];
                                             -1: delta q (argmax proposal) */
   int32_t passes, accepted, verified, committed;   /* cumulative counters */
-  int32_t pad[2];
+  int32_t pad[6];
 } isd_slot;
 
 typedef struct isd_ctx isd_ctx;
@@ -184,6 +184,21 @@ isd_status isd_get_status(isd_ctx* ctx, void* stream);
 
 /* Free the host-side context. */
 isd_status isd_release(isd_ctx* ctx);
+
+/* Kernel timing for benchmarks.  isd_profile(ctx, 1) starts recording a HIP event pair
+ * around every kernel the context launches (on the launch stream); isd_profile(ctx, 0) stops.
+ * isd_profile_report synchronizes the recorded events and returns, per kernel name, the
+ * number of launches and their summed duration, then clears the record.  At most `cap`
+ * entries are written; *n receives the number of distinct names.  Recording is bounded
+ * (ISD_E_CAPACITY from isd_step/isd_prefill when the event pool is exhausted). */
+typedef struct {
+  char name[32];
+  int32_t launches;
+  double total_ms;
+} isd_prof_entry;
+
+isd_status isd_profile(isd_ctx* ctx, int32_t enable);
+isd_status isd_profile_report(isd_ctx* ctx, isd_prof_entry* out, int32_t cap, int32_t* n);
 
 /* ---------------------------------------------------------------------------------------
  * Kernel-level entry points (used by the attention + acceptance microbench).

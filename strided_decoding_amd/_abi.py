@@ -20,7 +20,11 @@ ISD_SLOT_EMPTY, ISD_SLOT_A, ISD_SLOT_B, ISD_SLOT_DONE = 0, 1, 2, 3
 # symbols the header declares (checked by the CPU test-suite)
 EXPORTS = ("isd_init", "isd_prefill", "isd_step", "isd_get_buffers", "isd_get_status", "isd_release",
            "isd_attn_workspace_bytes", "isd_attn_paged", "isd_sample_workspace_bytes", "isd_sample",
-           "isd_version")
+           "isd_version", "isd_profile", "isd_profile_report")
+
+
+class ProfEntry(C.Structure):
+    _fields_ = [("name", C.c_char * 32), ("launches", C.c_int32), ("total_ms", C.c_double)]
 
 
 class IsdError(RuntimeError):
@@ -54,7 +58,7 @@ class Sizes(C.Structure):
 SLOT_INTS = 32   # isd_slot is 32 int32 words
 SLOT_FIELDS = ["state", "L", "c", "t", "n_gen", "max_new", "n_pages", "status"] + \
     [f"pending{i}" for i in range(ISD_MAX_STRIDE - 1)] + [f"q_row{i}" for i in range(ISD_MAX_STRIDE - 1)] + \
-    ["passes", "accepted", "verified", "committed", "pad0", "pad1"]
+    ["passes", "accepted", "verified", "committed"] + [f"pad{i}" for i in range(6)]
 
 
 class Buffers(C.Structure):
@@ -106,8 +110,10 @@ def load(path=LIB_PATH):
     lib.isd_sample_workspace_bytes.restype = C.c_size_t
     lib.isd_sample.argtypes = [C.POINTER(SampleArgs), C.c_void_p]
     lib.isd_version.restype = C.c_char_p
+    lib.isd_profile.argtypes = [C.c_void_p, C.c_int32]
+    lib.isd_profile_report.argtypes = [C.c_void_p, C.POINTER(ProfEntry), C.c_int32, C.POINTER(C.c_int32)]
     for f in ("isd_init", "isd_prefill", "isd_step", "isd_get_buffers", "isd_get_status", "isd_release",
-              "isd_attn_paged", "isd_sample"):
+              "isd_attn_paged", "isd_sample", "isd_profile", "isd_profile_report"):
         getattr(lib, f).restype = C.c_int
     _lib = lib
     return lib

@@ -71,7 +71,40 @@ struct isd_ctx {
   std::vector<long long> reserved;   // admission reservation per slot (pages)
   long long reserved_total = 0;
   isd_status sticky = ISD_OK;
+  // kernel timing (isd_profile)
+  bool prof_on = false;
+  bool prof_overflow = false;
+  std::vector<hipEvent_t> ev_pool;
+  std::vector<std::pair<const char*, int>> prof_recs;
+  int ev_used = 0;
 };
+
+namespace {
+
+constexpr int kProfEvents = 1 << 15;
+
+// Records a HIP event pair around the launches in its scope when profiling is on.
+struct ProfScope {
+  isd_ctx& x;
+  hipStream_t s;
+  int idx = -1;
+  ProfScope(isd_ctx& x_, const char* name, hipStream_t s_) : x(x_), s(s_) {
+    if (!x.prof_on) return;
+    if (x.ev_used + 2 > (int)x.ev_pool.size()) {
+      x.prof_overflow = true;
+      return;
+    }
+    idx = x.ev_used;
+    x.ev_used += 2;
+    hipEventRecord(x.ev_pool[idx], s);
+    x.prof_recs.emplace_back(name, idx);
+  }
+  ~ProfScope() {
+    if (idx >= 0) hipEventRecord(x.ev_pool[idx + 1], s);
+  }
+};
+
+}  // namespace
 
 namespace {
 
@@ -195,6 +228,17 @@ StepMeta meta(isd_ctx& x) {
   do {                                     \
     if ((expr) != hipSuccess) return ISD_E_HIP; \
   } while (0)
+// launch under a profiling scope (context reference `x` / context pointer `x`, stream `s`)
+#define TIMED(name, expr)                  \
+  do {                                     \
+    ProfScope p_(x, name, s);              \
+    HIP_OK(expr);                          \
+  } while (0)
+#define TIMEDP(name, expr)                 \
+  do {                                     \
+    ProfScope p_(*x, name, s);             \
+    HIP_OK(expr);                          \
+  } while (0)
 
 hipError_t gemm(const isd_ctx& x, const GemmArgs& g, hipStream_t s) {
   return x.bf ? launch_gemm_bf16(g, s) : launch_gemm_f32(g, s);
@@ -223,11 +267,11 @@ isd_status lora_target(isd_ctx& x, int layer, int tgt, const void* Xsrc, int ldx
   g.a_rows = x.mask_rows;
   g.C = (char*)x.lora_s + (size_t)s_off * x.act;
   g.ldc = 3 * r;
-  HIP_OK(gemm(x, g, s));
+  TIMED("lora_shrink", gemm(x, g, s));
   GemmArgs e = gargs((const char*)x.lora_s + (size_t)s_off * x.act, 3 * r, Bm, r, M, n_out, r, EPI_STORE_F32);
   e.C = x.lora_delta + d_off;
   e.ldc = x.delta_w;
-  HIP_OK(gemm(x, e, s));
+  TIMED("lora_expand", gemm(x, e, s));
   return ISD_OK;
 }
 
@@ -244,14 +288,14 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
                    hipStream_t s) {
   const isd_config& c = x.cfg;
   const int d = c.d_model, F = c.d_ffn, Hq = c.n_q_heads, Hkv = c.n_kv_heads, hd = c.head_dim;
-  if (x.bf) HIP_OK(launch_embed<bf16>(x.row_tok, (const bf16*)x.embed, x.X, M, d, c.vocab, s));
-  else HIP_OK(launch_embed<float>(x.row_tok, (const float*)x.embed, x.X, M, d, c.vocab, s));
+  if (x.bf) TIMED("embed", launch_embed<bf16>(x.row_tok, (const bf16*)x.embed, x.X, M, d, c.vocab, s));
+  else TIMED("embed", launch_embed<float>(x.row_tok, (const float*)x.embed, x.X, M, d, c.vocab, s));
   for (int l = 0; l < c.n_layers; ++l) {
     char* kl = x.k_pool + (size_t)l * x.kv_layer_bytes;
     char* vl = x.v_pool + (size_t)l * x.kv_layer_bytes;
     // attention block
-    if (x.bf) HIP_OK(launch_rmsnorm<bf16>(x.X, (const bf16*)x.attn_norm[l], (bf16*)x.Xn, M, d, c.rms_eps, s));
-    else HIP_OK(launch_rmsnorm<float>(x.X, (const float*)x.attn_norm[l], (float*)x.Xn, M, d, c.rms_eps, s));
+    if (x.bf) TIMED("rmsnorm", launch_rmsnorm<bf16>(x.X, (const bf16*)x.attn_norm[l], (bf16*)x.Xn, M, d, c.rms_eps, s));
+    else TIMED("rmsnorm", launch_rmsnorm<float>(x.X, (const float*)x.attn_norm[l], (float*)x.Xn, M, d, c.rms_eps, s));
     if (lora) {
       const int r = c.lora_rank;
       const char* wq = nullptr;
@@ -266,7 +310,7 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
       g.C = x.QKV;
       g.ldc = x.qkvw;
       with_delta(x, g, lora);
-      HIP_OK(gemm(x, g, s));
+      TIMED("gemm_qkv", gemm(x, g, s));
     }
     {
       RopeAppendArgs ra{};
@@ -285,8 +329,8 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
       ra.Hkv = Hkv;
       ra.hd = hd;
       ra.P = c.page_size;
-      if (x.bf) HIP_OK(launch_rope_append<bf16>(ra, s));
-      else HIP_OK(launch_rope_append<float>(ra, s));
+      if (x.bf) TIMED("rope_append", launch_rope_append<bf16>(ra, s));
+      else TIMED("rope_append", launch_rope_append<float>(ra, s));
     }
     {
       AttnArgs aa{};
@@ -308,18 +352,18 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
       aa.row_slot = x.row_slot;
       aa.n_rows = M;
       if (!x.bf) {
-        HIP_OK(launch_attn_f32(aa, s));
+        TIMED("attention", launch_attn_f32(aa, s));
       } else if (decode) {
         aa.split = kAttnSplit;
         aa.max_splits = x.max_splits;
         aa.part_o = x.part_o;
         aa.part_ml = x.part_ml;
         aa.part_rows = x.max_dec_rows;
-        HIP_OK(launch_attn_bf16(aa, s));
-        HIP_OK(launch_attn_combine_bf16(aa, s));
+        TIMED("attention", launch_attn_bf16(aa, s));
+        TIMED("attn_combine", launch_attn_combine_bf16(aa, s));
       } else {
         aa.split = 0;
-        HIP_OK(launch_attn_bf16(aa, s));
+        TIMED("attention", launch_attn_bf16(aa, s));
       }
     }
     if (lora) {
@@ -331,11 +375,11 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
       g.R = x.X;
       g.ldr = d;
       with_delta(x, g, lora);
-      HIP_OK(gemm(x, g, s));
+      TIMED("gemm_o", gemm(x, g, s));
     }
     // FFN block
-    if (x.bf) HIP_OK(launch_rmsnorm<bf16>(x.X, (const bf16*)x.ffn_norm[l], (bf16*)x.Xn, M, d, c.rms_eps, s));
-    else HIP_OK(launch_rmsnorm<float>(x.X, (const float*)x.ffn_norm[l], (float*)x.Xn, M, d, c.rms_eps, s));
+    if (x.bf) TIMED("rmsnorm", launch_rmsnorm<bf16>(x.X, (const bf16*)x.ffn_norm[l], (bf16*)x.Xn, M, d, c.rms_eps, s));
+    else TIMED("rmsnorm", launch_rmsnorm<float>(x.X, (const float*)x.ffn_norm[l], (float*)x.Xn, M, d, c.rms_eps, s));
     if (lora) {
       const int r = c.lora_rank;
       isd_status st;
@@ -349,7 +393,7 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
       g.ldc = F;
       with_delta(x, g, lora);
       g.delta_off2 = F;
-      HIP_OK(gemm(x, g, s));
+      TIMED("gemm_gate_up", gemm(x, g, s));
     }
     if (lora) {
       isd_status st = lora_target(x, l, 6, x.H, F, F, d, 0, 0, s);
@@ -360,16 +404,16 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
       g.R = x.X;
       g.ldr = d;
       with_delta(x, g, lora);
-      HIP_OK(gemm(x, g, s));
+      TIMED("gemm_down", gemm(x, g, s));
     }
   }
-  if (x.bf) HIP_OK(launch_rmsnorm<bf16>(x.X, (const bf16*)x.final_norm, (bf16*)x.Xn, M, d, c.rms_eps, s));
-  else HIP_OK(launch_rmsnorm<float>(x.X, (const float*)x.final_norm, (float*)x.Xn, M, d, c.rms_eps, s));
+  if (x.bf) TIMED("rmsnorm", launch_rmsnorm<bf16>(x.X, (const bf16*)x.final_norm, (bf16*)x.Xn, M, d, c.rms_eps, s));
+  else TIMED("rmsnorm", launch_rmsnorm<float>(x.X, (const float*)x.final_norm, (float*)x.Xn, M, d, c.rms_eps, s));
   GemmArgs g = gargs(x.Xn, d, x.lm_head, d, lm_M, c.vocab, d, EPI_STORE_F32);
   g.a_rows = lm_rows;
   g.C = x.logits[x.cur];
   g.ldc = c.vocab;
-  HIP_OK(gemm(x, g, s));
+  TIMED("lm_head", gemm(x, g, s));
   return ISD_OK;
 }
 
@@ -493,10 +537,10 @@ isd_status isd_prefill(isd_ctx* x, int32_t n, const int32_t* slots, const int32_
   }
   hipStream_t s = (hipStream_t)stream;
   StepMeta m = meta(*x);
-  HIP_OK(launch_prefill_setup(m, call, prompt_ids, x->q_tile, x->order, s));
+  TIMEDP("prefill_setup", launch_prefill_setup(m, call, prompt_ids, x->q_tile, x->order, s));
   isd_status st = forward(*x, M, call.item_off[n], /*decode=*/false, x->last_rows, n, /*lora=*/false, s);
   if (st != ISD_OK) return st;
-  HIP_OK(launch_row_stats(x->logits[x->cur], n, c.vocab, c.temperature, x->stats[x->cur], s));
+  TIMEDP("row_stats", launch_row_stats(x->logits[x->cur], n, c.vocab, c.temperature, x->stats[x->cur], s));
   SampleArgs a = sargs(*x);
   a.n_slots = n;
   a.slot_ids = x->order;
@@ -505,8 +549,8 @@ isd_status isd_prefill(isd_ctx* x, int32_t n, const int32_t* slots, const int32_
   a.stats = x->stats[x->cur];
   a.prefill = 1;
   a.first_tok = first_tok;
-  HIP_OK(launch_decide(a, s));
-  HIP_OK(launch_truncate(m, x->order, n, s));
+  TIMEDP("decide", launch_decide(a, s));
+  TIMEDP("truncate", launch_truncate(m, x->order, n, s));
   x->prefilled = true;
   return ISD_OK;
 }
@@ -517,13 +561,13 @@ isd_status isd_step(isd_ctx* x, int32_t* tokens, int32_t* n_commit, int32_t* n_a
   const isd_config& c = x->cfg;
   hipStream_t s = (hipStream_t)stream;
   StepMeta m = meta(*x);
-  HIP_OK(launch_assemble(m, s));
+  TIMEDP("assemble", launch_assemble(m, s));
   const int M = x->max_dec_rows;
   isd_status st = forward(*x, M, c.max_batch * x->items_per_slot, /*decode=*/true, nullptr, M,
                           /*lora=*/c.lora_rank > 0 && c.stride_n > 1, s);
   if (st != ISD_OK) return st;
   const int cur = x->cur, prev = cur ^ 1;
-  HIP_OK(launch_row_stats(x->logits[cur], M, c.vocab, c.temperature, x->stats[cur], s));
+  TIMEDP("row_stats", launch_row_stats(x->logits[cur], M, c.vocab, c.temperature, x->stats[cur], s));
   SampleArgs a = sargs(*x);
   a.n_slots = c.max_batch;
   a.logits = x->logits[cur];
@@ -535,8 +579,8 @@ isd_status isd_step(isd_ctx* x, int32_t* tokens, int32_t* n_commit, int32_t* n_a
   a.tokens = tokens;
   a.n_commit = n_commit;
   a.n_accept = n_accept;
-  HIP_OK(launch_decide(a, s));
-  HIP_OK(launch_truncate(m, nullptr, c.max_batch, s));
+  TIMEDP("decide", launch_decide(a, s));
+  TIMEDP("truncate", launch_truncate(m, nullptr, c.max_batch, s));
   x->cur = prev;
   return ISD_OK;
 }
@@ -571,8 +615,50 @@ isd_status isd_get_status(isd_ctx* x, void* stream) {
 
 isd_status isd_release(isd_ctx* x) {
   if (!x) return ISD_E_ARG;
+  for (hipEvent_t e : x->ev_pool) hipEventDestroy(e);
   delete x;
   return ISD_OK;
+}
+
+isd_status isd_profile(isd_ctx* x, int32_t enable) {
+  if (!x) return ISD_E_ARG;
+  if (enable && x->ev_pool.empty()) {
+    x->ev_pool.resize(kProfEvents);
+    for (auto& e : x->ev_pool)
+      if (hipEventCreate(&e) != hipSuccess) return ISD_E_HIP;
+  }
+  x->prof_on = enable != 0;
+  return ISD_OK;
+}
+
+isd_status isd_profile_report(isd_ctx* x, isd_prof_entry* out, int32_t cap, int32_t* n) {
+  if (!x || !n || (cap > 0 && !out)) return ISD_E_ARG;
+  std::vector<isd_prof_entry> agg;
+  if (!x->prof_recs.empty()) {
+    if (hipEventSynchronize(x->ev_pool[x->prof_recs.back().second + 1]) != hipSuccess) return ISD_E_HIP;
+  }
+  for (const auto& r : x->prof_recs) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, x->ev_pool[r.second], x->ev_pool[r.second + 1]) != hipSuccess) return ISD_E_HIP;
+    isd_prof_entry* e = nullptr;
+    for (auto& a : agg)
+      if (!strncmp(a.name, r.first, sizeof(a.name))) e = &a;
+    if (!e) {
+      agg.emplace_back();
+      e = &agg.back();
+      memset(e, 0, sizeof(*e));
+      strncpy(e->name, r.first, sizeof(e->name) - 1);
+    }
+    e->launches += 1;
+    e->total_ms += ms;
+  }
+  *n = (int32_t)agg.size();
+  for (int i = 0; i < cap && i < (int)agg.size(); ++i) out[i] = agg[i];
+  const bool overflow = x->prof_overflow;
+  x->prof_recs.clear();
+  x->ev_used = 0;
+  x->prof_overflow = false;
+  return overflow ? ISD_E_CAPACITY : ISD_OK;
 }
 
 size_t isd_attn_workspace_bytes(const isd_attn_args* a) {

@@ -432,12 +432,14 @@ __global__ __launch_bounds__(NT) void decide_kernel(SampleArgs a) {
       bool ok;
       RowStat qs;
       qs.ok = true;
+      // q is the proposing row's distribution for a sampled proposal, delta(v) for an argmax one
+      const bool sampled_q = a.propose == ISD_PROPOSE_SAMPLE && qr >= 0 && a.q_logits;
       if (greedy) {
         ok = (v == ps.arg);
       } else {
         const double px = weight_of(a.logits[(size_t)row * a.V + v], ps.m, a.T) / ps.S;
         double qx = 1.0;
-        if (qr >= 0 && a.q_logits) {
+        if (sampled_q) {
           qs = D.stat_prev(qr);
           if (!qs.ok) {
             failed = true;
@@ -458,7 +460,7 @@ __global__ __launch_bounds__(NT) void decide_kernel(SampleArgs a) {
         r = ps.arg;
       } else {
         const double u2 = philox_uniform(a.seed, b, t, L + k, 1);
-        if (qr >= 0 && a.q_logits) r = D.resid_draw(row, ps, qr, qs, u2);
+        if (sampled_q) r = D.resid_draw(row, ps, qr, qs, u2);
         else r = D.draw(row, ps, u2, v);
       }
       commit(r);

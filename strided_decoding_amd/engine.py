@@ -132,6 +132,17 @@ class Engine:
     def status(self):
         return self.lib.isd_get_status(self.ctx, self._s())
 
+    def profile(self, enable):
+        A.check("isd_profile", self.lib.isd_profile(self.ctx, 1 if enable else 0))
+
+    def profile_report(self):
+        """{kernel name: (launches, total milliseconds)} since the last report (synchronizes)."""
+        cap = 64
+        arr = (A.ProfEntry * cap)()
+        n = C.c_int32()
+        A.check("isd_profile_report", self.lib.isd_profile_report(self.ctx, arr, cap, C.byref(n)))
+        return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(min(n.value, cap))}
+
     # ------------------------------------------------------------------ views
     def _view(self, ptr, nbytes, dtype, shape):
         off = ptr - self.workspace.data_ptr()
@@ -157,9 +168,11 @@ class Engine:
 
     def logits(self):
         """Logits of the last decode pass [max_batch, 2N-1, V] (float32)."""
+        b = A.Buffers()          # the logits buffer alternates between passes: query it now
+        A.check("isd_get_buffers", self.lib.isd_get_buffers(self.ctx, C.byref(b)))
         V = self.shape.vocab
         rows = self.max_batch * self.R
-        return self._view(self._buf.logits, rows * V * 4, torch.float32, (self.max_batch, self.R, V))
+        return self._view(b.logits, rows * V * 4, torch.float32, (self.max_batch, self.R, V))
 
     def rows(self):
         n = self.max_batch * self.R

@@ -20,9 +20,10 @@ from oracle import isd as OI
 from oracle import model as M
 from oracle import philox, sampler
 
+from _decisions import CAT_TAU, first_divergence
+
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-ACC_TAU, CAT_TAU = 1e-3, 1e-5
 STATE_NAME = {1: "A", 2: "B", 3: "DONE", 0: "EMPTY"}
 
 
@@ -35,11 +36,6 @@ def make_engine(shape, w, N, T, propose, B, max_seq, lora=None, seed=1, n_pages=
     from strided_decoding_amd import Engine
     return Engine(shape, w, stride=N, temperature=T, propose=propose, seed=seed, max_batch=B,
                   max_seq_len=max_seq, lora=lora, n_pages=n_pages)
-
-
-def _near(decisions, T):
-    return any((d.kind == "accept" and d.margin < ACC_TAU) or (d.kind != "accept" and T > 0 and d.margin < CAT_TAU)
-               for d in decisions)
 
 
 def _adopt(dec, model, b, g, committed, rec_logits, R, N, T, propose):
@@ -125,10 +121,16 @@ def teacher_forced(shape, w, N, T, propose, prompts, max_new, steps, lora=None, 
             else:
                 decisions, otoks, onacc = rec.decisions, rec.tokens, rec.n_accept
             gt = [int(x) for x in g_tok[b, :g_nc[b]]]
-            if gt != list(otoks) or g_na[b] != onacc:
-                assert _near(decisions, T), (b, gt, otoks, [(d.kind, d.token, d.margin) for d in decisions])
+            g_pend = [gs[b][f"pending{j}"] for j in range(N - 1)] if gs[b]["state"] == 1 else None
+            greedy_tau = None if T > 0 else (0.0 if on_gpu_logits else 2 * logits_tol)
+            div = first_divergence(decisions, rec.state, N, gt, int(g_na[b]), g_pend, greedy_tau)
+            if div is not None:
+                d, is_near = div
+                assert is_near, (b, gt, otoks, (d.kind, d.token, d.margin))
                 near += 1
                 lockstep = False
+            else:
+                assert gt == list(otoks) and g_na[b] == onacc, (b, gt, otoks)
             committed[b] += gt
         if lockstep:
             pt = eng.page_table().cpu().numpy()

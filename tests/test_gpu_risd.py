@@ -40,7 +40,7 @@ def _generate(eng, prompts, max_new, max_steps=10_000):
     return out, steps, acc, ver
 
 
-@pytest.mark.parametrize("sticky", [None, (0.0, 10.0, 2.0, 7)])
+@pytest.mark.parametrize("sticky", [None, (0.0, 20.0, 4.0, 7)])
 def test_risd_greedy_equals_ar_greedy_bf16(sticky):
     shape = I.SMALL_BF16
     w = I.weights_numpy(shape, seed=0, scale=20.0, sticky=sticky)
