@@ -258,6 +258,29 @@ typedef struct {
 size_t isd_sample_workspace_bytes(int32_t batch, int32_t rows, int32_t vocab, int32_t q_rows);
 isd_status isd_sample(const isd_sample_args* a, void* stream);
 
+/* One projection of the decode step: Y = X W^T (X [M, K] row-major, W [N, K] row-major,
+ * i.e. out x in) in the context's arithmetic, as isd_step runs it.
+ *   dtype    ISD_BF16 (MFMA path, X and W bf16) or ISD_F32
+ *   mode     ISD_GEMM_STORE: Y act [M, N]; ISD_GEMM_STORE_F32: Y float [M, N];
+ *            ISD_GEMM_RESID: R float [M, N] += X W^T;
+ *            ISD_GEMM_SWIGLU: Y act [M, N] = silu(X W^T) * (X W2^T), W2 [N, K]
+ *   splits   split-K factor (bf16 only): 0 = the rule isd_step uses (a function of N and K)
+ *   workspace device fp32 [splits, M, N (x2 for SwiGLU)] when splits > 1, else unused
+ * K must be a multiple of 32 and N of 4 for bf16.  Errors: ISD_E_ARG, ISD_E_SHAPE. */
+enum { ISD_GEMM_STORE = 0, ISD_GEMM_STORE_F32 = 1, ISD_GEMM_RESID = 2, ISD_GEMM_SWIGLU = 3 };
+typedef struct {
+  int32_t dtype, mode, M, N, K, splits;
+  const void* X;
+  const void* W;
+  const void* W2;
+  void* Y;
+  float* R;
+  void* workspace;
+} isd_gemm_args;
+
+int32_t isd_gemm_splits(int32_t N, int32_t K, int32_t swiglu);
+isd_status isd_gemm(const isd_gemm_args* a, void* stream);
+
 /* Library version string. */
 const char* isd_version(void);
 

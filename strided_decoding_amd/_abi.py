@@ -20,7 +20,15 @@ ISD_SLOT_EMPTY, ISD_SLOT_A, ISD_SLOT_B, ISD_SLOT_DONE = 0, 1, 2, 3
 # symbols the header declares (checked by the CPU test-suite)
 EXPORTS = ("isd_init", "isd_prefill", "isd_step", "isd_get_buffers", "isd_get_status", "isd_release",
            "isd_attn_workspace_bytes", "isd_attn_paged", "isd_sample_workspace_bytes", "isd_sample",
-           "isd_version", "isd_profile", "isd_profile_report")
+           "isd_version", "isd_profile", "isd_profile_report", "isd_gemm", "isd_gemm_splits")
+
+ISD_GEMM_STORE, ISD_GEMM_STORE_F32, ISD_GEMM_RESID, ISD_GEMM_SWIGLU = 0, 1, 2, 3
+
+
+class GemmArgs(C.Structure):
+    _fields_ = [("dtype", C.c_int32), ("mode", C.c_int32), ("M", C.c_int32), ("N", C.c_int32), ("K", C.c_int32),
+                ("splits", C.c_int32), ("X", C.c_void_p), ("W", C.c_void_p), ("W2", C.c_void_p), ("Y", C.c_void_p),
+                ("R", C.c_void_p), ("workspace", C.c_void_p)]
 
 
 class ProfEntry(C.Structure):
@@ -110,6 +118,10 @@ def load(path=LIB_PATH):
     lib.isd_sample_workspace_bytes.restype = C.c_size_t
     lib.isd_sample.argtypes = [C.POINTER(SampleArgs), C.c_void_p]
     lib.isd_version.restype = C.c_char_p
+    lib.isd_gemm.argtypes = [C.POINTER(GemmArgs), C.c_void_p]
+    lib.isd_gemm.restype = C.c_int
+    lib.isd_gemm_splits.argtypes = [C.c_int32, C.c_int32, C.c_int32]
+    lib.isd_gemm_splits.restype = C.c_int32
     lib.isd_profile.argtypes = [C.c_void_p, C.c_int32]
     lib.isd_profile_report.argtypes = [C.c_void_p, C.POINTER(ProfEntry), C.c_int32, C.POINTER(C.c_int32)]
     for f in ("isd_init", "isd_prefill", "isd_step", "isd_get_buffers", "isd_get_status", "isd_release",

@@ -134,7 +134,13 @@ struct GemmArgs {
   const int32_t* delta_row;  // [M] delta row of output row m or -1
   int ldd;
   int delta_off2;            // EPI_SWIGLU: column offset of the up-projection delta
+  int splits;                // split-K factor (bf16 path; 1 = none)
+  float* part;               // split-K partials [splits, M, N (x2 for SwiGLU)] fp32
 };
+
+// Split-K factor of a bf16 projection: a function of the output width and K only (never of
+// the row count), so that a row's result is the same whatever the batch composition.
+int gemm_splits(int n_out, int K, bool dual);
 
 // ---------------------------------------------------------------------------------------
 // Kernel launchers (defined in the .hip files).

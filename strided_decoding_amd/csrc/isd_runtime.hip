@@ -45,6 +45,8 @@ struct isd_ctx {
   int R, qd, kd, qkvw;
   int max_pages, max_rows, max_dec_rows, n_chunks, max_splits, items_per_slot, q_max, ncb, q_tile;
   int max_items, n_mask, delta_w;
+  size_t part_floats = 0;       // split-K partial buffer (bf16 decode GEMMs)
+  float* gemm_part = nullptr;
   // weights
   const void *embed = nullptr, *final_norm = nullptr, *lm_head = nullptr;
   std::vector<const void*> attn_norm, wqkv, wo, ffn_norm, wg, wu, wd, lora_a, lora_b;
@@ -161,6 +163,7 @@ size_t carve(isd_ctx& x, char* base) {
   if (x.bf) {
     x.part_o = cv.take<float>((size_t)x.max_splits * x.max_dec_rows * x.qd);
     x.part_ml = cv.take<float>((size_t)x.max_splits * x.max_dec_rows * c.n_q_heads * 2);
+    x.gemm_part = cv.take<float>(x.part_floats);
   }
   for (int i = 0; i < 2; ++i) {
     x.logits[i] = cv.take<float>((size_t)x.max_dec_rows * V);
@@ -197,6 +200,19 @@ void derive(isd_ctx& x) {
   x.max_items = std::max(c.max_batch * x.items_per_slot, cdiv(c.max_prefill_tokens, x.q_tile) + c.max_batch);
   x.n_mask = c.max_batch * (c.stride_n - 1);
   x.delta_w = std::max(std::max(x.qkvw, 2 * c.d_ffn), c.d_model);
+  // split-K partials: the largest S * rows * width over the decode projections
+  {
+    const int d = c.d_model, F = c.d_ffn, r = std::max(c.lora_rank, 1);
+    const size_t M = x.max_dec_rows, Mm = std::max(1, x.n_mask);
+    auto need = [](size_t m, int n, int k, bool dual) {
+      return (size_t)gemm_splits(n, k, dual) * m * n * (dual ? 2 : 1);
+    };
+    size_t p = std::max({need(M, x.qkvw, d, false), need(M, d, x.qd, false), need(M, F, d, true),
+                         need(M, d, F, false), need(M, c.vocab, d, false)});
+    if (c.lora_rank > 0)
+      p = std::max({p, need(Mm, r, d, false), need(Mm, r, x.qd, false), need(Mm, r, F, false)});
+    x.part_floats = x.bf ? p : 0;
+  }
   x.kv_layer_bytes = (size_t)c.n_pages * x.kd * c.page_size * x.act;
 }
 
@@ -240,8 +256,21 @@ StepMeta meta(isd_ctx& x) {
     HIP_OK(expr);                          \
   } while (0)
 
-hipError_t gemm(const isd_ctx& x, const GemmArgs& g, hipStream_t s) {
-  return x.bf ? launch_gemm_bf16(g, s) : launch_gemm_f32(g, s);
+// Launch a projection.  bf16 GEMMs with at most a decode pass's rows use the split-K factor
+// of their (N, K); larger row counts (prefill) run unsplit.
+hipError_t gemm(const isd_ctx& x, GemmArgs g, hipStream_t s) {
+  if (!x.bf) return launch_gemm_f32(g, s);
+  g.splits = 1;
+  g.part = nullptr;
+  if (g.M <= x.max_dec_rows && x.gemm_part) {
+    const bool dual = g.epi == EPI_SWIGLU;
+    const int S = gemm_splits(g.N, g.K, dual);
+    if ((size_t)S * g.M * g.N * (dual ? 2 : 1) <= x.part_floats) {
+      g.splits = S;
+      g.part = x.gemm_part;
+    }
+  }
+  return launch_gemm_bf16(g, s);
 }
 
 GemmArgs gargs(const void* A, int lda, const void* B0, int ldb, int M, int N, int K, int epi) {
@@ -722,6 +751,38 @@ isd_status isd_attn_paged(const isd_attn_args* a, void* stream) {
   aa.n_rows = (int)rows;
   HIP_OK(launch_attn_bf16(aa, s));
   HIP_OK(launch_attn_combine_bf16(aa, s));
+  return ISD_OK;
+}
+
+int32_t isd_gemm_splits(int32_t N, int32_t K, int32_t swiglu) { return gemm_splits(N, K, swiglu != 0); }
+
+isd_status isd_gemm(const isd_gemm_args* a, void* stream) {
+  if (!a || !a->X || !a->W) return ISD_E_ARG;
+  if (a->dtype != ISD_BF16 && a->dtype != ISD_F32) return ISD_E_ARG;
+  if (a->mode < ISD_GEMM_STORE || a->mode > ISD_GEMM_SWIGLU) return ISD_E_ARG;
+  if (a->M < 0 || a->N < 1 || a->K < 1 || a->splits < 0) return ISD_E_ARG;
+  if (a->mode == ISD_GEMM_RESID ? !a->R : !a->Y) return ISD_E_ARG;
+  if (a->mode == ISD_GEMM_SWIGLU && !a->W2) return ISD_E_ARG;
+  GemmArgs g = gargs(a->X, a->K, a->W, a->K, a->M, a->N, a->K, a->mode);
+  g.B1 = a->W2;
+  g.C = a->Y;
+  g.ldc = a->N;
+  g.R = a->R;
+  g.ldr = a->N;
+  hipStream_t s = (hipStream_t)stream;
+  if (a->dtype == ISD_F32) {
+    HIP_OK(launch_gemm_f32(g, s));
+    return ISD_OK;
+  }
+  if (a->K % 32 || a->N % 4) return ISD_E_SHAPE;
+  const int S = a->splits ? a->splits : gemm_splits(a->N, a->K, a->mode == ISD_GEMM_SWIGLU);
+  if ((a->K / 32) % S) return ISD_E_SHAPE;
+  if (S > 1) {
+    if (!a->workspace) return ISD_E_ARG;
+    g.splits = S;
+    g.part = (float*)a->workspace;
+  }
+  HIP_OK(launch_gemm_bf16(g, s));
   return ISD_OK;
 }
 

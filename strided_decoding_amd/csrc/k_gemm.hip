@@ -1,16 +1,32 @@
 // Projection GEMMs of the decode step: Y[M, N] = X[M, K] W[N, K]^T with fused epilogues
 // (bf16 store, fp32 store, fp32 residual add, SwiGLU of a gate/up pair) and the MASK-row
-// LoRA delta.  bf16 path: MFMA 16x16x32 tiles, LDS double buffering; fp32 path: LDS-tiled
-// FMA.  Per output element the K order is fixed (k = 0, 32, 64, ...), independent of M and
-// of which other rows share the tile, so a row's result does not depend on the batch.
+// LoRA delta.
+//
+// bf16 path: one 224 x 256 output tile per workgroup (4 waves side by side, each 224 x 64 =
+// 7 x 2 MFMA 32x32x16 tiles, 224 accumulators per lane).  224 = 448 / 2 makes the decode row count
+// (64 slots x 7 rows) exactly two row tiles.  K is streamed in 32-wide stages through a
+// 4-deep LDS ring filled by direct global->LDS loads (16 bytes per lane), so no staging
+// registers are needed and three stages are in flight while one is consumed.  Each 64-byte
+// LDS row keeps its four 16-byte k-chunks XOR-swizzled by (row/4)%4 so that the 16 rows an
+// MFMA operand read touches fall in distinct banks.
+// Split-K (decode row counts only): split s covers k-stages [s kt, (s+1) kt) and writes fp32
+// partials that splitk_reduce_kernel sums in split order - no atomics - so every output
+// element has a fixed accumulation order that depends only on K and the split count, never
+// on the number of rows.  Workgroup ids are ordered so that the row tiles sharing a weight
+// tile differ by a multiple of 8 and run on the same XCD (one L2).
+// fp32 path: LDS-tiled FMA, same epilogues.
+#include <algorithm>
+
 #include "isd_common.h"
 
 namespace isd {
 namespace {
 
-constexpr int BM = 128;        // rows per tile
-constexpr int BK = 64;         // k per LDS stage (two MFMA k-steps)
-constexpr int LDSS = BK + 8;   // LDS row stride in bf16 (144 B; breaks bank aliasing)
+constexpr int BK = 32;            // k per pipeline stage (one MFMA k-step)
+constexpr int TM2 = 224, TN2 = 256;
+constexpr int NST = 5;            // LDS ring depth (5 x 30 KB)
+constexpr int GROUP_BYTES = 16 * BK * 2;                 // 16 rows x 64 B
+constexpr int STAGE_BYTES = (TM2 + TN2) / 16 * GROUP_BYTES;  // 30 KB
 
 template <typename T, int EPI>
 __device__ __forceinline__ void epilogue_store_t(const GemmArgs& a, int row, int col, float v, float v_up) {
@@ -34,115 +50,211 @@ __device__ __forceinline__ void epilogue_store_t(const GemmArgs& a, int row, int
   }
 }
 
-// 256 threads = 4 waves in a 2 x 2 arrangement, each wave a 64 x 64 sub-tile of 4 x 4 MFMA
-// tiles.  EPI_SWIGLU interleaves gate and up in 16-column blocks of the B tile so that a
-// lane holds gate and up of the same output element.
-template <int EPI>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+// D = A * B + C for one 32x32x16 bf16 tile: lane l holds A row (l%32) and B column (l%32)
+// with k-values 8*(l/32) .. 8*(l/32)+7; D register r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
+// column l%32.  (On gfx950 this tile sustains about 1.5x the rate of 16x16x32.)
+__device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int EPI, bool PARTIAL>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S,
+                                                                float* part) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU);
-  constexpr int BNO = DUAL ? 64 : 128;
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDSS];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][128 * LDSS];
+  constexpr int TNO = DUAL ? TN2 / 2 : TN2;
+  constexpr int AG = TM2 / 16;                    // 14 A row groups of 16 rows
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE_BYTES];
+
+  const int id = blockIdx.x;
+  const int grp = id / (8 * n_mt), rem = id % (8 * n_mt);
+  const int mt = rem / 8, unit = grp * 8 + (rem % 8);
+  if (unit >= n_units) return;
+  const int nt = unit / S, sp = unit % S;
+  const int kt_per = (a.K / BK) / S;
+  const int kbase = sp * kt_per * BK;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = blockIdx.x * BNO, m0 = blockIdx.y * BM;
-  const uint16_t* A = (const uint16_t*)a.A;
-  const uint16_t* B0 = (const uint16_t*)a.B0;
-  const uint16_t* B1 = (const uint16_t*)a.B1;
+  const int n0 = nt * TNO, m0 = mt * TM2;
 
-  // global -> register staging: 4 chunks of 16 B per thread for each operand
-  const uint16_t* pa[4];
-  const uint16_t* pb[4];
-  int soff[4];
+  // Loader: wave w fills A groups w, w+4, w+8, (w+12) and B groups w, w+4, w+8, w+12.
+  // Lane l writes LDS bytes [16 l, 16 l + 16) of its group: row l/4, slot l%4, which holds
+  // k-chunk (l%4) ^ ((row/4)%4) of that row.  For SwiGLU the B tile alternates 32-row
+  // blocks of the gate and up matrices, so each wave multiplies one gate block and the up
+  // block of the same 32 output columns.
+  const int lrow = lane >> 2;
+  const int chunk = (lane & 3) ^ ((lrow >> 2) & 3);
+  const uint16_t* asrc[4];
+  const uint16_t* bsrc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i, row = c >> 3, kc = (c & 7) * 8;
-    soff[i] = row * LDSS + kc;
-    const int m = m0 + row;
-    int src = -1;
-    if (m < a.M) src = a.a_rows ? a.a_rows[m] : m;
-    pa[i] = src >= 0 ? A + (size_t)src * a.lda + kc : nullptr;
+    const int g = wave + 4 * i;
+    const int m = m0 + g * 16 + lrow;
+    int srow = 0;
+    if (g < AG && m < a.M) {
+      srow = a.a_rows ? a.a_rows[m] : m;
+      if (srow < 0) srow = 0;          // unused row (its outputs are never consumed)
+    }
+    asrc[i] = (const uint16_t*)a.A + (size_t)srow * a.lda + kbase + chunk * 8;
+    const uint16_t* bm = (const uint16_t*)a.B0;
     int n;
-    const uint16_t* Bp;
     if (DUAL) {
-      const int blk = row >> 4;
-      Bp = (blk & 1) ? B1 : B0;
-      n = n0 + (blk >> 1) * 16 + (row & 15);
+      const int blk = g >> 1;
+      if (blk & 1) bm = (const uint16_t*)a.B1;
+      n = n0 + (blk >> 1) * 32 + (g & 1) * 16 + lrow;
     } else {
-      Bp = B0;
-      n = n0 + row;
+      n = n0 + g * 16 + lrow;
     }
-    pb[i] = n < a.N ? Bp + (size_t)n * a.ldb + kc : nullptr;
+    n = min(n, a.N - 1);
+    bsrc[i] = bm + (size_t)n * a.ldb + kbase + chunk * 8;
   }
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
-  u32x4_t ra[4], rb[4];
-  auto gload = [&](int k0) {
+  const int na = (wave + 12 < AG) ? 4 : 3;       // A groups of this wave
+
+  auto issue = [&](int kt) {
+    uint8_t* st = smem + (kt % NST) * STAGE_BYTES;
+    const int koff = kt * BK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ra[i] = pa[i] ? *(const u32x4_t*)(pa[i] + k0) : zero;
-      rb[i] = pb[i] ? *(const u32x4_t*)(pb[i] + k0) : zero;
+      if (i < na)
+        __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + koff), (lds_void*)(st + (wave + 4 * i) * GROUP_BYTES),
+                                         16, 0, 0);
     }
-  };
-  auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *(u32x4_t*)&As[buf][soff[i]] = ra[i];
-      *(u32x4_t*)&Bs[buf][soff[i]] = rb[i];
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + koff),
+                                       (lds_void*)(st + (AG + wave + 4 * i) * GROUP_BYTES), 16, 0, 0);
   };
 
-  f32x4_t acc[4][4];
+  f32x16_t acc[7][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 7; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = a.K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  const int lr = lane & 15, lg = (lane >> 4) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+  // Stage s lives in ring buffer s % NST.  Loads run NST-1 stages ahead; the MFMA operands
+  // of stage kt+1 are read from LDS into registers while the MFMAs of stage kt execute.
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < kt_per) issue(s);
+
+  // operand read: row (lane%32) of a 32-row block, k-chunk 2 kk + lane/32 (swizzled)
+  const int rig = lane & 15, half = (lane >> 4) & 1, khi = lane >> 5;
+  const int rd0 = rig * (BK * 2) + half * GROUP_BYTES;
+  const int sw = (rig >> 2) & 3;
+  auto wait_stage = [&](int later) {      // later = stages issued after the awaited one
+    if (later >= 3) wait_vmcnt<21>();
+    else if (later == 2) wait_vmcnt<14>();
+    else if (later == 1) wait_vmcnt<7>();
+    else wait_vmcnt<0>();
+  };
+  auto read_frags = [&](int kt, bf16x8_t (*af)[7], bf16x8_t (*bfr)[2]) {
+    const uint8_t* st = smem + (kt % NST) * STAGE_BYTES;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      bf16x8_t af[4], bfr[4];
+      const int off = rd0 + (((2 * kk + khi) ^ sw) * 16);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        af[t] = as_bf16x8(*(const u32x4_t*)&As[buf][(wm * 64 + t * 16 + lr) * LDSS + kk * 32 + lg]);
-        bfr[t] = as_bf16x8(*(const u32x4_t*)&Bs[buf][(wn * 64 + t * 16 + lr) * LDSS + kk * 32 + lg]);
-      }
+      for (int j = 0; j < 2; ++j)
+        bfr[kk][j] = as_bf16x8(*(const u32x4_t*)(st + (AG + 4 * wave + 2 * j) * GROUP_BYTES + off));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[i], bfr[j], acc[i][j]);
+      for (int i = 0; i < 7; ++i) af[kk][i] = as_bf16x8(*(const u32x4_t*)(st + (2 * i) * GROUP_BYTES + off));
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
+  };
+
+  bf16x8_t af[2][7], bfr[2][2];
+  wait_stage(min(NST - 2, kt_per - 1));
+  __builtin_amdgcn_s_barrier();
+  read_frags(0, af, bfr);
+  // One pipeline step: make stage kt+1 visible, refill the ring, read stage kt+1's operands,
+  // multiply stage kt's.  Ring buffer (kt+NST-1) % NST held stage kt-1, whose operands every
+  // wave consumed before this step's barrier.
+  for (int kt = 0; kt < kt_per; ++kt) {
+    // stages kt+2 .. kt+NST-2 may stay in flight (the last step re-reads stage kt)
+    wait_stage(kt + 1 < kt_per ? min(NST - 3, kt_per - 2 - kt) : 0);
+    __builtin_amdgcn_s_barrier();        // no fence: the later stages' loads stay in flight
+    if (kt + NST - 1 < kt_per) issue(kt + NST - 1);
+    bf16x8_t naf[2][7], nbfr[2][2];
+    read_frags(kt + 1 < kt_per ? kt + 1 : kt, naf, nbfr);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 7; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(af[kk][i], bfr[kk][j], acc[i][j]);
+    // interleave the 18 operand reads of the next stage with this stage's 28 MFMAs
+#pragma unroll
+    for (int g = 0; g < 18; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int i = 0; i < 7; ++i) af[kk][i] = naf[kk][i];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bfr[kk][j] = nbfr[kk][j];
+    }
   }
 
-  const int rq = (lane >> 4) * 4;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 7; ++i) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = m0 + wm * 64 + i * 16 + rq + r;
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + 32 * i + 8 * (r >> 2) + 4 * khi + (r & 3);
+      if (row >= a.M) continue;
       if (DUAL) {
-#pragma unroll
-        for (int jp = 0; jp < 2; ++jp) {
-          const int col = n0 + (2 * wn + jp) * 16 + lr;
-          epilogue_store_t<bf16, EPI>(a, row, col, acc[i][2 * jp][r], acc[i][2 * jp + 1][r]);
+        const int col = n0 + 32 * wave + (lane & 31);
+        if (PARTIAL) {
+          if (col < a.N) {
+            float* pr = part + ((size_t)sp * a.M + row) * (2 * (size_t)a.N);
+            pr[col] = acc[i][0][r];
+            pr[a.N + col] = acc[i][1][r];
+          }
+        } else {
+          epilogue_store_t<bf16, EPI>(a, row, col, acc[i][0][r], acc[i][1][r]);
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n0 + wn * 64 + j * 16 + lr;
-          epilogue_store_t<bf16, EPI>(a, row, col, acc[i][j][r], 0.f);
+        for (int j = 0; j < 2; ++j) {
+          const int col = n0 + 64 * wave + 32 * j + (lane & 31);
+          if (PARTIAL) {
+            if (col < a.N) part[((size_t)sp * a.M + row) * (size_t)a.N + col] = acc[i][j][r];
+          } else {
+            epilogue_store_t<bf16, EPI>(a, row, col, acc[i][j][r], 0.f);
+          }
         }
       }
     }
+  }
+}
+
+// Sum the split-K partials in split order and apply the epilogue.
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a, int S, const float* part) {
+  constexpr bool DUAL = (EPI == EPI_SWIGLU);
+  const size_t ld = DUAL ? 2 * (size_t)a.N : (size_t)a.N;
+  const size_t n4 = (size_t)a.M * a.N / 4;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n4; e += (size_t)gridDim.x * blockDim.x) {
+    const int row = (int)(e * 4 / a.N), col = (int)(e * 4 % a.N);
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S; ++s) {
+      const float* pr = part + ((size_t)s * a.M + row) * ld;
+      v += *(const f32x4_t*)(pr + col);
+      if (DUAL) u += *(const f32x4_t*)(pr + a.N + col);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) epilogue_store_t<bf16, EPI>(a, row, col + j, v[j], u[j]);
   }
 }
 
@@ -205,21 +317,50 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
       epilogue_store_t<float, EPI>(a, m0 + ty * 4 + i, n0 + tx * 4 + j, acc[i][j], accu[i][j]);
 }
 
+template <int EPI>
+hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
+  const bool dual = EPI == EPI_SWIGLU;
+  const int tno = dual ? TN2 / 2 : TN2;
+  const int n_mt = (a.M + TM2 - 1) / TM2, n_nt = (a.N + tno - 1) / tno;
+  const int S = (a.splits > 1 && a.part) ? a.splits : 1;
+  const int units = n_nt * S;
+  dim3 grid(((units + 7) / 8) * 8 * n_mt);
+  if (S > 1) {
+    hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, true>), grid, dim3(256), 0, s, a, n_mt, units, S, a.part);
+    const size_t n4 = (size_t)a.M * a.N / 4;
+    const int blocks = (int)std::min<size_t>((n4 + 255) / 256, 4096);
+    hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3(blocks), dim3(256), 0, s, a, S, (const float*)a.part);
+  } else {
+    hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, false>), grid, dim3(256), 0, s, a, n_mt, units, 1, nullptr);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+}  // namespace isd
+
+int gemm_splits(int n_out, int K, bool dual) {
+  const int tno = dual ? isd::TN2 / 2 : isd::TN2;
+  const int tiles = (n_out + tno - 1) / tno;
+  int S = 1;
+  while (S < 8 && 2 * tiles * (2 * S) <= 256 && (K / isd::BK) % (2 * S) == 0 && K / (2 * S) >= 512) S *= 2;
+  return S;
+}
+
+namespace isd {
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
-  if (a.K % BK != 0) return hipErrorInvalidValue;
-  const int bno = a.epi == EPI_SWIGLU ? 64 : 128;
-  dim3 grid((a.N + bno - 1) / bno, (a.M + BM - 1) / BM);
+  if (a.K % BK != 0 || a.N % 4 != 0) return hipErrorInvalidValue;
+  const int S = (a.splits > 1 && a.part) ? a.splits : 1;
+  if ((a.K / BK) % S != 0) return hipErrorInvalidValue;
   switch (a.epi) {
-    case EPI_STORE: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_STORE>, grid, dim3(256), 0, s, a); break;
-    case EPI_STORE_F32: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_STORE_F32>, grid, dim3(256), 0, s, a); break;
-    case EPI_RESID: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_RESID>, grid, dim3(256), 0, s, a); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_SWIGLU>, grid, dim3(256), 0, s, a); break;
+    case EPI_STORE: return launch_big<EPI_STORE>(a, s);
+    case EPI_STORE_F32: return launch_big<EPI_STORE_F32>(a, s);
+    case EPI_RESID: return launch_big<EPI_RESID>(a, s);
+    case EPI_SWIGLU: return launch_big<EPI_SWIGLU>(a, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s) {

@@ -211,6 +211,29 @@ def attn_paged(q, k_pool, v_pool, page_table, ctx_len, q_len, n_kv_heads, out=No
     return out, workspace, args
 
 
+def gemm(X, W, mode="store", W2=None, out=None, R=None, splits=0, workspace=None, stream=None):
+    """Kernel-level projection (see isd_gemm): X [M, K], W [N, K] (bf16 or float32 on device)."""
+    lib = A.load()
+    M, K = X.shape
+    N = W.shape[0]
+    modes = {"store": A.ISD_GEMM_STORE, "store_f32": A.ISD_GEMM_STORE_F32, "resid": A.ISD_GEMM_RESID,
+             "swiglu": A.ISD_GEMM_SWIGLU}
+    md = modes[mode]
+    bf = X.dtype == torch.bfloat16
+    if out is None and md != A.ISD_GEMM_RESID:
+        out = torch.empty((M, N), dtype=torch.float32 if md == A.ISD_GEMM_STORE_F32 else X.dtype, device=X.device)
+    S = splits or (lib.isd_gemm_splits(N, K, 1 if md == A.ISD_GEMM_SWIGLU else 0) if bf else 1)
+    if bf and S > 1 and workspace is None:
+        workspace = torch.empty(S * M * N * (2 if md == A.ISD_GEMM_SWIGLU else 1), dtype=torch.float32,
+                                device=X.device)
+    args = A.GemmArgs(A.ISD_BF16 if bf else A.ISD_F32, md, M, N, K, splits, X.data_ptr(), W.data_ptr(),
+                      0 if W2 is None else W2.data_ptr(), 0 if out is None else out.data_ptr(),
+                      0 if R is None else R.data_ptr(), 0 if workspace is None else workspace.data_ptr())
+    stream = stream if stream is not None else torch.cuda.current_stream(X.device)
+    A.check("isd_gemm", lib.isd_gemm(C.byref(args), C.c_void_p(stream.cuda_stream)))
+    return out if md != A.ISD_GEMM_RESID else R
+
+
 def sample(slots, logits, q_logits, stride, temperature, propose, seed, tokens, n_commit, n_accept,
            workspace=None, stream=None):
     """Kernel-level acceptance step (see isd_sample).  slots: int32 [B, 32] device tensor (in/out)."""
