@@ -266,6 +266,9 @@ isd_status isd_sample(const isd_sample_args* a, void* stream);
  *            ISD_GEMM_SWIGLU: Y act [M, N] = silu(X W^T) * (X W2^T), W2 [N, K]
  *   splits   split-K factor (bf16 only): 0 = the rule isd_step uses (a function of N and K)
  *   workspace device fp32 [splits, M, N (x2 for SwiGLU)] when splits > 1, else unused
+ *   norm_g, norm_out  ISD_GEMM_RESID only, optional (NULL = off): after the residual update,
+ *            norm_out [M, N] act = RMSNorm(R row) * norm_g, eps norm_eps (as isd_step fuses
+ *            the next block's input norm into the O and down projections)
  * K must be a multiple of 32 and N of 4 for bf16.  Errors: ISD_E_ARG, ISD_E_SHAPE. */
 enum { ISD_GEMM_STORE = 0, ISD_GEMM_STORE_F32 = 1, ISD_GEMM_RESID = 2, ISD_GEMM_SWIGLU = 3 };
 typedef struct {
@@ -276,6 +279,9 @@ typedef struct {
   void* Y;
   float* R;
   void* workspace;
+  const void* norm_g;
+  void* norm_out;
+  float norm_eps;
 } isd_gemm_args;
 
 int32_t isd_gemm_splits(int32_t N, int32_t K, int32_t swiglu);

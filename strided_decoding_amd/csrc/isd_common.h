@@ -60,6 +60,18 @@ ISD_DEV float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+// Sum over a 1024-thread block: wave trees, then the 16 wave sums in a fixed pairwise order.
+// sh must hold 16 floats.  Every thread receives the total.
+ISD_DEV float block_sum_1024(float v, float* sh) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float s8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s8[i] = sh[2 * i] + sh[2 * i + 1];
+  return ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+}
 ISD_DEV double wave_sum_d(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -136,6 +148,11 @@ struct GemmArgs {
   int delta_off2;            // EPI_SWIGLU: column offset of the up-projection delta
   int splits;                // split-K factor (bf16 path; 1 = none)
   float* part;               // split-K partials [splits, M, N (x2 for SwiGLU)] fp32
+  // EPI_RESID only, optional: after R += X W^T, norm_out[row] = RMSNorm(R[row]) * norm_g
+  // (act type), fused into the split-K reduction when there is one
+  const void* norm_g;
+  void* norm_out;
+  float norm_eps;
 };
 
 // Split-K factor of a bf16 projection: a function of the output width and K only (never of

@@ -122,7 +122,7 @@ isd_status check_config(const isd_config* c) {
     return ISD_E_ARG;
   if (c->page_size != 16) return ISD_E_SHAPE;
   if (c->n_q_heads % c->n_kv_heads) return ISD_E_SHAPE;
-  if (c->head_dim % 2) return ISD_E_SHAPE;
+  if (c->head_dim % 2 || c->d_model % 4) return ISD_E_SHAPE;
   if (c->vocab > kStatChunk * 256) return ISD_E_SHAPE;
   const int G = c->n_q_heads / c->n_kv_heads;
   if (c->dtype == ISD_BF16) {
@@ -322,9 +322,12 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
   for (int l = 0; l < c.n_layers; ++l) {
     char* kl = x.k_pool + (size_t)l * x.kv_layer_bytes;
     char* vl = x.v_pool + (size_t)l * x.kv_layer_bytes;
-    // attention block
-    if (x.bf) TIMED("rmsnorm", launch_rmsnorm<bf16>(x.X, (const bf16*)x.attn_norm[l], (bf16*)x.Xn, M, d, c.rms_eps, s));
-    else TIMED("rmsnorm", launch_rmsnorm<float>(x.X, (const float*)x.attn_norm[l], (float*)x.Xn, M, d, c.rms_eps, s));
+    // attention block (layers after the first get their input norm from the previous
+    // layer's down projection)
+    if (l == 0) {
+      if (x.bf) TIMED("rmsnorm", launch_rmsnorm<bf16>(x.X, (const bf16*)x.attn_norm[0], (bf16*)x.Xn, M, d, c.rms_eps, s));
+      else TIMED("rmsnorm", launch_rmsnorm<float>(x.X, (const float*)x.attn_norm[0], (float*)x.Xn, M, d, c.rms_eps, s));
+    }
     if (lora) {
       const int r = c.lora_rank;
       const char* wq = nullptr;
@@ -400,15 +403,17 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
       if (st != ISD_OK) return st;
     }
     {
+      // O projection + residual, then the FFN input norm of the updated rows
       GemmArgs g = gargs(x.O, x.qd, x.wo[l], x.qd, M, d, x.qd, EPI_RESID);
       g.R = x.X;
       g.ldr = d;
+      g.norm_g = x.ffn_norm[l];
+      g.norm_out = x.Xn;
+      g.norm_eps = c.rms_eps;
       with_delta(x, g, lora);
       TIMED("gemm_o", gemm(x, g, s));
     }
     // FFN block
-    if (x.bf) TIMED("rmsnorm", launch_rmsnorm<bf16>(x.X, (const bf16*)x.ffn_norm[l], (bf16*)x.Xn, M, d, c.rms_eps, s));
-    else TIMED("rmsnorm", launch_rmsnorm<float>(x.X, (const float*)x.ffn_norm[l], (float*)x.Xn, M, d, c.rms_eps, s));
     if (lora) {
       const int r = c.lora_rank;
       isd_status st;
@@ -429,15 +434,17 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
       if (st != ISD_OK) return st;
     }
     {
+      // down projection + residual, then the next layer's input norm (the final norm last)
       GemmArgs g = gargs(x.H, F, x.wd[l], F, M, d, F, EPI_RESID);
       g.R = x.X;
       g.ldr = d;
+      g.norm_g = l + 1 < c.n_layers ? x.attn_norm[l + 1] : x.final_norm;
+      g.norm_out = x.Xn;
+      g.norm_eps = c.rms_eps;
       with_delta(x, g, lora);
       TIMED("gemm_down", gemm(x, g, s));
     }
   }
-  if (x.bf) TIMED("rmsnorm", launch_rmsnorm<bf16>(x.X, (const bf16*)x.final_norm, (bf16*)x.Xn, M, d, c.rms_eps, s));
-  else TIMED("rmsnorm", launch_rmsnorm<float>(x.X, (const float*)x.final_norm, (float*)x.Xn, M, d, c.rms_eps, s));
   GemmArgs g = gargs(x.Xn, d, x.lm_head, d, lm_M, c.vocab, d, EPI_STORE_F32);
   g.a_rows = lm_rows;
   g.C = x.logits[x.cur];
@@ -769,6 +776,12 @@ isd_status isd_gemm(const isd_gemm_args* a, void* stream) {
   g.ldc = a->N;
   g.R = a->R;
   g.ldr = a->N;
+  if (a->norm_out) {
+    if (a->mode != ISD_GEMM_RESID || !a->norm_g || !(a->norm_eps > 0.f) || a->N % 4) return ISD_E_ARG;
+    g.norm_g = a->norm_g;
+    g.norm_out = a->norm_out;
+    g.norm_eps = a->norm_eps;
+  }
   hipStream_t s = (hipStream_t)stream;
   if (a->dtype == ISD_F32) {
     HIP_OK(launch_gemm_f32(g, s));

@@ -208,21 +208,28 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* tok, const T*
   for (int i = threadIdx.x; i < d; i += 256) dst[i] = to_f(src[i]);
 }
 
-// y = g * x / sqrt(mean(x^2) + eps), one block per row, fixed-order reduction.
+// y = g * x / sqrt(mean(x^2) + eps), one block of 1024 threads per row, fixed-order
+// reduction: thread t owns the 4-column groups t + 1024 k (d is a multiple of 4), squares
+// accumulated group by group, then a fixed tree (the same order the fused GEMM epilogue uses).
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* X, const T* g, T* Y, int d, float eps) {
-  __shared__ float sh[4];
+__global__ __launch_bounds__(1024) void rmsnorm_kernel(const float* X, const T* g, T* Y, int d, float eps) {
+  __shared__ float sh[16];
   const int r = blockIdx.x, tid = threadIdx.x;
   const float* x = X + (size_t)r * d;
   float ss = 0.f;
-  for (int i = tid; i < d; i += 256) ss += x[i] * x[i];
-  ss = wave_sum(ss);
-  if ((tid & 63) == 0) sh[tid >> 6] = ss;
-  __syncthreads();
-  const float tot = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+  for (int c = 4 * tid; c < d; c += 4096) {
+    const f32x4_t v = *(const f32x4_t*)(x + c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ss = fmaf(v[j], v[j], ss);
+  }
+  const float tot = block_sum_1024(ss, sh);
   const float denom = sqrtf(tot / (float)d + eps);
   T* y = Y + (size_t)r * d;
-  for (int i = tid; i < d; i += 256) y[i] = from_f<T>((x[i] / denom) * to_f(g[i]));
+  for (int c = 4 * tid; c < d; c += 4096) {
+    const f32x4_t v = *(const f32x4_t*)(x + c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[c + j] = from_f<T>((v[j] / denom) * to_f(g[c + j]));
+  }
 }
 
 // RoPE (rotate-half) on q and k, write q to q_out and k, v into the slot's pages at `pos`.
@@ -327,7 +334,7 @@ hipError_t launch_embed(const int32_t* tok, const T* table, float* X, int rows, 
 template <typename T>
 hipError_t launch_rmsnorm(const float* X, const T* g, T* Y, int rows, int d, float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rmsnorm_kernel<T>, dim3(rows), dim3(256), 0, s, X, g, Y, d, eps);
+  hipLaunchKernelGGL(rmsnorm_kernel<T>, dim3(rows), dim3(1024), 0, s, X, g, Y, d, eps);
   return hipGetLastError();
 }
 

@@ -258,6 +258,52 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a, int S, c
   }
 }
 
+// Split-K reduction fused with the residual update and the RMSNorm of the updated row: one
+// block of 1024 threads per row; thread t owns the 4-column groups t + 1024 k.  Each group is
+// summed over the splits in order (all split loads issued together), added to the residual,
+// and its squares accumulated in the same order and tree as the standalone RMSNorm kernel, so
+// both paths give the same normalized row for the same residual row.
+constexpr int kNormThreads = 1024;
+constexpr int kNormMaxGroups = 2;         // rows up to 8192 wide
+constexpr int kMaxSplits = 8;
+__global__ __launch_bounds__(kNormThreads) void splitk_resid_norm_kernel(GemmArgs a, int S, const float* part) {
+  __shared__ float sh[kNormThreads / 64];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int dr = a.delta_row ? a.delta_row[row] : -1;
+  float* R = a.R + (size_t)row * a.ldr;
+  const size_t split_stride = (size_t)a.M * a.N;
+  const float* prow = part + (size_t)row * a.N;
+  f32x4_t rv[kNormMaxGroups];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < kNormMaxGroups; ++k) {
+    const int c = 4 * (tid + kNormThreads * k);
+    rv[k] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    if (c < a.N) {
+      f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < S; ++s) v += *(const f32x4_t*)(prow + s * split_stride + c);
+      if (dr >= 0) v += *(const f32x4_t*)(a.delta + (size_t)dr * a.ldd + c);
+      const f32x4_t r = *(const f32x4_t*)(R + c) + v;
+      *(f32x4_t*)(R + c) = r;
+      rv[k] = r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ss = fmaf(r[j], r[j], ss);
+    }
+  }
+  const float tot = block_sum_1024(ss, sh);
+  const float denom = sqrtf(tot / (float)a.N + a.norm_eps);
+  const bf16* g = (const bf16*)a.norm_g;
+  bf16* y = (bf16*)a.norm_out + (size_t)row * a.N;
+#pragma unroll
+  for (int k = 0; k < kNormMaxGroups; ++k) {
+    const int c = 4 * (tid + kNormThreads * k);
+    if (c < a.N) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[c + j] = from_f<bf16>((rv[k][j] / denom) * to_f(g[c + j]));
+    }
+  }
+}
+
 // fp32 reference-precision path: 64 x 64 tile, 256 threads with 4 x 4 outputs each.
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
@@ -325,13 +371,23 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
   const int S = (a.splits > 1 && a.part) ? a.splits : 1;
   const int units = n_nt * S;
   dim3 grid(((units + 7) / 8) * 8 * n_mt);
+  const bool norm = EPI == EPI_RESID && a.norm_out;
   if (S > 1) {
     hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, true>), grid, dim3(256), 0, s, a, n_mt, units, S, a.part);
+    if (norm) {
+      hipLaunchKernelGGL(splitk_resid_norm_kernel, dim3(a.M), dim3(kNormThreads), 0, s, a, S, (const float*)a.part);
+      return hipGetLastError();
+    }
     const size_t n4 = (size_t)a.M * a.N / 4;
     const int blocks = (int)std::min<size_t>((n4 + 255) / 256, 4096);
     hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3(blocks), dim3(256), 0, s, a, S, (const float*)a.part);
   } else {
     hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, false>), grid, dim3(256), 0, s, a, n_mt, units, 1, nullptr);
+  }
+  if (norm) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_rmsnorm<bf16>(a.R, (const bf16*)a.norm_g, (bf16*)a.norm_out, a.M, a.N, a.norm_eps, s);
   }
   return hipGetLastError();
 }
@@ -352,6 +408,8 @@ namespace isd {
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
   if (a.K % BK != 0 || a.N % 4 != 0) return hipErrorInvalidValue;
+  if (a.norm_out && (a.epi != EPI_RESID || a.N > 4 * kNormThreads * kNormMaxGroups)) return hipErrorInvalidValue;
+  if ((a.splits > 1 && a.part) && a.splits > kMaxSplits) return hipErrorInvalidValue;
   const int S = (a.splits > 1 && a.part) ? a.splits : 1;
   if ((a.K / BK) % S != 0) return hipErrorInvalidValue;
   switch (a.epi) {
@@ -373,7 +431,9 @@ hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s) {
     case EPI_SWIGLU: hipLaunchKernelGGL(gemm_f32_kernel<EPI_SWIGLU>, grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !a.norm_out) return e;
+  return launch_rmsnorm<float>(a.R, (const float*)a.norm_g, (float*)a.norm_out, a.M, a.N, a.norm_eps, s);
 }
 
 }  // namespace isd

@@ -105,6 +105,27 @@ def test_gemm_row_invariance():
     assert torch.equal(big[5:6], one)
 
 
+@pytest.mark.parametrize("splits", [0, 1])
+def test_gemm_residual_with_fused_rmsnorm(splits):
+    """R += H Wd^T, then y = RMSNorm(R) * g (fused into the split-K reduction when split)."""
+    from strided_decoding_amd import gemm
+    M, d, F = 448, 4096, 12288
+    H = _rand((M, F), 17, 1.0)
+    Wd = _rand((d, F), 18, 0.02)
+    R0 = _rand((M, d), 19, 1.0, torch.float32)
+    g = (1.0 + 0.1 * _rand((d,), 20, 1.0, torch.float32)).to(torch.bfloat16)
+    R = R0.clone()
+    y = torch.empty((M, d), dtype=torch.bfloat16, device=DEV)
+    gemm(H, Wd, "resid", R=R, splits=splits, norm_g=g, norm_out=y, norm_eps=1e-6)
+    torch.cuda.synchronize()
+    rows, cols = _pick(M, d, 400, 21)
+    ref = R0.cpu().numpy().astype(np.float64)[rows, cols] + _ref(H, Wd, rows, cols)
+    _check(R.cpu().numpy()[rows, cols], ref, bf16=False)
+    Rg = R.double().cpu().numpy()
+    yref = Rg / np.sqrt((Rg ** 2).mean(axis=1, keepdims=True) + 1e-6) * g.double().cpu().numpy()
+    _check(y.float().cpu().numpy().ravel(), yref.ravel())
+
+
 def test_gemm_fp32_path():
     from strided_decoding_amd import gemm
     X = _rand((37, 200), 15, 1.0, torch.float32)
