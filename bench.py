@@ -40,6 +40,12 @@ def parse():
     p.add_argument("--profile-steps", type=int, default=6)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--out", default=None, help="also write the JSON line to this file")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="only run a plain device copy of this many MiB (counter calibration) and exit")
+    p.add_argument("--trace-summary", default=None, metavar="DIR",
+                   help="only summarise a rocprofv3 --kernel-trace csv output directory (no GPU) and exit")
+    p.add_argument("--pmc-summary", default=None, metavar="DIR",
+                   help="only summarise rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (no GPU) and exit")
     return p.parse_args()
 
 
@@ -67,6 +73,12 @@ def kernel_model(shape, M, N, ctx_rows, attn_keys):
     return g
 
 
+def tpf_projection(p, N):
+    """Tokens per forward of the ISD state machine at a per-token acceptance p (a projection for
+    trained weights; random-init weights accept almost nothing)."""
+    return (2 + sum(p ** k for k in range(1, N - 1))) / (2 - p ** (N - 1))
+
+
 def step_bytes(shape, M, ctx_rows):
     """Algorithmic HBM bytes of one pass: weights once, KV of every slot, logits out and in."""
     L = shape.n_layers
@@ -76,6 +88,155 @@ def step_bytes(shape, M, ctx_rows):
     w = L * ((qd + 2 * kd) * d + d * qd + 3 * F * d) * 2 + V * d * 2
     kv = ctx_rows * 2 * kd * 2 * L
     return w + kv + 2 * M * V * 4
+
+
+# Kernel (demangled-name pattern) behind each profiled operation whose traffic can be read from
+# rocprofv3 counters: the decode launches are the most frequent grid of that kernel in a run.
+OP_KERNELS = {
+    "gemm_gate_up": (r"gemm_bf16_big_kernel<3, false>", ("k_gemm.hip",)),
+    "lm_head": (r"gemm_bf16_big_kernel<1, false>", ("k_gemm.hip",)),
+    "attention": (r"attn_bf16_kernel<", ("k_attn.hip",)),
+    "row_stats": (r"row_stats_kernel", ("k_sampler.hip",)),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qwen3_8b_b64.md")
+COPY_KERNEL = r"neg_kernel"
+
+
+def kernel_source_sha(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files + ("isd_common.h",):
+        with open(os.path.join(ROOT, "strided_decoding_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _csv_rows(root, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(root, "**", "*" + suffix), recursive=True)):
+        with open(f, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {root}")
+    return rows
+
+
+def _col(row, *names):
+    low = {k.lower(): v for k, v in row.items()}
+    for n in names:
+        if n.lower() in low:
+            return low[n.lower()]
+    raise KeyError(names)
+
+
+def _grid(row):
+    try:
+        return int(_col(row, "Grid_Size"))
+    except KeyError:
+        return int(_col(row, "Grid_Size_X")) * int(_col(row, "Grid_Size_Y")) * int(_col(row, "Grid_Size_Z"))
+
+
+def _short(name, n=90):
+    name = name.replace("isd::(anonymous namespace)::", "").replace("(isd::EpiMode)", "")
+    return name if len(name) <= n else name[:n - 3] + "..."
+
+
+def trace_summary(root):
+    """Per (kernel, grid) dispatch count and durations from a rocprofv3 --kernel-trace csv run."""
+    rows = _csv_rows(root, "kernel_trace.csv")
+    acc = {}
+    for r in rows:
+        k = (_col(r, "Kernel_Name"), _grid(r))
+        ns = int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))
+        e = acc.setdefault(k, [0, 0, float("inf"), 0])
+        e[0] += 1
+        e[1] += ns
+        e[2] = min(e[2], ns)
+        e[3] = max(e[3], ns)
+    tot = sum(e[1] for e in acc.values())
+    print("| kernel | grid (threads) | dispatches | avg us | min us | max us | % time |")
+    print("|---|---|---|---|---|---|---|")
+    for (name, grid), e in sorted(acc.items(), key=lambda kv: -kv[1][1])[:30]:
+        print(f"| `{_short(name)}` | {grid} | {e[0]} | {e[1] / e[0] / 1e3:.1f} | {e[2] / 1e3:.1f} | "
+              f"{e[3] / 1e3:.1f} | {100 * e[1] / tot:.1f} |")
+
+
+def _counter_by_grid(root, counter, pattern):
+    import re
+    per = {}
+    for r in _csv_rows(root, "counter_collection.csv"):
+        if _col(r, "Counter_Name") != counter or not re.search(pattern, _col(r, "Kernel_Name")):
+            continue
+        per.setdefault(_grid(r), []).append(float(_col(r, "Counter_Value")))
+    if not per:
+        raise SystemExit(f"no {counter} records for /{pattern}/ under {root}")
+    grid = max(per, key=lambda g: len(per[g]))
+    v = per[grid]
+    return grid, len(v), sum(v) / len(v)
+
+
+def pmc_summary(root):
+    """HBM traffic per decode launch of each kernel in OP_KERNELS, calibrated on a plain copy.
+
+    root holds four rocprofv3 --pmc runs: fetch_bench and write_bench (FETCH_SIZE resp.
+    WRITE_SIZE over the benchmark), fetch_copy and write_copy (the same counters over
+    --copy-probe-mib, whose kernel reads and writes a known number of bytes), and
+    copy_probe.log, the probe's own output.
+    """
+    import re
+    copy_bytes = None
+    for line in open(os.path.join(root, "copy_probe.log")):
+        m = re.match(r"(\d+) bytes read and", line)
+        if m:
+            copy_bytes = int(m.group(1))
+    _, _, cf = _counter_by_grid(os.path.join(root, "fetch_copy"), "FETCH_SIZE", COPY_KERNEL)
+    _, _, cw = _counter_by_grid(os.path.join(root, "write_copy"), "WRITE_SIZE", COPY_KERNEL)
+    kf, kw = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    print(f"copy calibration: {copy_bytes} bytes each way; FETCH_SIZE {cf:.0f} KiB -> factor {kf:.4f}; "
+          f"WRITE_SIZE {cw:.0f} KiB -> factor {kw:.4f}\n")
+    print("| op | kernel | grid | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | traffic bytes (calibrated) |")
+    print("|---|---|---|---|---|---|---|")
+    rec = {}
+    for op, (pat, files) in OP_KERNELS.items():
+        try:
+            g, n, f = _counter_by_grid(os.path.join(root, "fetch_bench"), "FETCH_SIZE", pat)
+            g2, _, w = _counter_by_grid(os.path.join(root, "write_bench"), "WRITE_SIZE", pat)
+        except SystemExit:
+            continue
+        t = f * 1024 * kf + w * 1024 * kw
+        rec[op] = {"grid": g, "traffic_bytes": t, "fetch_kib": f, "write_kib": w,
+                   "source_sha": kernel_source_sha(files)}
+        print(f"| {op} | `{pat}` | {g}/{g2} | {n} | {f:.0f} | {w:.0f} | {t:.4g} |")
+    print("\n```json\n" + json.dumps({"calibration": {"fetch": kf, "write": kw}, "ops": rec}, indent=1) + "\n```")
+
+
+def load_traffic(op):
+    """Calibrated HBM bytes per launch of op from the committed counter summary, or None when
+    there is none or the kernel's source has changed since the counters were taken."""
+    import re
+    if not os.path.exists(TRAFFIC_FILE) or op not in OP_KERNELS:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(TRAFFIC_FILE).read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))["ops"].get(op)
+    if not rec or rec["source_sha"] != kernel_source_sha(OP_KERNELS[op][1]):
+        return None
+    return rec["traffic_bytes"]
+
+
+def copy_probe(mib):
+    """A plain device copy of a known size: the counters' calibration kernel."""
+    import torch
+    n = mib * 2**20 // 4
+    x = torch.randn(n, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    print(f"{n * 4} bytes read and {n * 4} bytes written per torch.neg launch", flush=True)
 
 
 def cpu_baseline(shape, weights, eng, B, N, T):
@@ -128,6 +289,12 @@ def cpu_baseline(shape, weights, eng, B, N, T):
 
 def main():
     args = parse()
+    if args.trace_summary:
+        return trace_summary(args.trace_summary)
+    if args.pmc_summary:
+        return pmc_summary(args.pmc_summary)
+    if args.copy_probe_mib:
+        return copy_probe(args.copy_probe_mib)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
         sys.exit(2)
@@ -215,6 +382,7 @@ def main():
         gbs = d.get("GBps", 0.0)
         roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": gbs / HBM_PEAK_GBS, "traffic": None}
+    roof["traffic"] = load_traffic(dom)
     roof["kernel"] = dom
     roof["per_launch"] = {"bytes": b, "flops": f, "avg_us": d["avg_us"]}
     sb = step_bytes(shape, B * R, ctx_rows / P)
@@ -231,7 +399,7 @@ def main():
         "step_hbm_GBps": sb / (ms * 1e-3) / 1e9,
         "step_hbm_frac": sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "step_algorithmic_bytes": sb,
-        "projected_tokens_per_s_at_p0.9": args.steps / elapsed * B * 2.919,
+        "projected_tokens_per_s_at_p0.9": args.steps / elapsed * B * tpf_projection(0.9, N),
         "roofline": roof,
         "kernels": kernels,
     }
