@@ -29,7 +29,7 @@ class GemmArgs(C.Structure):
     _fields_ = [("dtype", C.c_int32), ("mode", C.c_int32), ("M", C.c_int32), ("N", C.c_int32), ("K", C.c_int32),
                 ("splits", C.c_int32), ("X", C.c_void_p), ("W", C.c_void_p), ("W2", C.c_void_p), ("Y", C.c_void_p),
                 ("R", C.c_void_p), ("workspace", C.c_void_p), ("norm_g", C.c_void_p), ("norm_out", C.c_void_p),
-                ("norm_eps", C.c_float)]
+                ("norm_eps", C.c_float), ("path", C.c_int32)]
 
 
 class ProfEntry(C.Structure):

@@ -153,7 +153,10 @@ struct GemmArgs {
   const void* norm_g;
   void* norm_out;
   float norm_eps;
+  int path;                  // bf16 kernel choice: GEMM_PATH_AUTO / _TILED / _SKINNY
 };
+enum { GEMM_PATH_AUTO = 0, GEMM_PATH_TILED = 1, GEMM_PATH_SKINNY = 2 };
+constexpr int kSkinnyMaxRows = 64;   // the skinny kernel holds at most two 32-row MFMA tiles
 
 // Split-K factor of a bf16 projection: a function of the output width and K only (never of
 // the row count), so that a row's result is the same whatever the batch composition.

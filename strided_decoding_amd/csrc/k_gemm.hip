@@ -26,6 +26,10 @@ constexpr int BK = 32;            // k per pipeline stage (one MFMA k-step)
 constexpr int TM2 = 224, TN2 = 256;
 constexpr int NST = 5;            // LDS ring depth (5 x 30 KB)
 constexpr int GROUP_BYTES = 16 * BK * 2;                 // 16 rows x 64 B
+#ifndef ISD_SKINNY_STAGES
+#define ISD_SKINNY_STAGES 6
+#endif
+constexpr int kSkinnyStages = ISD_SKINNY_STAGES;         // LDS ring depth of the skinny kernel
 constexpr int STAGE_BYTES = (TM2 + TN2) / 16 * GROUP_BYTES;  // 30 KB
 
 template <typename T, int EPI>
@@ -239,6 +243,129 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs a, int n
   }
 }
 
+// Skinny path for at most 64 rows (decode at small batch, where a projection is bound by
+// streaming its weights from HBM).  One single-wave workgroup per (output-column group, K
+// split); no barriers.  The wave streams its weight rows and the (L2-resident) activation
+// rows through a private SD-stage LDS ring filled by direct global->LDS loads: lane l writes
+// the 16 bytes it will read back as its MFMA operand, so the ring needs no swizzle and the
+// loads of SD-1 stages stay in flight under explicit vmcnt waits while one stage is
+// multiplied.  The MFMA (32x32x16), the k-chunk held by each lane, the k-step order, the split
+// rule and the partial layout are those of the tiled kernel, so every output element is
+// accumulated in exactly the same order and the two paths give bit-identical results.
+template <int EPI, bool PARTIAL, int MT, int SD>
+__global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_nt, int S, float* part) {
+  constexpr bool DUAL = (EPI == EPI_SWIGLU);
+  constexpr int NB = 2;                     // 32-column MFMA tiles per wave (gate + up for SwiGLU)
+  constexpr int TNO = DUAL ? 32 : 64;       // output columns per wave
+  constexpr int OPS = MT + NB;              // operand tiles per 16-k step
+  constexpr int STAGE = OPS * 2 * 1024;     // bytes per 32-k stage: OPS tiles x 2 k-steps x 1 KB
+  constexpr int PER_STAGE = OPS * 2;        // direct loads per stage
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SD * STAGE];
+  const int lane = threadIdx.x;
+  const int unit = blockIdx.x;
+  const int sp = unit / n_nt, nt = unit - sp * n_nt;
+  const int kt_per = (a.K / BK) / S;
+  const int kbase = sp * kt_per * BK;
+  const int n0 = nt * TNO;
+  const int r32 = lane & 31, khi = lane >> 5;
+
+  // lane operand: row / column r32 of a 32-wide tile, k-values 8 khi .. 8 khi + 7 of a 16-k step
+  const uint16_t* src[OPS];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int m = 32 * i + r32;
+    int srow = 0;
+    if (m < a.M) {
+      srow = a.a_rows ? a.a_rows[m] : m;
+      if (srow < 0) srow = 0;                 // unused row (its outputs are never consumed)
+    }
+    src[i] = (const uint16_t*)a.A + (size_t)srow * a.lda + kbase + khi * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const uint16_t* bm = (const uint16_t*)((DUAL && j) ? a.B1 : a.B0);
+    const int n = min(DUAL ? n0 + r32 : n0 + 32 * j + r32, a.N - 1);
+    src[MT + j] = bm + (size_t)n * a.ldb + kbase + khi * 8;
+  }
+
+  // stage kt -> ring slot kt % SD; tile t, k-step kk at slot + (2 t + kk) KB, lane l at + 16 l
+  auto issue = [&](int kt) {
+    uint8_t* st = smem + (kt % SD) * STAGE;
+    const int koff = kt * BK;
+#pragma unroll
+    for (int t = 0; t < OPS; ++t)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        __builtin_amdgcn_global_load_lds((const void*)(src[t] + koff + 16 * kk), (lds_void*)(st + (2 * t + kk) * 1024),
+                                         16, 0, 0);
+  };
+  f32x16_t acc[MT][NB];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  auto mul = [&](int kt) {
+    const uint8_t* st = smem + (kt % SD) * STAGE + 16 * lane;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8_t x[OPS];
+#pragma unroll
+      for (int t = 0; t < OPS; ++t) x[t] = as_bf16x8(*(const u32x4_t*)(st + (2 * t + kk) * 1024));
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma32x32x16(x[i], x[MT + j], acc[i][j]);
+    }
+  };
+
+  // Stage kt is issued SD-1 steps before it is multiplied; before multiplying it, at most the
+  // loads of the stages issued after it may be outstanding.
+  const int pro = min(SD - 1, kt_per);
+  for (int kt = 0; kt < pro; ++kt) issue(kt);
+  int kt = 0;
+  for (; kt + SD - 1 < kt_per; ++kt) {
+    issue(kt + SD - 1);
+    wait_vmcnt<(SD - 1) * PER_STAGE>();
+    mul(kt);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  wait_vmcnt<0>();
+  for (; kt < kt_per; ++kt) mul(kt);
+
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 32 * i + 8 * (r >> 2) + 4 * khi + (r & 3);
+      if (row >= a.M) continue;
+      if (DUAL) {
+        const int col = n0 + r32;
+        if (PARTIAL) {
+          if (col < a.N) {
+            float* pr = part + ((size_t)sp * a.M + row) * (2 * (size_t)a.N);
+            pr[col] = acc[i][0][r];
+            pr[a.N + col] = acc[i][1][r];
+          }
+        } else {
+          epilogue_store_t<bf16, EPI>(a, row, col, acc[i][0][r], acc[i][1][r]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int col = n0 + 32 * j + r32;
+          if (PARTIAL) {
+            if (col < a.N) part[((size_t)sp * a.M + row) * (size_t)a.N + col] = acc[i][j][r];
+          } else {
+            epilogue_store_t<bf16, EPI>(a, row, col, acc[i][j][r], 0.f);
+          }
+        }
+      }
+    }
+  }
+}
+
 // Sum the split-K partials in split order and apply the epilogue.
 template <int EPI>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a, int S, const float* part) {
@@ -363,6 +490,27 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
       epilogue_store_t<float, EPI>(a, m0 + ty * 4 + i, n0 + tx * 4 + j, acc[i][j], accu[i][j]);
 }
 
+// After the main kernel: the ordered split-K reduction (fused with the residual update and the
+// next RMSNorm when asked), or the standalone RMSNorm when there is no split.
+template <int EPI>
+hipError_t finish(const GemmArgs& a, int S, hipStream_t s) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const bool norm = EPI == EPI_RESID && a.norm_out;
+  if (S > 1) {
+    if (norm) {
+      hipLaunchKernelGGL(splitk_resid_norm_kernel, dim3(a.M), dim3(kNormThreads), 0, s, a, S, (const float*)a.part);
+      return hipGetLastError();
+    }
+    const size_t n4 = (size_t)a.M * a.N / 4;
+    const int blocks = (int)std::min<size_t>((n4 + 255) / 256, 4096);
+    hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3(blocks), dim3(256), 0, s, a, S, (const float*)a.part);
+    return hipGetLastError();
+  }
+  if (norm) return launch_rmsnorm<bf16>(a.R, (const bf16*)a.norm_g, (bf16*)a.norm_out, a.M, a.N, a.norm_eps, s);
+  return hipSuccess;
+}
+
 template <int EPI>
 hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
   const bool dual = EPI == EPI_SWIGLU;
@@ -371,25 +519,35 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
   const int S = (a.splits > 1 && a.part) ? a.splits : 1;
   const int units = n_nt * S;
   dim3 grid(((units + 7) / 8) * 8 * n_mt);
-  const bool norm = EPI == EPI_RESID && a.norm_out;
-  if (S > 1) {
+  if (S > 1)
     hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, true>), grid, dim3(256), 0, s, a, n_mt, units, S, a.part);
-    if (norm) {
-      hipLaunchKernelGGL(splitk_resid_norm_kernel, dim3(a.M), dim3(kNormThreads), 0, s, a, S, (const float*)a.part);
-      return hipGetLastError();
-    }
-    const size_t n4 = (size_t)a.M * a.N / 4;
-    const int blocks = (int)std::min<size_t>((n4 + 255) / 256, 4096);
-    hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3(blocks), dim3(256), 0, s, a, S, (const float*)a.part);
-  } else {
+  else
     hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, false>), grid, dim3(256), 0, s, a, n_mt, units, 1, nullptr);
+  return finish<EPI>(a, S, s);
+}
+
+template <int EPI>
+hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
+  constexpr int SD = kSkinnyStages;
+  const int tno = EPI == EPI_SWIGLU ? 32 : 64;
+  const int n_nt = (a.N + tno - 1) / tno;
+  const int S = (a.splits > 1 && a.part) ? a.splits : 1;
+  dim3 grid(n_nt * S);
+  float* part = S > 1 ? a.part : nullptr;
+  if (a.M <= 32) {
+    if (S > 1) hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, true, 1, SD>), grid, dim3(64), 0, s, a, n_nt, S, part);
+    else hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, false, 1, SD>), grid, dim3(64), 0, s, a, n_nt, S, part);
+  } else {
+    if (S > 1) hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, true, 2, SD>), grid, dim3(64), 0, s, a, n_nt, S, part);
+    else hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, false, 2, SD>), grid, dim3(64), 0, s, a, n_nt, S, part);
   }
-  if (norm) {
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_rmsnorm<bf16>(a.R, (const bf16*)a.norm_g, (bf16*)a.norm_out, a.M, a.N, a.norm_eps, s);
-  }
-  return hipGetLastError();
+  return finish<EPI>(a, S, s);
+}
+
+template <int EPI>
+hipError_t launch_path(const GemmArgs& a, hipStream_t s) {
+  const bool skinny = a.path == GEMM_PATH_SKINNY || (a.path == GEMM_PATH_AUTO && a.M <= kSkinnyMaxRows);
+  return skinny ? launch_skinny<EPI>(a, s) : launch_big<EPI>(a, s);
 }
 
 }  // namespace
@@ -412,11 +570,12 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if ((a.splits > 1 && a.part) && a.splits > kMaxSplits) return hipErrorInvalidValue;
   const int S = (a.splits > 1 && a.part) ? a.splits : 1;
   if ((a.K / BK) % S != 0) return hipErrorInvalidValue;
+  if (a.path == GEMM_PATH_SKINNY && a.M > kSkinnyMaxRows) return hipErrorInvalidValue;
   switch (a.epi) {
-    case EPI_STORE: return launch_big<EPI_STORE>(a, s);
-    case EPI_STORE_F32: return launch_big<EPI_STORE_F32>(a, s);
-    case EPI_RESID: return launch_big<EPI_RESID>(a, s);
-    case EPI_SWIGLU: return launch_big<EPI_SWIGLU>(a, s);
+    case EPI_STORE: return launch_path<EPI_STORE>(a, s);
+    case EPI_STORE_F32: return launch_path<EPI_STORE_F32>(a, s);
+    case EPI_RESID: return launch_path<EPI_RESID>(a, s);
+    case EPI_SWIGLU: return launch_path<EPI_SWIGLU>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

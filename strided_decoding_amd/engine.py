@@ -211,11 +211,15 @@ def attn_paged(q, k_pool, v_pool, page_table, ctx_len, q_len, n_kv_heads, out=No
     return out, workspace, args
 
 
+GEMM_PATHS = {"auto": 0, "tiled": 1, "skinny": 2}
+
+
 def gemm(X, W, mode="store", W2=None, out=None, R=None, splits=0, workspace=None, stream=None,
-         norm_g=None, norm_out=None, norm_eps=1e-6):
+         norm_g=None, norm_out=None, norm_eps=1e-6, path="auto"):
     """Kernel-level projection (see isd_gemm): X [M, K], W [N, K] (bf16 or float32 on device).
 
-    mode "resid" with norm_g / norm_out also writes RMSNorm(R) * norm_g into norm_out."""
+    mode "resid" with norm_g / norm_out also writes RMSNorm(R) * norm_g into norm_out.
+    path: "auto", "tiled" or "skinny" (bf16 kernel choice; M <= 64 for skinny)."""
     lib = A.load()
     M, K = X.shape
     N = W.shape[0]
@@ -233,7 +237,7 @@ def gemm(X, W, mode="store", W2=None, out=None, R=None, splits=0, workspace=None
                       0 if W2 is None else W2.data_ptr(), 0 if out is None else out.data_ptr(),
                       0 if R is None else R.data_ptr(), 0 if workspace is None else workspace.data_ptr(),
                       0 if norm_g is None else norm_g.data_ptr(), 0 if norm_out is None else norm_out.data_ptr(),
-                      float(norm_eps))
+                      float(norm_eps), GEMM_PATHS[path])
     stream = stream if stream is not None else torch.cuda.current_stream(X.device)
     A.check("isd_gemm", lib.isd_gemm(C.byref(args), C.c_void_p(stream.cuda_stream)))
     return out if md != A.ISD_GEMM_RESID else R

@@ -126,6 +126,57 @@ def test_gemm_residual_with_fused_rmsnorm(splits):
     _check(y.float().cpu().numpy().ravel(), yref.ravel())
 
 
+SKINNY_ROWS = [1, 7, 28, 32, 33, 56, 64]
+
+
+@pytest.mark.parametrize("M", SKINNY_ROWS)
+@pytest.mark.parametrize("mode,N,K", [("store", 6144, 4096), ("store_f32", 2048, 4096), ("resid", 4096, 4096),
+                                      ("swiglu", 1536, 4096), ("resid", 512, 12288), ("store", 200, 96)])
+def test_skinny_path_bit_identical_to_tiled(M, mode, N, K):
+    """The two bf16 kernels accumulate every output in the same order: bit-identical results."""
+    from strided_decoding_amd import gemm
+    print(f"skinny vs tiled {mode} M={M} N={N} K={K}", flush=True)
+    X = _rand((M, K), 30 + M, 1.0)
+    W = _rand((N, K), 31, 0.02)
+    W2 = _rand((N, K), 32, 0.02) if mode == "swiglu" else None
+    outs = []
+    for path in ("tiled", "skinny"):
+        if mode == "resid":
+            R = _rand((M, N), 33, 1.0, torch.float32)
+            outs.append(gemm(X, W, mode, R=R, path=path))
+        else:
+            outs.append(gemm(X, W, mode, W2=W2, path=path))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    if M in (7, 56):
+        rows, cols = _pick(M, N, 300, 34)
+        ref = _ref(X, W, rows, cols)
+        if mode == "swiglu":
+            u = _ref(X, W2, rows, cols)
+            ref = ref / (1 + np.exp(-ref)) * u
+        if mode == "resid":
+            ref = ref + _rand((M, N), 33, 1.0, torch.float32).cpu().numpy().astype(np.float64)[rows, cols]
+        _check(outs[1].float().cpu().numpy()[rows, cols], ref, bf16=mode in ("store", "swiglu"))
+
+
+@pytest.mark.parametrize("splits", [0, 1])
+def test_skinny_fused_rmsnorm_and_row_gather(splits):
+    """Skinny path with the fused residual + RMSNorm, and equal to the tiled path bit for bit."""
+    from strided_decoding_amd import gemm
+    M, d, F = 56, 4096, 12288
+    H = _rand((M, F), 40, 1.0)
+    Wd = _rand((d, F), 41, 0.02)
+    g = (1.0 + 0.1 * _rand((d,), 42, 1.0, torch.float32)).to(torch.bfloat16)
+    res = []
+    for path in ("tiled", "skinny"):
+        R = _rand((M, d), 43, 1.0, torch.float32)
+        y = torch.empty((M, d), dtype=torch.bfloat16, device=DEV)
+        gemm(H, Wd, "resid", R=R, splits=splits, norm_g=g, norm_out=y, norm_eps=1e-6, path=path)
+        res.append((R, y))
+    torch.cuda.synchronize()
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
 def test_gemm_fp32_path():
     from strided_decoding_amd import gemm
     X = _rand((37, 200), 15, 1.0, torch.float32)
