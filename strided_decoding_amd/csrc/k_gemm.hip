@@ -26,10 +26,14 @@ constexpr int BK = 32;            // k per pipeline stage (one MFMA k-step)
 constexpr int TM2 = 224, TN2 = 256;
 constexpr int NST = 5;            // LDS ring depth (5 x 30 KB)
 constexpr int GROUP_BYTES = 16 * BK * 2;                 // 16 rows x 64 B
-#ifndef ISD_SKINNY_STAGES
-#define ISD_SKINNY_STAGES 6
+#ifndef ISD_SKINNY_STAGES_1
+#define ISD_SKINNY_STAGES_1 10
 #endif
-constexpr int kSkinnyStages = ISD_SKINNY_STAGES;         // LDS ring depth of the skinny kernel
+#ifndef ISD_SKINNY_STAGES_2
+#define ISD_SKINNY_STAGES_2 8
+#endif
+// LDS ring depth of the skinny kernel for one / two 32-row tiles
+constexpr int kSkinnyStages1 = ISD_SKINNY_STAGES_1, kSkinnyStages2 = ISD_SKINNY_STAGES_2;
 constexpr int STAGE_BYTES = (TM2 + TN2) / 16 * GROUP_BYTES;  // 30 KB
 
 template <typename T, int EPI>
@@ -246,10 +250,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs a, int n
 // Skinny path for at most 64 rows (decode at small batch, where a projection is bound by
 // streaming its weights from HBM).  One single-wave workgroup per (output-column group, K
 // split); no barriers.  The wave streams its weight rows and the (L2-resident) activation
-// rows through a private SD-stage LDS ring filled by direct global->LDS loads: lane l writes
-// the 16 bytes it will read back as its MFMA operand, so the ring needs no swizzle and the
-// loads of SD-1 stages stay in flight under explicit vmcnt waits while one stage is
-// multiplied.  The MFMA (32x32x16), the k-chunk held by each lane, the k-step order, the split
+// rows through a private SD-stage LDS ring filled by direct global->LDS loads, with the loads
+// of SD-1 stages in flight under explicit vmcnt waits while one stage is multiplied.  The MFMA (32x32x16), the k-chunk held by each lane, the k-step order, the split
 // rule and the partial layout are those of the tiled kernel, so every output element is
 // accumulated in exactly the same order and the two paths give bit-identical results.
 template <int EPI, bool PARTIAL, int MT, int SD>
@@ -258,8 +260,9 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_
   constexpr int NB = 2;                     // 32-column MFMA tiles per wave (gate + up for SwiGLU)
   constexpr int TNO = DUAL ? 32 : 64;       // output columns per wave
   constexpr int OPS = MT + NB;              // operand tiles per 16-k step
-  constexpr int STAGE = OPS * 2 * 1024;     // bytes per 32-k stage: OPS tiles x 2 k-steps x 1 KB
+  constexpr int STAGE = OPS * 2 * 1024;     // bytes per 32-k stage: OPS tiles x 2 row groups x 1 KB
   constexpr int PER_STAGE = OPS * 2;        // direct loads per stage
+  static_assert((SD - 1) * PER_STAGE < 64, "vmcnt counts at most 63 outstanding loads");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SD * STAGE];
   const int lane = threadIdx.x;
   const int unit = blockIdx.x;
@@ -269,35 +272,45 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_
   const int n0 = nt * TNO;
   const int r32 = lane & 31, khi = lane >> 5;
 
-  // lane operand: row / column r32 of a 32-wide tile, k-values 8 khi .. 8 khi + 7 of a 16-k step
-  const uint16_t* src[OPS];
+  // Loader (the tiled kernel's 16-row group layout): one direct load per 16-row group and
+  // stage; lane l fills LDS bytes [16 l, 16 l + 16) of the group with row l/4, k-chunk
+  // (l%4) ^ ((row/4)%4), so every instruction reads 64 contiguous bytes of 16 rows and the
+  // operand reads below are free of bank conflicts.
+  const int lrow = lane >> 2;
+  const int chunk = (lane & 3) ^ ((lrow >> 2) & 3);
+  const uint16_t* src[OPS][2];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    const int m = 32 * i + r32;
-    int srow = 0;
-    if (m < a.M) {
-      srow = a.a_rows ? a.a_rows[m] : m;
-      if (srow < 0) srow = 0;                 // unused row (its outputs are never consumed)
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int m = 32 * i + 16 * g + lrow;
+      int srow = 0;
+      if (m < a.M) {
+        srow = a.a_rows ? a.a_rows[m] : m;
+        if (srow < 0) srow = 0;               // unused row (its outputs are never consumed)
+      }
+      src[i][g] = (const uint16_t*)a.A + (size_t)srow * a.lda + kbase + chunk * 8;
     }
-    src[i] = (const uint16_t*)a.A + (size_t)srow * a.lda + kbase + khi * 8;
-  }
 #pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const uint16_t* bm = (const uint16_t*)((DUAL && j) ? a.B1 : a.B0);
-    const int n = min(DUAL ? n0 + r32 : n0 + 32 * j + r32, a.N - 1);
-    src[MT + j] = bm + (size_t)n * a.ldb + kbase + khi * 8;
-  }
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const uint16_t* bm = (const uint16_t*)((DUAL && j) ? a.B1 : a.B0);
+      const int r = 16 * g + lrow;
+      const int n = min(DUAL ? n0 + r : n0 + 32 * j + r, a.N - 1);
+      src[MT + j][g] = bm + (size_t)n * a.ldb + kbase + chunk * 8;
+    }
 
-  // stage kt -> ring slot kt % SD; tile t, k-step kk at slot + (2 t + kk) KB, lane l at + 16 l
+  // stage kt -> ring slot kt % SD; tile t, row group g at slot + (2 t + g) KB
   auto issue = [&](int kt) {
     uint8_t* st = smem + (kt % SD) * STAGE;
     const int koff = kt * BK;
 #pragma unroll
     for (int t = 0; t < OPS; ++t)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        __builtin_amdgcn_global_load_lds((const void*)(src[t] + koff + 16 * kk), (lds_void*)(st + (2 * t + kk) * 1024),
-                                         16, 0, 0);
+      for (int g = 0; g < 2; ++g)
+        __builtin_amdgcn_global_load_lds((const void*)(src[t][g] + koff), (lds_void*)(st + (2 * t + g) * 1024), 16, 0,
+                                         0);
   };
   f32x16_t acc[MT][NB];
 #pragma unroll
@@ -306,13 +319,18 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // operand of lane L: row r32 (group r32/16, row r32%16), k-chunk 2 kk + khi, swizzled
+  const int rig = r32 & 15;
+  const int rd0 = (r32 >> 4) * 1024 + rig * 64;
+  const int sw = (rig >> 2) & 3;
   auto mul = [&](int kt) {
-    const uint8_t* st = smem + (kt % SD) * STAGE + 16 * lane;
+    const uint8_t* st = smem + (kt % SD) * STAGE + rd0;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
+      const int off = ((2 * kk + khi) ^ sw) * 16;
       bf16x8_t x[OPS];
 #pragma unroll
-      for (int t = 0; t < OPS; ++t) x[t] = as_bf16x8(*(const u32x4_t*)(st + (2 * t + kk) * 1024));
+      for (int t = 0; t < OPS; ++t) x[t] = as_bf16x8(*(const u32x4_t*)(st + 2 * t * 1024 + off));
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -528,18 +546,18 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
 
 template <int EPI>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
-  constexpr int SD = kSkinnyStages;
+  constexpr int SD1 = kSkinnyStages1, SD2 = kSkinnyStages2;
   const int tno = EPI == EPI_SWIGLU ? 32 : 64;
   const int n_nt = (a.N + tno - 1) / tno;
   const int S = (a.splits > 1 && a.part) ? a.splits : 1;
   dim3 grid(n_nt * S);
   float* part = S > 1 ? a.part : nullptr;
   if (a.M <= 32) {
-    if (S > 1) hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, true, 1, SD>), grid, dim3(64), 0, s, a, n_nt, S, part);
-    else hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, false, 1, SD>), grid, dim3(64), 0, s, a, n_nt, S, part);
+    if (S > 1) hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, true, 1, SD1>), grid, dim3(64), 0, s, a, n_nt, S, part);
+    else hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, false, 1, SD1>), grid, dim3(64), 0, s, a, n_nt, S, part);
   } else {
-    if (S > 1) hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, true, 2, SD>), grid, dim3(64), 0, s, a, n_nt, S, part);
-    else hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, false, 2, SD>), grid, dim3(64), 0, s, a, n_nt, S, part);
+    if (S > 1) hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, true, 2, SD2>), grid, dim3(64), 0, s, a, n_nt, S, part);
+    else hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, false, 2, SD2>), grid, dim3(64), 0, s, a, n_nt, S, part);
   }
   return finish<EPI>(a, S, s);
 }
