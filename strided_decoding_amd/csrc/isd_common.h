@@ -23,16 +23,14 @@ ISD_DEV T from_f(float f);
 template <>
 ISD_DEV float from_f<float>(float f) { return f; }
 template <>
-ISD_DEV bf16 from_f<bf16>(float f) {
-  uint32_t u = __float_as_uint(f);
+ISD_DEV bf16 from_f<bf16>(float f) {   // v_cvt_pk_bf16_f32: round to nearest even
   bf16 r;
-  if ((u & 0x7fffffffu) > 0x7f800000u) {
-    r.u = (uint16_t)((u >> 16) | 0x40u);
-  } else {
-    u += 0x7fffu + ((u >> 16) & 1u);
-    r.u = (uint16_t)(u >> 16);
-  }
+  r.u = __builtin_bit_cast(uint16_t, (__bf16)f);
   return r;
+}
+// Two floats rounded to bf16 (nearest even) and packed, lo in the low half.
+ISD_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
 }
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;   // MFMA operand (8 bf16)
@@ -112,7 +110,17 @@ ISD_DEV double philox_uniform(uint64_t seed, uint32_t slot, uint32_t t, uint32_t
 
 // One attention work item: nq consecutive query positions pos0 .. pos0+nq-1 of `slot`,
 // stored in activation rows row0 .. row0+nq-1.
-struct AttnItem {
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Wait until at most N vector-memory operations of this wave are outstanding (direct
+// global->LDS loads included: their data is in LDS once they are no longer counted).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+struct AttnItem {              // query rows row0 .. row0+nq-1 of one slot at positions pos0 ..
   int32_t slot, row0, nq, pos0;
 };
 
@@ -125,7 +133,6 @@ struct ChunkStat {
 };
 
 constexpr int kStatChunk = 4096;        // logits per statistics chunk
-constexpr int kAttnSplit = 256;         // keys per split-context partial (multiple of 32)
 
 enum EpiMode : int { EPI_STORE = 0, EPI_STORE_F32 = 1, EPI_RESID = 2, EPI_SWIGLU = 3 };
 
@@ -192,6 +199,10 @@ struct AttnArgs {
 };
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_combine_bf16(const AttnArgs& a, hipStream_t s);
+// Keys per context split of a decode pass, from the number of slots the context serves: short
+// splits when few slots must still fill the chip, long ones when partials would cost bytes.
+// Fixed per context, so a row's attention never depends on the other rows of a pass.
+int attn_split_len(int batch);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 
 template <typename T>

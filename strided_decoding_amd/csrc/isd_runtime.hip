@@ -44,6 +44,7 @@ struct isd_ctx {
   size_t act;             // bytes per activation element
   int R, qd, kd, qkvw;
   int max_pages, max_rows, max_dec_rows, n_chunks, max_splits, items_per_slot, q_max, ncb, q_tile;
+  int attn_split;         // keys per context split of a decode pass
   int max_items, n_mask, delta_w;
   size_t part_floats = 0;       // split-K partial buffer (bf16 decode GEMMs)
   float* gemm_part = nullptr;
@@ -191,7 +192,8 @@ void derive(isd_ctx& x) {
   x.max_dec_rows = c.max_batch * x.R;
   x.max_rows = std::max(x.max_dec_rows, c.max_prefill_tokens);
   x.n_chunks = cdiv(c.vocab, kStatChunk);
-  x.max_splits = cdiv(c.max_seq_len + 2 * c.stride_n, kAttnSplit);
+  x.attn_split = attn_split_len(c.max_batch);
+  x.max_splits = cdiv(c.max_seq_len + 2 * c.stride_n, x.attn_split);
   const int G = c.n_q_heads / c.n_kv_heads;
   x.ncb = (x.R * G <= 32) ? 2 : 4;
   x.q_max = std::max(1, 16 * x.ncb / G);
@@ -386,7 +388,7 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
       if (!x.bf) {
         TIMED("attention", launch_attn_f32(aa, s));
       } else if (decode) {
-        aa.split = kAttnSplit;
+        aa.split = x.attn_split;
         aa.max_splits = x.max_splits;
         aa.part_o = x.part_o;
         aa.part_ml = x.part_ml;
@@ -699,7 +701,7 @@ isd_status isd_profile_report(isd_ctx* x, isd_prof_entry* out, int32_t cap, int3
 
 size_t isd_attn_workspace_bytes(const isd_attn_args* a) {
   if (!a) return 0;
-  const int splits = cdiv(std::max(1, a->max_ctx), kAttnSplit);
+  const int splits = cdiv(std::max(1, a->max_ctx), attn_split_len(a->batch));
   const size_t rows = (size_t)a->batch * a->rows;
   size_t off = 0;
   off = align_up(off + a->batch * sizeof(AttnItem));
@@ -718,7 +720,8 @@ isd_status isd_attn_paged(const isd_attn_args* a, void* stream) {
     return ISD_E_ARG;
   const int G = a->n_q_heads / a->n_kv_heads;
   if (a->head_dim != 128 || a->page_size != 16 || G * a->rows > 64) return ISD_E_SHAPE;
-  const int splits = cdiv(a->max_ctx, kAttnSplit);
+  const int split = attn_split_len(a->batch);
+  const int splits = cdiv(a->max_ctx, split);
   const size_t rows = (size_t)a->batch * a->rows;
   char* w = (char*)a->workspace;
   size_t off = 0;
@@ -747,7 +750,7 @@ isd_status isd_attn_paged(const isd_attn_args* a, void* stream) {
   aa.hd = a->head_dim;
   aa.P = a->page_size;
   aa.ncb = G * a->rows <= 32 ? 2 : 4;
-  aa.split = kAttnSplit;
+  aa.split = split;
   aa.max_splits = splits;
   aa.part_o = part_o;
   aa.part_ml = part_ml;

@@ -2,34 +2,61 @@
 // of consecutive prompt positions).  Keys and values are read only from the KV pages, the
 // block's own K/V having been appended first, and a row at position p sees keys 0 .. p.
 //
-// bf16 path (head_dim 128): one wave per (item, KV head, context split).  The up to 64 query
-// rows of a KV-head group (positions x G query heads) are the columns of two MFMA products
+// bf16 path (head_dim 128): one single-wave workgroup per (item, KV head, context split).
+// The up to 64 query rows of a KV-head group (positions x G query heads) are the columns of
+// two MFMA products
 //   S^T = K Q^T          (A = 16 keys x 32 dims per step, B = Q^T)
 //   O^T += V^T P^T       (A = V^T rows = dims, k = 32 keys; B = P^T)
-// so that every operand is a 16-byte contiguous load: K pages are [token][dim], V pages are
-// stored transposed [dim][token] within a page.  The key order inside a 32-key step is
-// permuted so that the S^T accumulator registers of a lane are exactly the P^T operand
-// slots of the next product (no cross-lane traffic).  Online softmax in the log2 domain with
-// wave reductions over the 4 lane groups sharing a column.  Context splits begin at
-// multiples of the split length and 32-key steps at absolute positions, and masked keys
-// contribute exact zeros, so a row's result does not depend on the other rows of its block.
+// K pages are [token][dim] and V pages [dim][token] (transposed within a page), so both
+// operands are 16-byte row chunks.  The wave streams its 32-key blocks (two 16-token pages of
+// K and of V, 16 KB) through a private NBUF-block LDS ring with direct global->LDS loads,
+// NBUF-1 blocks in flight under explicit vmcnt waits while one is multiplied; every load
+// instruction reads 1 KB of one page contiguously, and the chunks are XOR-swizzled in LDS so
+// the operand reads are free of bank conflicts.  The key order inside a block is permuted so
+// that the S^T accumulator registers of a lane are exactly the P^T operand slots of the next
+// product (no cross-lane traffic).  Online softmax in the log2 domain with wave reductions
+// over the 4 lane groups sharing a column.  Context splits begin at multiples of the split
+// length and blocks at absolute positions, and masked keys contribute exact zeros, so a
+// row's result does not depend on the other rows of its pass.  With splits, each split
+// writes fp32 partials (output, reference maximum, sum) and attn_combine_kernel merges them
+// in split order.  (A workgroup's global-memory handoff to another workgroup would need a
+// device-scope fence, which writes back the XCD's L2: a kernel boundary is cheaper.)
+#include <algorithm>
+
 #include "isd_common.h"
 
 namespace isd {
 namespace {
 
 constexpr int HD = 128;
+constexpr int kBlockBytes = 16384;         // one 32-key block: K and V, two pages each
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kRescale = 8.f;            // log2 headroom of the softmax reference maximum
+#ifndef ISD_ATTN_NBUF
+#define ISD_ATTN_NBUF 2
+#endif
+constexpr int kAttnBufs = ISD_ATTN_NBUF;
 
 ISD_DEV u32x4_t ld16(const uint16_t* p) { return *(const u32x4_t*)p; }
+ISD_DEV u32x4_t lds16(const uint8_t* p) { return *(const u32x4_t*)p; }
 
-template <int NCB>
-__global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a) {
+// Wait until no LDS (or scalar-memory) access of this wave is outstanding.
+ISD_DEV void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14)); }
+
+// One workgroup per (item, KV head, context split); wave w handles the 16 query columns
+// 16 w .. 16 w + 15 of the KV-head group and 16/NCB of the 16 loads of each KV block.
+template <int NCB, int NBUF>
+__global__ __launch_bounds__(64 * NCB) void attn_bf16_kernel(AttnArgs a) {
+  constexpr int PW = 16 / NCB;                       // KV loads per block issued by each wave
+  static_assert(NBUF >= 2 && NBUF <= 4 && (NBUF - 1) * PW + 4 < 64, "vmcnt counts at most 63 loads");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * kBlockBytes];
   const AttnItem it = a.items[blockIdx.x];
-  if (it.nq <= 0) return;
   const int kvh = blockIdx.y, split = blockIdx.z;
-  const int lane = threadIdx.x, lr = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
   const int G = a.Hq / a.Hkv;
+  const size_t q_stride = (size_t)a.Hq * HD;
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  if (it.nq <= 0) return;
   const int ctx = a.ctx_len[it.slot];
   const int key_hi = min(ctx, it.pos0 + it.nq);
   int k_begin = 0, k_end = key_hi;
@@ -39,209 +66,246 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a) {
     k_end = min(key_hi, k_begin + a.split);
   }
   const float scale = 1.4426950408889634f * rsqrtf((float)HD);
-  const uint16_t* q = (const uint16_t*)a.q;
-  const uint16_t* kp = (const uint16_t*)a.k_pool;
-  const uint16_t* vp = (const uint16_t*)a.v_pool;
-  const size_t q_stride = (size_t)a.Hq * HD;
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
 
-  bf16x8_t qf[NCB][4];
-  int qpos[NCB];
-  bool qvalid[NCB];
-#pragma unroll
-  for (int c = 0; c < NCB; ++c) {
-    const int qr = c * 16 + lr, p = qr / G, h = qr % G;
-    qvalid[c] = p < it.nq;
-    qpos[c] = it.pos0 + p;
-    const uint16_t* src = q + (size_t)(it.row0 + p) * q_stride + (size_t)(kvh * G + h) * HD + g * 8;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[c][ks] = as_bf16x8(qvalid[c] ? ld16(src + ks * 32) : zero);
-  }
+  // Q^T operand of this wave: lane (lr, g) holds query column 16 w + lr (position (16 w + lr)/G,
+  // head (16 w + lr) % G), dims 32 ks + 8 g .. +7, loaded by direct global->LDS loads into
+  // the last ring slot ahead of the first KV blocks (lane l reads back its own 16 bytes).
+  const int qcol = wave * 16 + lr, qp = qcol / G, qh = qcol % G;
+  const bool qvalid = qp < it.nq;
+  const int qpos = it.pos0 + qp;
+  const uint16_t* qsrc =
+      (const uint16_t*)a.q + (size_t)(it.row0 + (qvalid ? qp : 0)) * q_stride + (size_t)(kvh * G + qh) * HD + g * 8;
 
-  float m_run[NCB], l_run[NCB];
-  f32x4_t o[8][NCB];
-#pragma unroll
-  for (int c = 0; c < NCB; ++c) {
-    m_run[c] = kNegInf;
-    l_run[c] = 0.f;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) o[d][c] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  }
-
+  // Page ids of the key range, lane l holding logical page win + l (a window of 64 pages,
+  // 1024 keys; longer ranges reload it), read out with readlane: no memory access inside the
+  // KV pipeline besides its own loads.
   const int32_t* pt = a.page_table + (size_t)it.slot * a.max_pages;
+  const int last_page = (k_end - 1) >> 4;
+  int win = k_begin >> 4;
+  int pid = pt[min(win + lane, last_page)];
+  wait_vmcnt<0>();
+  auto page_of = [&](int pg) -> int {
+    if (pg >= win + 64) {
+      wait_vmcnt<0>();
+      win = pg;
+      pid = pt[min(win + lane, last_page)];
+      wait_vmcnt<0>();
+    }
+    return __builtin_amdgcn_readlane(pid, pg - win);
+  };
   const size_t page_elems = (size_t)a.Hkv * 16 * HD;
+  const uint16_t* kbase = (const uint16_t*)a.k_pool + (size_t)kvh * 16 * HD;
+  const uint16_t* vbase = (const uint16_t*)a.v_pool + (size_t)kvh * HD * 16;
 
-  for (int kb = k_begin; kb < k_end; kb += 32) {
-    // K: MFMA row i of key block b holds key kb + 8*(i/4) + 4*b + i%4
-    bf16x8_t kf[2][4];
+  // Block blk (keys k_begin + 32 blk ..) -> ring slot blk % NBUF: K at +0 (token t: 256 bytes at
+  // t * 256, dim chunk c in 16-byte slot c ^ h(t), h(t) = (t & 3) | ((t >> 1) & 12)); V at
+  // +8192 (page j at + 4096 j, dim row d: 32 bytes at d * 32, key half e in slot e ^ (d/8 % 2)).
+  // Load i < 8 of a block: K tokens 4i .. 4i+3; load 8 + i: V of page i/4, dims 32 (i%4) .. +31.
+  auto issue = [&](int blk) {
+    const int kb = k_begin + 32 * blk;
+    uint8_t* st = ring + (blk % NBUF) * kBlockBytes;
+    const int pg0 = page_of(kb >> 4);
+    const int pg1 = kb + 16 < k_end ? page_of((kb >> 4) + 1) : pg0;   // past the context: any valid page
+#pragma unroll
+    for (int jj = 0; jj < PW; ++jj) {
+      const int j = wave * PW + jj;
+      const uint16_t* src;
+      if (j < 8) {
+        const int t = 4 * j + (lane >> 4);
+        const int c = (lane & 15) ^ ((t & 3) | ((t >> 1) & 12));
+        src = kbase + (size_t)(j < 4 ? pg0 : pg1) * page_elems + (size_t)(t & 15) * HD + c * 8;
+      } else {
+        const int i = j - 8;
+        const int dim = 32 * (i & 3) + (lane >> 1);
+        const int e = (lane & 1) ^ ((dim >> 3) & 1);
+        src = vbase + (size_t)(i < 4 ? pg0 : pg1) * page_elems + (size_t)dim * 16 + e * 8;
+      }
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(st + j * 1024), 16, 0, 0);
+    }
+  };
+
+  bf16x8_t qf[4];
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4_t o[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) o[d] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+  // One 32-key block.  Softmax in the log2 domain against a per-column reference maximum m
+  // that is raised only when a block's maximum exceeds it by more than kRescale (so p <= 2^8
+  // and the accumulators are rescaled rarely); the sum l and the output use the same m, so
+  // the result is exact up to rounding.  Blocks whose keys are all visible to every row
+  // (below the first query position and inside the range) skip all masking.
+  auto compute = [&](int blk) {
+    const int kb = k_begin + 32 * blk;
+    const uint8_t* st = ring + (blk % NBUF) * kBlockBytes;
+    const bool tail = kb + 32 > k_end;               // keys past the range in this block
+    const bool clean = !tail && kb + 31 <= it.pos0;  // no causal or range mask
+    // K: MFMA row i of key block b holds key kb + 8*(i/4) + 4*b + i%4, whose swizzle h is i
+    f32x4_t s[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const int key = kb + 8 * (lr >> 2) + 4 * b + (lr & 3);
-      if (key < k_end) {
-        const uint16_t* base = kp + (size_t)pt[key >> 4] * page_elems + (size_t)(kvh * 16 + (key & 15)) * HD + g * 8;
+      const int t = 8 * (lr >> 2) + 4 * b + (lr & 3);
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kf[b][ks] = as_bf16x8(ld16(base + ks * 32));
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kf[b][ks] = as_bf16x8(zero);
-      }
+      for (int ks = 0; ks < 4; ++ks)
+        acc = mfma16x16x32(as_bf16x8(lds16(st + t * 256 + (((4 * ks + g) ^ lr) * 16))), qf[ks], acc);
+      s[b] = acc;
     }
-    // V^T: row d = dblk*16 + lr, keys kb + 8g .. kb + 8g + 7 (zero beyond k_end)
+    // V^T: row d = dblk*16 + lr, keys kb + 8g .. kb + 8g + 7 (zero past the range)
     bf16x8_t vf[8];
     {
-      const int key0 = kb + 8 * g;
-      if (key0 < k_end) {
-        const uint16_t* base = vp + (size_t)pt[key0 >> 4] * page_elems + (size_t)kvh * HD * 16 + (key0 & 15);
-        const int nvalid = k_end - key0;
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          u32x4_t raw = ld16(base + (size_t)(d * 16 + lr) * 16);
-          if (nvalid < 8) {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              const int j0 = 2 * w;
-              uint32_t m = 0u;
-              if (j0 < nvalid) m |= 0x0000ffffu;
-              if (j0 + 1 < nvalid) m |= 0xffff0000u;
-              raw[w] &= m;
-            }
-          }
-          vf[d] = as_bf16x8(raw);
-        }
-      } else {
-#pragma unroll
-        for (int d = 0; d < 8; ++d) vf[d] = as_bf16x8(zero);
-      }
-    }
-
-    bf16x8_t pf[NCB];
-#pragma unroll
-    for (int c = 0; c < NCB; ++c) {
-      f32x4_t s[2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(kf[b][ks], qf[c][ks], acc);
-        s[b] = acc;
-      }
-      float sv[8];
-      float mx = kNegInf;
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kb + 8 * g + 4 * b + r;
-          const bool vis = qvalid[c] && key < k_end && key <= qpos[c];
-          const float v = vis ? s[b][r] * scale : kNegInf;
-          sv[4 * b + r] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[c], mx);
-      float alpha = 1.f;
-      uint16_t pb[8];
-      float ps = 0.f;
-      if (m_new == kNegInf) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pb[j] = 0;
-      } else {
-        alpha = exp2f(m_run[c] - m_new);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const bf16 pbv = from_f<bf16>(exp2f(sv[j] - m_new));
-          pb[j] = pbv.u;
-          ps += to_f(pbv);
-        }
-      }
-      ps += __shfl_xor(ps, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
-      l_run[c] = l_run[c] * alpha + ps;
-      m_run[c] = m_new;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) o[d][c] *= alpha;
-      u32x4_t pk;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) pk[w] = (uint32_t)pb[2 * w] | ((uint32_t)pb[2 * w + 1] << 16);
-      pf[c] = as_bf16x8(pk);
-    }
-#pragma unroll
-    for (int d = 0; d < 8; ++d)
-#pragma unroll
-      for (int c = 0; c < NCB; ++c) o[d][c] = mfma16x16x32(vf[d], pf[c], o[d][c]);
-  }
-
-#pragma unroll
-  for (int c = 0; c < NCB; ++c) {
-    if (!qvalid[c]) continue;
-    const int qr = c * 16 + lr, p = qr / G, h = qr % G;
-    const int row = it.row0 + p, head = kvh * G + h;
-    if (a.split) {
-      float* po = a.part_o + ((size_t)(split * a.part_rows + row) * a.Hq + head) * HD;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) *(f32x4_t*)(po + d * 16 + 4 * g) = o[d][c];
-      if (g == 0) {
-        float* pml = a.part_ml + ((size_t)(split * a.part_rows + row) * a.Hq + head) * 2;
-        pml[0] = m_run[c];
-        pml[1] = l_run[c];
-      }
-    } else {
-      const float inv = l_run[c] > 0.f ? 1.f / l_run[c] : 0.f;
-      uint16_t* out = (uint16_t*)a.out + (size_t)row * q_stride + (size_t)head * HD;
+      const uint8_t* vrow = st + 8192 + (g >> 1) * 4096 + lr * 32 + (((g & 1) ^ ((lr >> 3) & 1)) * 16);
+      const int nvalid = k_end - (kb + 8 * g);
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
-        uint32_t lo = (uint32_t)from_f<bf16>(o[d][c][0] * inv).u | ((uint32_t)from_f<bf16>(o[d][c][1] * inv).u << 16);
-        uint32_t hi = (uint32_t)from_f<bf16>(o[d][c][2] * inv).u | ((uint32_t)from_f<bf16>(o[d][c][3] * inv).u << 16);
-        *(uint2*)(out + d * 16 + 4 * g) = make_uint2(lo, hi);
+        u32x4_t raw = lds16(vrow + d * 16 * 32);
+        if (tail) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            uint32_t m = 0u;
+            if (2 * w < nvalid) m |= 0x0000ffffu;
+            if (2 * w + 1 < nvalid) m |= 0xffff0000u;
+            raw[w] &= m;
+          }
+        }
+        vf[d] = as_bf16x8(raw);
       }
     }
+    float sv[8];
+    float mx = kNegInf;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = s[b][r] * scale;
+        if (!clean) {
+          const int key = kb + 8 * g + 4 * b + r;
+          if (!(key < k_end && key <= qpos)) v = kNegInf;
+        }
+        sv[4 * b + r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const bool raise = mx > m_run + kRescale;      // also the first visible key of the column
+    const float m_new = raise ? mx : m_run;
+    const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+    uint32_t pk[4];
+    float ps = 0.f;
+    if (m_new == kNegInf) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) pk[w] = 0u;
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        pk[w] = pack_bf16x2(__builtin_amdgcn_exp2f(sv[2 * w] - m_new), __builtin_amdgcn_exp2f(sv[2 * w + 1] - m_new));
+        ps += __uint_as_float(pk[w] << 16) + __uint_as_float(pk[w] & 0xffff0000u);
+      }
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    if (__any(raise)) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) o[d] *= alpha;
+    }
+    const bf16x8_t pf = as_bf16x8((u32x4_t){pk[0], pk[1], pk[2], pk[3]});
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[d] = mfma16x16x32(vf[d], pf, o[d]);
+  };
+
+  // Pipeline: block blk is issued NBUF-1 blocks ahead into ring slot blk % NBUF.  Each wave
+  // waits for its own loads of block blk, then one barrier makes the whole block visible and
+  // also tells that every wave is done with block blk-1, whose slot is refilled next.
+  const int nblk = (k_end - k_begin + 31) >> 5;
+  const int pro = min(NBUF - 1, nblk);
+  {
+    uint8_t* qs = ring + (NBUF - 1) * kBlockBytes + wave * 4096;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      __builtin_amdgcn_global_load_lds((const void*)(qsrc + ks * 32), (lds_void*)(qs + ks * 1024), 16, 0, 0);
+  }
+  for (int blk = 0; blk < pro; ++blk) issue(blk);
+  if (pro >= 3) wait_vmcnt<3 * PW>();                // this wave's Q has landed
+  else if (pro == 2) wait_vmcnt<2 * PW>();
+  else if (pro == 1) wait_vmcnt<PW>();
+  else wait_vmcnt<0>();
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const u32x4_t v = lds16(ring + (NBUF - 1) * kBlockBytes + wave * 4096 + ks * 1024 + 16 * lane);
+    qf[ks] = as_bf16x8(qvalid ? v : zero);
+  }
+  wait_lgkm0();                                      // Q is in registers before its slot is refilled
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int later = min(NBUF - 2, nblk - 1 - blk);  // blocks issued after blk
+    if (later >= 2) wait_vmcnt<2 * PW>();
+    else if (later == 1) wait_vmcnt<PW>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (blk + NBUF - 1 < nblk) issue(blk + NBUF - 1);
+    compute(blk);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  if (!a.split) {
+    if (qvalid) {
+      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+      uint16_t* out = (uint16_t*)a.out + (size_t)(it.row0 + qp) * q_stride + (size_t)(kvh * G + qh) * HD;
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+        *(uint2*)(out + d * 16 + 4 * g) =
+            make_uint2(pack_bf16x2(o[d][0] * inv, o[d][1] * inv), pack_bf16x2(o[d][2] * inv, o[d][3] * inv));
+    }
+    return;
+  }
+
+  if (qvalid) {
+    const int row = it.row0 + qp, head = kvh * G + qh;
+    float* po = a.part_o + ((size_t)(split * a.part_rows + row) * a.Hq + head) * HD;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) *(f32x4_t*)(po + d * 16 + 4 * g) = o[d];
+    if (g == 0) *(float2*)(a.part_ml + ((size_t)(split * a.part_rows + row) * a.Hq + head) * 2) = make_float2(m_run, l_run);
   }
 }
 
-// Combine the split partials of each row in ascending split order (row at position p uses
-// splits 0 .. ceil((p+1)/split)-1).  Dead rows (position -1) are written as zeros.
+// Merge the split partials of each row in ascending split order (the row at position p uses
+// splits 0 .. ceil((p+1)/split)-1); dead rows (position -1) are written as zeros.  Thread t
+// of a row's block handles 16 dims of head t / 8.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int row = blockIdx.x;
   const int pos = a.row_pos[row];
-  uint16_t* out = (uint16_t*)a.out + (size_t)row * a.Hq * HD;
-  const int per_head = HD / 16;                    // threads per head (16 dims each)
-  for (int t = threadIdx.x; t < a.Hq * per_head; t += blockDim.x) {
-    const int head = t / per_head, d0 = (t % per_head) * 16;
-    float acc[16];
+  const size_t stride = (size_t)a.part_rows * a.Hq;          // between splits
+  for (int t = threadIdx.x; t < a.Hq * 8; t += blockDim.x) {
+    const int head = t >> 3, sub = t & 7;
+    f32x4_t acc[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int j = 0; j < 4; ++j) acc[j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    float inv = 0.f;
     if (pos >= 0) {
-      const int ns = (pos + 1 + a.split - 1) / a.split;
+      const int ns = pos / a.split + 1;
+      const size_t e0 = (size_t)row * a.Hq + head;
       float M = kNegInf;
-      for (int s = 0; s < ns; ++s)
-        M = fmaxf(M, a.part_ml[((size_t)(s * a.part_rows + row) * a.Hq + head) * 2]);
+#pragma unroll 4
+      for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, a.part_ml[(e0 + sp * stride) * 2]);
       float L = 0.f;
-      for (int s = 0; s < ns; ++s) {
-        const float* ml = a.part_ml + ((size_t)(s * a.part_rows + row) * a.Hq + head) * 2;
-        const float w = (ml[0] == kNegInf) ? 0.f : exp2f(ml[0] - M);
-        L += w * ml[1];
-        const float* po = a.part_o + ((size_t)(s * a.part_rows + row) * a.Hq + head) * HD + d0;
+#pragma unroll 4
+      for (int sp = 0; sp < ns; ++sp) {
+        const size_t e = e0 + sp * stride;
+        const float2 ml = *(const float2*)(a.part_ml + e * 2);
+        const float w = (ml.x == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+        L += w * ml.y;
+        const f32x4_t* po = (const f32x4_t*)(a.part_o + e * HD + 16 * sub);
 #pragma unroll
-        for (int i = 0; i < 16; i += 4) {
-          const f32x4_t v = *(const f32x4_t*)(po + i);
-          acc[i] += w * v[0];
-          acc[i + 1] += w * v[1];
-          acc[i + 2] += w * v[2];
-          acc[i + 3] += w * v[3];
-        }
+        for (int j = 0; j < 4; ++j) acc[j] += w * po[j];
       }
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] *= inv;
+      inv = L > 0.f ? 1.f / L : 0.f;
     }
-    uint32_t pk[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      pk[i] = (uint32_t)from_f<bf16>(acc[2 * i]).u | ((uint32_t)from_f<bf16>(acc[2 * i + 1]).u << 16);
-    uint4* dst = (uint4*)(out + (size_t)head * HD + d0);
-    dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-    dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+    u32x4_t* out = (u32x4_t*)((uint16_t*)a.out + (size_t)row * a.Hq * HD + (size_t)head * HD + 16 * sub);
+    out[0] = (u32x4_t){pack_bf16x2(acc[0][0] * inv, acc[0][1] * inv), pack_bf16x2(acc[0][2] * inv, acc[0][3] * inv),
+                       pack_bf16x2(acc[1][0] * inv, acc[1][1] * inv), pack_bf16x2(acc[1][2] * inv, acc[1][3] * inv)};
+    out[1] = (u32x4_t){pack_bf16x2(acc[2][0] * inv, acc[2][1] * inv), pack_bf16x2(acc[2][2] * inv, acc[2][3] * inv),
+                       pack_bf16x2(acc[3][0] * inv, acc[3][1] * inv), pack_bf16x2(acc[3][2] * inv, acc[3][3] * inv)};
   }
 }
 
@@ -316,6 +380,8 @@ __global__ void attn_setup_kernel(AttnItem* items, int32_t* row_pos, int32_t* ro
 
 }  // namespace
 
+int attn_split_len(int batch) { return batch <= 16 ? 128 : batch <= 32 ? 256 : 512; }
+
 hipError_t launch_attn_setup(AttnItem* items, int32_t* row_pos, int32_t* row_slot, const int32_t* ctx_len,
                              const int32_t* q_len, int batch, int rows, hipStream_t s) {
   hipLaunchKernelGGL(attn_setup_kernel, dim3((batch + 63) / 64), dim3(64), 0, s, items, row_pos, row_slot, ctx_len,
@@ -326,11 +392,12 @@ hipError_t launch_attn_setup(AttnItem* items, int32_t* row_pos, int32_t* row_slo
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.hd != HD || a.P != 16) return hipErrorInvalidValue;
   if (a.n_items <= 0) return hipSuccess;
+  if (a.split && a.split % 32) return hipErrorInvalidValue;
   dim3 grid(a.n_items, a.Hkv, a.split ? a.max_splits : 1);
   if (a.ncb == 2) {
-    hipLaunchKernelGGL(attn_bf16_kernel<2>, grid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<2, kAttnBufs>), grid, dim3(128), 0, s, a);
   } else if (a.ncb == 4) {
-    hipLaunchKernelGGL(attn_bf16_kernel<4>, grid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<4, kAttnBufs>), grid, dim3(256), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }

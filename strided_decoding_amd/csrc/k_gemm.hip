@@ -58,15 +58,6 @@ __device__ __forceinline__ void epilogue_store_t(const GemmArgs& a, int row, int
   }
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 // D = A * B + C for one 32x32x16 bf16 tile: lane l holds A row (l%32) and B column (l%32)

@@ -173,3 +173,13 @@ def test_small_bf16_end_to_end():
     prompts = I.ragged_prompts([40, 7, 130, 19], shape.vocab, seed=3)
     teacher_forced(shape, w, 4, 1.0, "sample", prompts, [12, 20, 8, 16], steps=14, logits_tol=2e-2, rel=True,
                    on_gpu_logits=True)
+
+
+def test_small_bf16_long_prompt():
+    """A prompt longer than 1024 tokens: prefill attention spans more than one 64-page window of
+    page ids, and decode passes merge many context splits."""
+    shape = I.SMALL_BF16
+    w = I.weights_numpy(shape, seed=0, scale=20.0)
+    prompts = I.ragged_prompts([1300, 90], shape.vocab, seed=8)
+    teacher_forced(shape, w, 4, 1.0, "sample", prompts, [6, 6], steps=4, logits_tol=2e-2, rel=True,
+                   on_gpu_logits=True)
