@@ -39,6 +39,7 @@ def parse():
     p.add_argument("--gen", type=int, default=1024)
     p.add_argument("--profile-steps", type=int, default=6)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graphs", action="store_true", help="launch every pass eagerly (no HIP graph replay)")
     p.add_argument("--out", default=None, help="also write the JSON line to this file")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB (counter calibration) and exit")
@@ -326,20 +327,19 @@ def main():
         log(f"prefilled slots {sl[0]}..{sl[-1]}")
     log(f"prefill {B}x{args.prompt_len} in {time.perf_counter() - t0:.1f}s")
 
+    eng.set_graphs(not args.no_graphs)
     for _ in range(args.warmup):
         eng.step()
     torch.cuda.synchronize()
     st0 = eng.slots_host()
-    tot = torch.zeros((), dtype=torch.int64, device=dev)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        _, nc, _ = eng.step()
-        tot += nc.sum()
+        eng.step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    committed = int(tot.item())
     st1 = eng.slots_host()
+    committed = sum(s1["committed"] - s0["committed"] for s0, s1 in zip(st0, st1))
     passes = sum(s1["passes"] - s0["passes"] for s0, s1 in zip(st0, st1))
     verified = sum(s1["verified"] - s0["verified"] for s0, s1 in zip(st0, st1))
     accepted = sum(s1["accepted"] - s0["accepted"] for s0, s1 in zip(st0, st1))
@@ -392,7 +392,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (random-init weights N(0,0.02), uniformly random prompt ids)",
         "config": {"workload": wl.name, "batch": B, "stride": N, "prompt_len": args.prompt_len,
-                   "max_new": args.gen, "propose": wl.propose, "temperature": T, "parallelism": "single GPU"},
+                   "max_new": args.gen, "propose": wl.propose, "temperature": T, "parallelism": "single GPU",
+                   "hip_graphs": not args.no_graphs},
         "isd_steps_per_s": args.steps / elapsed,
         "tokens_per_forward": committed / max(1, passes),
         "acceptance": accepted / max(1, verified),

@@ -20,7 +20,7 @@ ISD_SLOT_EMPTY, ISD_SLOT_A, ISD_SLOT_B, ISD_SLOT_DONE = 0, 1, 2, 3
 # symbols the header declares (checked by the CPU test-suite)
 EXPORTS = ("isd_init", "isd_prefill", "isd_step", "isd_get_buffers", "isd_get_status", "isd_release",
            "isd_attn_workspace_bytes", "isd_attn_paged", "isd_sample_workspace_bytes", "isd_sample",
-           "isd_version", "isd_profile", "isd_profile_report", "isd_gemm", "isd_gemm_splits")
+           "isd_version", "isd_profile", "isd_profile_report", "isd_gemm", "isd_gemm_splits", "isd_set_graphs")
 
 ISD_GEMM_STORE, ISD_GEMM_STORE_F32, ISD_GEMM_RESID, ISD_GEMM_SWIGLU = 0, 1, 2, 3
 
@@ -124,9 +124,10 @@ def load(path=LIB_PATH):
     lib.isd_gemm_splits.argtypes = [C.c_int32, C.c_int32, C.c_int32]
     lib.isd_gemm_splits.restype = C.c_int32
     lib.isd_profile.argtypes = [C.c_void_p, C.c_int32]
+    lib.isd_set_graphs.argtypes = [C.c_void_p, C.c_int32]
     lib.isd_profile_report.argtypes = [C.c_void_p, C.POINTER(ProfEntry), C.c_int32, C.POINTER(C.c_int32)]
     for f in ("isd_init", "isd_prefill", "isd_step", "isd_get_buffers", "isd_get_status", "isd_release",
-              "isd_attn_paged", "isd_sample", "isd_profile", "isd_profile_report"):
+              "isd_attn_paged", "isd_sample", "isd_profile", "isd_profile_report", "isd_set_graphs"):
         getattr(lib, f).restype = C.c_int
     _lib = lib
     return lib

@@ -80,6 +80,14 @@ struct isd_ctx {
   std::vector<hipEvent_t> ev_pool;
   std::vector<std::pair<const char*, int>> prof_recs;
   int ev_used = 0;
+  // graph replay of isd_step (isd_set_graphs): one executable graph per logits-buffer parity,
+  // valid for the output pointers it was captured with
+  bool graphs = false;
+  hipStream_t cap_stream = nullptr;
+  struct StepGraph {
+    hipGraphExec_t exec = nullptr;
+    const void *tokens = nullptr, *n_commit = nullptr, *n_accept = nullptr;
+  } step_graph[2];
 };
 
 namespace {
@@ -593,18 +601,18 @@ isd_status isd_prefill(isd_ctx* x, int32_t n, const int32_t* slots, const int32_
   return ISD_OK;
 }
 
-isd_status isd_step(isd_ctx* x, int32_t* tokens, int32_t* n_commit, int32_t* n_accept, void* stream) {
-  if (!x || !tokens || !n_commit || !n_accept) return ISD_E_ARG;
-  if (!x->prefilled) return ISD_E_STATE;
+namespace {
+
+// The launches of one decode pass on stream s, reading logits buffer parity cur.
+isd_status step_launches(isd_ctx* x, int32_t* tokens, int32_t* n_commit, int32_t* n_accept, int cur, hipStream_t s) {
   const isd_config& c = x->cfg;
-  hipStream_t s = (hipStream_t)stream;
   StepMeta m = meta(*x);
   TIMEDP("assemble", launch_assemble(m, s));
   const int M = x->max_dec_rows;
   isd_status st = forward(*x, M, c.max_batch * x->items_per_slot, /*decode=*/true, nullptr, M,
                           /*lora=*/c.lora_rank > 0 && c.stride_n > 1, s);
   if (st != ISD_OK) return st;
-  const int cur = x->cur, prev = cur ^ 1;
+  const int prev = cur ^ 1;
   TIMEDP("row_stats", launch_row_stats(x->logits[cur], M, c.vocab, c.temperature, x->stats[cur], s));
   SampleArgs a = sargs(*x);
   a.n_slots = c.max_batch;
@@ -619,7 +627,63 @@ isd_status isd_step(isd_ctx* x, int32_t* tokens, int32_t* n_commit, int32_t* n_a
   a.n_accept = n_accept;
   TIMEDP("decide", launch_decide(a, s));
   TIMEDP("truncate", launch_truncate(m, nullptr, c.max_batch, s));
-  x->cur = prev;
+  return ISD_OK;
+}
+
+void drop_graphs(isd_ctx* x) {
+  for (auto& g : x->step_graph) {
+    if (g.exec) hipGraphExecDestroy(g.exec);
+    g = isd_ctx::StepGraph{};
+  }
+}
+
+}  // namespace
+
+isd_status isd_step(isd_ctx* x, int32_t* tokens, int32_t* n_commit, int32_t* n_accept, void* stream) {
+  if (!x || !tokens || !n_commit || !n_accept) return ISD_E_ARG;
+  if (!x->prefilled) return ISD_E_STATE;
+  hipStream_t s = (hipStream_t)stream;
+  const int cur = x->cur;
+  if (x->graphs && !x->prof_on) {
+    isd_ctx::StepGraph& g = x->step_graph[cur];
+    if (g.exec && (g.tokens != tokens || g.n_commit != n_commit || g.n_accept != n_accept)) {
+      hipGraphExecDestroy(g.exec);
+      g = isd_ctx::StepGraph{};
+    }
+    if (!g.exec) {
+      hipGraph_t graph = nullptr;
+      HIP_OK(hipStreamBeginCapture(x->cap_stream, hipStreamCaptureModeRelaxed));
+      const isd_status st = step_launches(x, tokens, n_commit, n_accept, cur, x->cap_stream);
+      const hipError_t e = hipStreamEndCapture(x->cap_stream, &graph);
+      if (st != ISD_OK) {
+        if (graph) hipGraphDestroy(graph);
+        return st;
+      }
+      if (e != hipSuccess || !graph) return ISD_E_HIP;
+      const hipError_t ei = hipGraphInstantiate(&g.exec, graph, nullptr, nullptr, 0);
+      hipGraphDestroy(graph);
+      if (ei != hipSuccess) {
+        g.exec = nullptr;
+        return ISD_E_HIP;
+      }
+      g.tokens = tokens;
+      g.n_commit = n_commit;
+      g.n_accept = n_accept;
+    }
+    HIP_OK(hipGraphLaunch(g.exec, s));
+  } else {
+    const isd_status st = step_launches(x, tokens, n_commit, n_accept, cur, s);
+    if (st != ISD_OK) return st;
+  }
+  x->cur = cur ^ 1;
+  return ISD_OK;
+}
+
+isd_status isd_set_graphs(isd_ctx* x, int32_t enable) {
+  if (!x) return ISD_E_ARG;
+  if (enable && !x->cap_stream) HIP_OK(hipStreamCreateWithFlags(&x->cap_stream, hipStreamNonBlocking));
+  if (!enable) drop_graphs(x);
+  x->graphs = enable != 0;
   return ISD_OK;
 }
 
@@ -654,6 +718,8 @@ isd_status isd_get_status(isd_ctx* x, void* stream) {
 isd_status isd_release(isd_ctx* x) {
   if (!x) return ISD_E_ARG;
   for (hipEvent_t e : x->ev_pool) hipEventDestroy(e);
+  drop_graphs(x);
+  if (x->cap_stream) hipStreamDestroy(x->cap_stream);
   delete x;
   return ISD_OK;
 }

@@ -135,6 +135,10 @@ class Engine:
     def profile(self, enable):
         A.check("isd_profile", self.lib.isd_profile(self.ctx, 1 if enable else 0))
 
+    def set_graphs(self, enable):
+        """Replay isd_step from captured HIP graphs (see isd_set_graphs)."""
+        A.check("isd_set_graphs", self.lib.isd_set_graphs(self.ctx, 1 if enable else 0))
+
     def profile_report(self):
         """{kernel name: (launches, total milliseconds)} since the last report (synchronizes)."""
         cap = 64
