@@ -68,11 +68,11 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_
 }
 
 template <int EPI, bool PARTIAL>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S,
-                                                                float* part) {
+__global__ __launch_bounds__(512) void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU);
   constexpr int TNO = DUAL ? TN2 / 2 : TN2;
   constexpr int AG = TM2 / 16;                    // 14 A row groups of 16 rows
+  constexpr int NG = (TM2 + TN2) / 16;            // 30 row groups per stage
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE_BYTES];
 
   const int id = blockIdx.x;
@@ -86,64 +86,58 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs a, int n
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = nt * TNO, m0 = mt * TM2;
 
-  // Loader: wave w fills A groups w, w+4, w+8, (w+12) and B groups w, w+4, w+8, w+12.
-  // Lane l writes LDS bytes [16 l, 16 l + 16) of its group: row l/4, slot l%4, which holds
-  // k-chunk (l%4) ^ ((row/4)%4) of that row.  For SwiGLU the B tile alternates 32-row
-  // blocks of the gate and up matrices, so each wave multiplies one gate block and the up
-  // block of the same 32 output columns.
+  // Loader: wave w fills row groups w, w+8, w+16, w+24 of the 30 (A groups 0..13, then the B
+  // groups).  Lane l writes LDS bytes [16 l, 16 l + 16) of its group: row l/4, slot l%4,
+  // which holds k-chunk (l%4) ^ ((row/4)%4) of that row.  B block t (rows 32t .. 32t+31 of
+  // the tile) is wave t's operand; for SwiGLU the blocks alternate gate and up rows of the
+  // same 32 output columns (block t: matrix t%2, outputs 32 (t/2) ..).
   const int lrow = lane >> 2;
   const int chunk = (lane & 3) ^ ((lrow >> 2) & 3);
-  const uint16_t* asrc[4];
-  const uint16_t* bsrc[4];
+  const uint16_t* src[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int g = wave + 4 * i;
-    const int m = m0 + g * 16 + lrow;
-    int srow = 0;
-    if (g < AG && m < a.M) {
-      srow = a.a_rows ? a.a_rows[m] : m;
-      if (srow < 0) srow = 0;          // unused row (its outputs are never consumed)
-    }
-    asrc[i] = (const uint16_t*)a.A + (size_t)srow * a.lda + kbase + chunk * 8;
-    const uint16_t* bm = (const uint16_t*)a.B0;
-    int n;
-    if (DUAL) {
-      const int blk = g >> 1;
-      if (blk & 1) bm = (const uint16_t*)a.B1;
-      n = n0 + (blk >> 1) * 32 + (g & 1) * 16 + lrow;
+    const int g = wave + 8 * i;
+    if (g < AG) {
+      const int m = m0 + g * 16 + lrow;
+      int srow = 0;
+      if (m < a.M) {
+        srow = a.a_rows ? a.a_rows[m] : m;
+        if (srow < 0) srow = 0;          // unused row (its outputs are never consumed)
+      }
+      src[i] = (const uint16_t*)a.A + (size_t)srow * a.lda + kbase + chunk * 8;
     } else {
-      n = n0 + g * 16 + lrow;
+      const int bg = min(g, NG - 1) - AG;         // B row group 0..15
+      const uint16_t* bm = (const uint16_t*)a.B0;
+      int n;
+      if (DUAL) {
+        const int blk = bg >> 1;
+        if (blk & 1) bm = (const uint16_t*)a.B1;
+        n = n0 + (blk >> 1) * 32 + (bg & 1) * 16 + lrow;
+      } else {
+        n = n0 + bg * 16 + lrow;
+      }
+      n = min(n, a.N - 1);
+      src[i] = bm + (size_t)n * a.ldb + kbase + chunk * 8;
     }
-    n = min(n, a.N - 1);
-    bsrc[i] = bm + (size_t)n * a.ldb + kbase + chunk * 8;
   }
-  const int na = (wave + 12 < AG) ? 4 : 3;       // A groups of this wave
+  const int ng = (wave + 24 < NG) ? 4 : 3;        // groups of this wave
 
   auto issue = [&](int kt) {
     uint8_t* st = smem + (kt % NST) * STAGE_BYTES;
     const int koff = kt * BK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (i < na)
-        __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + koff), (lds_void*)(st + (wave + 4 * i) * GROUP_BYTES),
-                                         16, 0, 0);
-    }
-#pragma unroll
     for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + koff),
-                                       (lds_void*)(st + (AG + wave + 4 * i) * GROUP_BYTES), 16, 0, 0);
+      if (i < ng)
+        __builtin_amdgcn_global_load_lds((const void*)(src[i] + koff), (lds_void*)(st + (wave + 8 * i) * GROUP_BYTES),
+                                         16, 0, 0);
   };
 
-  f32x16_t acc[7][2];
+  f32x16_t acc[7];
 #pragma unroll
   for (int i = 0; i < 7; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-  // Stage s lives in ring buffer s % NST.  Loads run NST-1 stages ahead; the MFMA operands
-  // of stage kt+1 are read from LDS into registers while the MFMAs of stage kt execute.
   for (int s = 0; s < NST - 1; ++s)
     if (s < kt_per) issue(s);
 
@@ -151,86 +145,156 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs a, int n
   const int rig = lane & 15, half = (lane >> 4) & 1, khi = lane >> 5;
   const int rd0 = rig * (BK * 2) + half * GROUP_BYTES;
   const int sw = (rig >> 2) & 3;
-  auto wait_stage = [&](int later) {      // later = stages issued after the awaited one
-    if (later >= 3) wait_vmcnt<21>();
-    else if (later == 2) wait_vmcnt<14>();
-    else if (later == 1) wait_vmcnt<7>();
-    else wait_vmcnt<0>();
-  };
-  auto read_frags = [&](int kt, bf16x8_t (*af)[7], bf16x8_t (*bfr)[2]) {
-    const uint8_t* st = smem + (kt % NST) * STAGE_BYTES;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int off = rd0 + (((2 * kk + khi) ^ sw) * 16);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfr[kk][j] = as_bf16x8(*(const u32x4_t*)(st + (AG + 4 * wave + 2 * j) * GROUP_BYTES + off));
-#pragma unroll
-      for (int i = 0; i < 7; ++i) af[kk][i] = as_bf16x8(*(const u32x4_t*)(st + (2 * i) * GROUP_BYTES + off));
+  // waits: every wave has issued ng loads per stage (3 or 4); allow the later stages' loads
+  auto wait_stage = [&](int later) {
+    if (ng == 4) {
+      if (later >= 3) wait_vmcnt<12>();
+      else if (later == 2) wait_vmcnt<8>();
+      else if (later == 1) wait_vmcnt<4>();
+      else wait_vmcnt<0>();
+    } else {
+      if (later >= 3) wait_vmcnt<9>();
+      else if (later == 2) wait_vmcnt<6>();
+      else if (later == 1) wait_vmcnt<3>();
+      else wait_vmcnt<0>();
     }
   };
+  // frags of k-step kk of stage kt: 7 A blocks and this wave's B block
+  auto read_frags = [&](int kt, int kk, bf16x8_t* af, bf16x8_t& bf) {
+    const uint8_t* st = smem + (kt % NST) * STAGE_BYTES;
+    const int off = rd0 + (((2 * kk + khi) ^ sw) * 16);
+    bf = as_bf16x8(*(const u32x4_t*)(st + (AG + 2 * wave) * GROUP_BYTES + off));
+#pragma unroll
+    for (int i = 0; i < 7; ++i) af[i] = as_bf16x8(*(const u32x4_t*)(st + (2 * i) * GROUP_BYTES + off));
+  };
 
-  bf16x8_t af[2][7], bfr[2][2];
+  bf16x8_t a0[7], a1[7], b0, b1;
   wait_stage(min(NST - 2, kt_per - 1));
   __builtin_amdgcn_s_barrier();
-  read_frags(0, af, bfr);
-  // One pipeline step: make stage kt+1 visible, refill the ring, read stage kt+1's operands,
-  // multiply stage kt's.  Ring buffer (kt+NST-1) % NST held stage kt-1, whose operands every
-  // wave consumed before this step's barrier.
+  read_frags(0, 0, a0, b0);
+  // One pipeline step: make stage kt+1 visible, refill the ring, then multiply stage kt's
+  // k-step 0 while reading its k-step 1, and its k-step 1 while reading stage kt+1's k-step 0.
+  // Ring buffer (kt+NST-1) % NST held stage kt-1, which every wave finished before this
+  // step's barrier.
   for (int kt = 0; kt < kt_per; ++kt) {
-    // stages kt+2 .. kt+NST-2 may stay in flight (the last step re-reads stage kt)
     wait_stage(kt + 1 < kt_per ? min(NST - 3, kt_per - 2 - kt) : 0);
     __builtin_amdgcn_s_barrier();        // no fence: the later stages' loads stay in flight
     if (kt + NST - 1 < kt_per) issue(kt + NST - 1);
-    bf16x8_t naf[2][7], nbfr[2][2];
-    read_frags(kt + 1 < kt_per ? kt + 1 : kt, naf, nbfr);
+    read_frags(kt, 1, a1, b1);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int i = 0; i < 7; ++i) acc[i] = mfma32x32x16(a0[i], b0, acc[i]);
 #pragma unroll
-      for (int i = 0; i < 7; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(af[kk][i], bfr[kk][j], acc[i][j]);
-    // interleave the 18 operand reads of the next stage with this stage's 28 MFMAs
-#pragma unroll
-    for (int g = 0; g < 18; ++g) {
+    for (int g = 0; g < 7; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    read_frags(kt + 1 < kt_per ? kt + 1 : kt, 0, a0, b0);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int i = 0; i < 7; ++i) acc[i] = mfma32x32x16(a1[i], b1, acc[i]);
 #pragma unroll
-      for (int i = 0; i < 7; ++i) af[kk][i] = naf[kk][i];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) bfr[kk][j] = nbfr[kk][j];
+    for (int g = 0; g < 7; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
 
+  // Epilogue through LDS: each wave's 224 x 32 fp32 tile is staged row-major (rows padded to
+  // 36 floats) in two halves (blocks 0-3, then 4-6), then written out in 16-byte row chunks.
+  // Accumulator register r of block i in lane l is tile row 32 i + 8 (r/4) + 4 (l/32) + r%4,
+  // column l%32.
+  __syncthreads();                                 // every wave is done with the ring
+  constexpr int LD = 36;
+  float* tile = (float*)smem + (size_t)wave * (128 * LD);
+  const int cl = lane & 31;
+  const int wcol = DUAL ? n0 + 32 * (wave >> 1) : n0 + 32 * wave;   // first output column of this wave
 #pragma unroll
-  for (int i = 0; i < 7; ++i) {
+  for (int h = 0; h < 2; ++h) {
+    const int i0 = 4 * h, nb = h ? 3 : 4, r0 = m0 + 128 * h;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = m0 + 32 * i + 8 * (r >> 2) + 4 * khi + (r & 3);
-      if (row >= a.M) continue;
-      if (DUAL) {
-        const int col = n0 + 32 * wave + (lane & 31);
-        if (PARTIAL) {
-          if (col < a.N) {
-            float* pr = part + ((size_t)sp * a.M + row) * (2 * (size_t)a.N);
-            pr[col] = acc[i][0][r];
-            pr[a.N + col] = acc[i][1][r];
+    for (int i = 0; i < 4; ++i) {
+      if (i >= nb) break;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tile[(32 * i + 8 * (r >> 2) + 4 * khi + (r & 3)) * LD + cl] = acc[i0 + i][r];
+    }
+    if (DUAL && !PARTIAL) {
+      __syncthreads();                             // the partner wave's tile is staged too
+      // pair p = wave/2: gate tile in wave 2p, up tile in wave 2p+1; the two waves split the rows
+      const float* gt = (const float*)smem + (size_t)(wave & ~1) * (128 * LD);
+      const float* ut = gt + 128 * LD;
+      const int rows_h = nb * 32, rbeg = (wave & 1) * (rows_h / 2);
+      for (int q = lane; q < (rows_h / 2) * 4; q += 64) {
+        const int tr = rbeg + (q >> 2), c8 = (q & 3) * 8, row = r0 + tr, col = wcol + c8;
+        if (row >= a.M || col >= a.N) continue;
+        float g[8], u[8];
+        *(f32x4_t*)&g[0] = *(const f32x4_t*)&gt[tr * LD + c8];
+        *(f32x4_t*)&g[4] = *(const f32x4_t*)&gt[tr * LD + c8 + 4];
+        *(f32x4_t*)&u[0] = *(const f32x4_t*)&ut[tr * LD + c8];
+        *(f32x4_t*)&u[4] = *(const f32x4_t*)&ut[tr * LD + c8 + 4];
+        const int dr = a.delta_row ? a.delta_row[row] : -1;
+        uint32_t pk[4];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          float v0 = g[j], v1 = g[j + 1], w0 = u[j], w1 = u[j + 1];
+          if (dr >= 0) {
+            const float* dl = a.delta + (size_t)dr * a.ldd + col + j;
+            v0 += dl[0];
+            v1 += dl[1];
+            w0 += dl[a.delta_off2];
+            w1 += dl[a.delta_off2 + 1];
           }
-        } else {
-          epilogue_store_t<bf16, EPI>(a, row, col, acc[i][0][r], acc[i][1][r]);
+          pk[j >> 1] = pack_bf16x2(v0 / (1.0f + expf(-v0)) * w0, v1 / (1.0f + expf(-v1)) * w1);
         }
-      } else {
+        uint16_t* dst = (uint16_t*)a.C + (size_t)row * a.ldc + col;
+        if (col + 8 <= a.N) {
+          *(u32x4_t*)dst = (u32x4_t){pk[0], pk[1], pk[2], pk[3]};
+        } else {
+          for (int j = 0; j < 8 && col + j < a.N; ++j) dst[j] = (uint16_t)(pk[j >> 1] >> (16 * (j & 1)));
+        }
+      }
+      __syncthreads();                             // both tiles are read before the next half
+    } else if (!PARTIAL && EPI == EPI_STORE) {
+      for (int q = lane; q < nb * 32 * 4; q += 64) {
+        const int tr = q >> 2, c8 = (q & 3) * 8, row = r0 + tr, col = wcol + c8;
+        if (row >= a.M || col >= a.N) continue;
+        float v[8];
+        *(f32x4_t*)&v[0] = *(const f32x4_t*)&tile[tr * LD + c8];
+        *(f32x4_t*)&v[4] = *(const f32x4_t*)&tile[tr * LD + c8 + 4];
+        const int dr = a.delta_row ? a.delta_row[row] : -1;
+        if (dr >= 0) {
+          const float* dl = a.delta + (size_t)dr * a.ldd + col;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = n0 + 64 * wave + 32 * j + (lane & 31);
-          if (PARTIAL) {
-            if (col < a.N) part[((size_t)sp * a.M + row) * (size_t)a.N + col] = acc[i][j][r];
+          for (int j = 0; j < 8; ++j) v[j] += dl[j];
+        }
+        uint32_t pk[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pk[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+        uint16_t* dst = (uint16_t*)a.C + (size_t)row * a.ldc + col;
+        if (col + 8 <= a.N) {
+          *(u32x4_t*)dst = (u32x4_t){pk[0], pk[1], pk[2], pk[3]};
+        } else {
+          for (int j = 0; j < 8 && col + j < a.N; ++j) dst[j] = (uint16_t)(pk[j >> 1] >> (16 * (j & 1)));
+        }
+      }
+    } else {
+      // fp32 outputs: split-K partials (raw sums), fp32 store or residual add (with delta)
+      for (int q = lane; q < nb * 32 * 8; q += 64) {
+        const int tr = q >> 3, c4 = (q & 7) * 4, row = r0 + tr, col = wcol + c4;
+        if (row >= a.M || col >= a.N) continue;
+        f32x4_t v = *(const f32x4_t*)&tile[tr * LD + c4];
+        if (PARTIAL) {
+          float* dst = DUAL ? part + ((size_t)sp * a.M + row) * (2 * (size_t)a.N) + (wave & 1) * a.N + col
+                            : part + ((size_t)sp * a.M + row) * (size_t)a.N + col;
+          *(f32x4_t*)dst = v;
+        } else {
+          const int dr = a.delta_row ? a.delta_row[row] : -1;
+          if (dr >= 0) v += *(const f32x4_t*)(a.delta + (size_t)dr * a.ldd + col);
+          if (EPI == EPI_RESID) {
+            f32x4_t* dst = (f32x4_t*)(a.R + (size_t)row * a.ldr + col);
+            *dst = *dst + v;
           } else {
-            epilogue_store_t<bf16, EPI>(a, row, col, acc[i][j][r], 0.f);
+            *(f32x4_t*)((float*)a.C + (size_t)row * a.ldc + col) = v;
           }
         }
       }
@@ -529,9 +593,9 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
   const int units = n_nt * S;
   dim3 grid(((units + 7) / 8) * 8 * n_mt);
   if (S > 1)
-    hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, true>), grid, dim3(256), 0, s, a, n_mt, units, S, a.part);
+    hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, true>), grid, dim3(512), 0, s, a, n_mt, units, S, a.part);
   else
-    hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, false>), grid, dim3(256), 0, s, a, n_mt, units, 1, nullptr);
+    hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, false>), grid, dim3(512), 0, s, a, n_mt, units, 1, nullptr);
   return finish<EPI>(a, S, s);
 }
 
