@@ -86,8 +86,9 @@ __global__ __launch_bounds__(512) void gemm_bf16_big_kernel(GemmArgs a, int n_mt
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = nt * TNO, m0 = mt * TM2;
 
-  // Loader: wave w fills row groups w, w+8, w+16, w+24 of the 30 (A groups 0..13, then the B
-  // groups).  Lane l writes LDS bytes [16 l, 16 l + 16) of its group: row l/4, slot l%4,
+  // Loader: wave w fills row groups w, w+8, w+16, min(w+24, 29) of the 30 (A groups 0..13,
+  // then the B groups; waves 6 and 7 both refill group 29 with the same bytes, so every wave
+  // issues 4 loads per stage).  Lane l writes LDS bytes [16 l, 16 l + 16) of its group: row l/4, slot l%4,
   // which holds k-chunk (l%4) ^ ((row/4)%4) of that row.  B block t (rows 32t .. 32t+31 of
   // the tile) is wave t's operand; for SwiGLU the blocks alternate gate and up rows of the
   // same 32 output columns (block t: matrix t%2, outputs 32 (t/2) ..).
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_big_kernel(GemmArgs a, int n_mt
   const uint16_t* src[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int g = wave + 8 * i;
+    const int g = min(wave + 8 * i, NG - 1);
     if (g < AG) {
       const int m = m0 + g * 16 + lrow;
       int srow = 0;
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_big_kernel(GemmArgs a, int n_mt
       }
       src[i] = (const uint16_t*)a.A + (size_t)srow * a.lda + kbase + chunk * 8;
     } else {
-      const int bg = min(g, NG - 1) - AG;         // B row group 0..15
+      const int bg = g - AG;                      // B row group 0..15
       const uint16_t* bm = (const uint16_t*)a.B0;
       int n;
       if (DUAL) {
@@ -120,16 +121,16 @@ __global__ __launch_bounds__(512) void gemm_bf16_big_kernel(GemmArgs a, int n_mt
       src[i] = bm + (size_t)n * a.ldb + kbase + chunk * 8;
     }
   }
-  const int ng = (wave + 24 < NG) ? 4 : 3;        // groups of this wave
-
-  auto issue = [&](int kt) {
-    uint8_t* st = smem + (kt % NST) * STAGE_BYTES;
+  // Stage kt goes to ring slot kt % NST.  Every step issues exactly one stage (past the last
+  // stage it re-loads the last one into the slot just freed, which is never read again), so
+  // the number of loads in flight is the same at every wait.
+  auto issue = [&](int kt, int slot) {
+    uint8_t* st = smem + slot * STAGE_BYTES;
     const int koff = kt * BK;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (i < ng)
-        __builtin_amdgcn_global_load_lds((const void*)(src[i] + koff), (lds_void*)(st + (wave + 8 * i) * GROUP_BYTES),
-                                         16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + koff),
+                                       (lds_void*)(st + min(wave + 8 * i, NG - 1) * GROUP_BYTES), 16, 0, 0);
   };
 
   f32x16_t acc[7];
@@ -138,27 +139,12 @@ __global__ __launch_bounds__(512) void gemm_bf16_big_kernel(GemmArgs a, int n_mt
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-  for (int s = 0; s < NST - 1; ++s)
-    if (s < kt_per) issue(s);
+  for (int s = 0; s < NST - 1; ++s) issue(min(s, kt_per - 1), s);
 
   // operand read: row (lane%32) of a 32-row block, k-chunk 2 kk + lane/32 (swizzled)
   const int rig = lane & 15, half = (lane >> 4) & 1, khi = lane >> 5;
   const int rd0 = rig * (BK * 2) + half * GROUP_BYTES;
   const int sw = (rig >> 2) & 3;
-  // waits: every wave has issued ng loads per stage (3 or 4); allow the later stages' loads
-  auto wait_stage = [&](int later) {
-    if (ng == 4) {
-      if (later >= 3) wait_vmcnt<12>();
-      else if (later == 2) wait_vmcnt<8>();
-      else if (later == 1) wait_vmcnt<4>();
-      else wait_vmcnt<0>();
-    } else {
-      if (later >= 3) wait_vmcnt<9>();
-      else if (later == 2) wait_vmcnt<6>();
-      else if (later == 1) wait_vmcnt<3>();
-      else wait_vmcnt<0>();
-    }
-  };
   // frags of k-step kk of stage kt: 7 A blocks and this wave's B block
   auto read_frags = [&](int kt, int kk, bf16x8_t* af, bf16x8_t& bf) {
     const uint8_t* st = smem + (kt % NST) * STAGE_BYTES;
@@ -169,36 +155,45 @@ __global__ __launch_bounds__(512) void gemm_bf16_big_kernel(GemmArgs a, int n_mt
   };
 
   bf16x8_t a0[7], a1[7], b0, b1;
-  wait_stage(min(NST - 2, kt_per - 1));
+  wait_vmcnt<4 * (NST - 2)>();                     // stage 0 has landed
   __builtin_amdgcn_s_barrier();
   read_frags(0, 0, a0, b0);
-  // One pipeline step: make stage kt+1 visible, refill the ring, then multiply stage kt's
-  // k-step 0 while reading its k-step 1, and its k-step 1 while reading stage kt+1's k-step 0.
-  // Ring buffer (kt+NST-1) % NST held stage kt-1, which every wave finished before this
-  // step's barrier.
+  // One pipeline step: make stage kt+1 visible (stages kt+2 .. kt+NST-2 stay in flight), then
+  // multiply stage kt's k-step 0 while reading its k-step 1, refill the slot of stage kt-1
+  // (every wave finished it before the barrier) and multiply k-step 1 while reading stage
+  // kt+1's k-step 0.  The loads are interleaved with the MFMAs so that a stalled load issue
+  // does not leave the matrix unit idle.
   for (int kt = 0; kt < kt_per; ++kt) {
-    wait_stage(kt + 1 < kt_per ? min(NST - 3, kt_per - 2 - kt) : 0);
+    wait_vmcnt<4 * (NST - 3)>();
     __builtin_amdgcn_s_barrier();        // no fence: the later stages' loads stay in flight
-    if (kt + NST - 1 < kt_per) issue(kt + NST - 1);
-    read_frags(kt, 1, a1, b1);
+    {
+      const uint8_t* st = smem + (kt % NST) * STAGE_BYTES;
+      const int off = rd0 + (((2 + khi) ^ sw) * 16);                   // k-step 1 of stage kt
+      uint8_t* dst = smem + ((kt + NST - 1) % NST) * STAGE_BYTES;
+      const int koff = min(kt + NST - 1, kt_per - 1) * BK;
 #pragma unroll
-    for (int i = 0; i < 7; ++i) acc[i] = mfma32x32x16(a0[i], b0, acc[i]);
+      for (int i = 0; i < 7; ++i) {
+        acc[i] = mfma32x32x16(a0[i], b0, acc[i]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i == 0) b1 = as_bf16x8(*(const u32x4_t*)(st + (AG + 2 * wave) * GROUP_BYTES + off));
+        a1[i] = as_bf16x8(*(const u32x4_t*)(st + (2 * i) * GROUP_BYTES + off));
+        if (i < 4)
+          __builtin_amdgcn_global_load_lds((const void*)(src[i] + koff),
+                                           (lds_void*)(dst + min(wave + 8 * i, NG - 1) * GROUP_BYTES), 16, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    read_frags(kt + 1 < kt_per ? kt + 1 : kt, 0, a0, b0);
+#pragma unroll
+    for (int i = 0; i < 7; ++i) acc[i] = mfma32x32x16(a1[i], b1, acc[i]);
 #pragma unroll
     for (int g = 0; g < 7; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    read_frags(kt + 1 < kt_per ? kt + 1 : kt, 0, a0, b0);
-#pragma unroll
-    for (int i = 0; i < 7; ++i) acc[i] = mfma32x32x16(a1[i], b1, acc[i]);
-#pragma unroll
-    for (int g = 0; g < 7; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
+  wait_vmcnt<0>();                                 // the re-loads past the last stage
 
   // Epilogue through LDS: each wave's 224 x 32 fp32 tile is staged row-major (rows padded to
   // 36 floats) in two halves (blocks 0-3, then 4-6), then written out in 16-byte row chunks.
