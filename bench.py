@@ -34,9 +34,12 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--batch", type=int, default=64)
-    p.add_argument("--prompt-len", type=int, default=1024)
-    p.add_argument("--gen", type=int, default=1024)
+    p.add_argument("--workload", choices=("isd", "risd"), default="isd",
+                   help="isd: decode throughput (default); risd: R-ISD == AR check and overhead factor")
+    p.add_argument("--model", choices=("8b", "32b"), default="8b", help="model shape of the isd workload")
+    p.add_argument("--batch", type=int, default=None, help="slots (default: the workload's)")
+    p.add_argument("--prompt-len", type=int, default=None)
+    p.add_argument("--gen", type=int, default=None)
     p.add_argument("--profile-steps", type=int, default=6)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graphs", action="store_true", help="launch every pass eagerly (no HIP graph replay)")
@@ -284,8 +287,191 @@ def cpu_baseline(shape, weights, eng, B, N, T):
     n_tok = len(out.tokens)
     return {"value": n_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"one ISD pass of one slot (1 of {B}): {len(ids)} rows over a {L}-token synthetic KV "
-                      f"cache, 36 layers + LM head + decisions, fp32 numpy; committed {n_tok} token(s) "
+                      f"cache, {shape.n_layers} layers + LM head + decisions, fp32 numpy; committed {n_tok} token(s) "
                       f"in {dt:.1f}s"}
+
+
+def prefill_engine(I, Engine, torch, shape, weights, dev, B, N, T, propose, prompt_len, gen, lora=None, chunk=16):
+    """An engine with B slots prefilled with uniformly random prompts (16 slots per call)."""
+    max_seq = prompt_len + gen + 2 * N + 8
+    eng = Engine(shape, weights, stride=N, temperature=T, propose=propose, seed=I.SEED_PHILOX, max_batch=B,
+                 max_seq_len=max_seq, max_prefill_tokens=chunk * prompt_len, lora=lora, device=dev)
+    log(f"engine N={N} lora={'yes' if lora else 'no'}: kv pool {eng.sizes[0] / 2**30:.1f} GiB, "
+        f"workspace {eng.sizes[1] / 2**30:.2f} GiB")
+    prompts = I.prompts(B, prompt_len, shape.vocab)
+    t0 = time.perf_counter()
+    first = []
+    for s0 in range(0, B, chunk):
+        sl = list(range(s0, min(B, s0 + chunk)))
+        first += eng.prefill(sl, [prompts[b] for b in sl], [gen] * len(sl)).cpu().tolist()
+        torch.cuda.synchronize()
+    log(f"prefill {B}x{prompt_len} in {time.perf_counter() - t0:.1f}s")
+    return eng, first
+
+
+def timed_steps(eng, torch, steps, warmup, graphs):
+    """Warm-up steps, then `steps` steps between two synchronizations; slot records around them."""
+    eng.set_graphs(graphs)
+    for _ in range(warmup):
+        eng.step()
+    torch.cuda.synchronize()
+    st0 = eng.slots_host()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        eng.step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    return elapsed, st0, eng.slots_host()
+
+
+def delta(st0, st1, field):
+    return sum(s1[field] - s0[field] for s0, s1 in zip(st0, st1))
+
+
+def kernel_profile(eng, shape, B, N, steps):
+    """Per-op launch counts and durations (HIP events on the launch stream) over `steps` passes,
+    with the algorithmic bytes / flops of the same passes."""
+    R = 2 * N - 1
+    ctx_rows = attn_keys = 0
+    eng.profile(True)
+    for _ in range(steps):
+        for s in eng.slots_host():
+            q = R if s["state"] == 1 else (N if s["state"] == 2 else 0)
+            if q:
+                ctx_rows += s["L"] + q
+                attn_keys += sum(s["L"] + i + 1 for i in range(q))
+        eng.step()
+    rep = eng.profile_report()
+    eng.profile(False)
+    P = max(1, steps)
+    model = kernel_model(shape, B * R, N, ctx_rows / P, attn_keys / P)
+    kernels = {}
+    for name, (n, tot_ms) in rep.items():
+        e = {"launches_per_step": n / P, "avg_us": 1e3 * tot_ms / n, "ms_per_step": tot_ms / P}
+        if name in model:
+            b, f = model[name]
+            e["GBps"] = b / (e["avg_us"] * 1e-6) / 1e9
+            e["TFLOPs"] = f / (e["avg_us"] * 1e-6) / 1e12
+        kernels[name] = e
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    d = kernels[dom]
+    b, f = model.get(dom, (0.0, 0.0))
+    intensity = f / b if b else 0.0
+    if dom in model and intensity > MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": d["TFLOPs"], "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": d["TFLOPs"] / MFMA_BF16_PEAK_TFS}
+    else:
+        gbs = d.get("GBps", 0.0)
+        roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}
+    roof["traffic"] = load_traffic(dom)
+    roof["kernel"] = dom
+    roof["per_launch"] = {"bytes": b, "flops": f, "avg_us": d["avg_us"]}
+    return kernels, roof, ctx_rows / P
+
+
+def report(args, wl_name, shape, B, N, T, propose, prompt_len, gen, elapsed, st0, st1, kernels, roof, ctx_rows,
+           metric=METRIC):
+    committed = delta(st0, st1, "committed")
+    ms = 1e3 * elapsed / args.steps
+    sb = step_bytes(shape, B * (2 * N - 1), ctx_rows)
+    return {
+        "metric": metric, "value": committed / elapsed, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (random-init weights N(0,0.02), uniformly random prompt ids)",
+        "config": {"workload": wl_name, "batch": B, "stride": N, "prompt_len": prompt_len, "max_new": gen,
+                   "propose": propose, "temperature": T, "parallelism": "single GPU",
+                   "hip_graphs": not args.no_graphs},
+        "isd_steps_per_s": args.steps / elapsed,
+        "tokens_per_forward": committed / max(1, delta(st0, st1, "passes")),
+        "acceptance": delta(st0, st1, "accepted") / max(1, delta(st0, st1, "verified")),
+        "step_hbm_GBps": sb / (ms * 1e-3) / 1e9,
+        "step_hbm_frac": sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "step_algorithmic_bytes": sb,
+        "projected_tokens_per_s_at_p0.9": args.steps / elapsed * B * tpf_projection(0.9, N),
+        "roofline": roof,
+        "kernels": kernels,
+    }
+
+
+def emit(args, out):
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(line + "\n")
+
+
+def generate(eng, torch, B):
+    """Decode every slot to completion; the committed tokens of each slot (prefill's first one
+    not included)."""
+    toks = [[] for _ in range(B)]
+    n = 0
+    while True:
+        st = eng.slots_host()
+        if not any(s["state"] in (1, 2) for s in st):
+            return toks, n
+        tok, nc, _ = eng.step()
+        n += 1
+        t, c = tok.cpu().numpy(), nc.cpu().numpy()
+        for b in range(B):
+            toks[b] += t[b, :c[b]].tolist()
+
+
+def run_risd(args, I, Engine, torch, dev):
+    """R-ISD on the 8B shape: greedy R-ISD (gated rank-128 LoRA on the MASK rows) must commit
+    exactly the tokens of greedy AR decoding (N = 1) with the base weights; the overhead factor
+    alpha is the R-ISD step time over the step time of ISD without the adapter (same shapes)."""
+    wl = I.RISD_8B
+    shape, N, T, propose = wl.model, wl.stride, wl.temperature, wl.propose
+    B = args.batch or wl.batch
+    pl = args.prompt_len or wl.prompt_len
+    gen = args.gen or wl.max_new
+    t0 = time.perf_counter()
+    weights, lora = I.weights_torch(shape, dev, lora_rank=wl.lora_rank)
+    torch.cuda.synchronize()
+    log(f"weights + rank-{wl.lora_rank} adapter generated in {time.perf_counter() - t0:.1f}s")
+    seqs = {}
+    for name, n, lo in (("risd", N, lora), ("ar", 1, None)):
+        eng, first = prefill_engine(I, Engine, torch, shape, weights, dev, B, n, T, propose, pl, gen, lora=lo)
+        eng.set_graphs(not args.no_graphs)
+        t0 = time.perf_counter()
+        toks, steps = generate(eng, torch, B)
+        seqs[name] = [[f] + t for f, t in zip(first, toks)]
+        log(f"{name}: {steps} passes, {sum(len(t) for t in toks)} tokens in {time.perf_counter() - t0:.1f}s")
+        del eng
+        torch.cuda.empty_cache()
+    same = seqs["risd"] == seqs["ar"]
+    n_cmp = sum(len(t) for t in seqs["ar"])
+    first_diff = None
+    if not same:
+        for b, (x, y) in enumerate(zip(seqs["risd"], seqs["ar"])):
+            if x != y:
+                first_diff = {"slot": b, "index": next(i for i, (u, v) in enumerate(zip(x, y)) if u != v)}
+                break
+    log(f"R-ISD greedy == AR greedy: {same} ({n_cmp} tokens)")
+    res = {}
+    for name, lo in (("isd", None), ("risd", lora)):
+        eng, _ = prefill_engine(I, Engine, torch, shape, weights, dev, B, N, T, propose, pl, gen, lora=lo)
+        elapsed, st0, st1 = timed_steps(eng, torch, args.steps, args.warmup, not args.no_graphs)
+        log(f"{name}: {1e3 * elapsed / args.steps:.3f} ms/step")
+        if name == "risd":
+            kernels, roof, ctx = kernel_profile(eng, shape, B, N, args.profile_steps)
+        res[name] = (elapsed, st0, st1)
+        del eng
+        torch.cuda.empty_cache()
+    elapsed, st0, st1 = res["risd"]
+    out = report(args, wl.name, shape, B, N, T, propose, pl, gen, elapsed, st0, st1, kernels, roof, ctx,
+                 metric="committed tokens/s on 1 MI355X (8B-shape R-ISD, batch 16, N=4, greedy)")
+    out["config"]["lora_rank"] = wl.lora_rank
+    out["risd_alpha"] = res["risd"][0] / res["isd"][0]
+    out["isd_no_adapter_ms_per_step"] = 1e3 * res["isd"][0] / args.steps
+    out["risd_equals_ar_greedy"] = same
+    out["ar_tokens_compared"] = n_cmp
+    if first_diff:
+        out["first_difference"] = first_diff
+    emit(args, out)
 
 
 def main():
@@ -304,113 +490,30 @@ def main():
     import isd_inputs as I
     from strided_decoding_amd import Engine
 
-    wl = I.QWEN3_8B_DECODE
-    shape = wl.model
-    B, N, T = args.batch, wl.stride, wl.temperature
-    R = 2 * N - 1
     dev = torch.device("cuda:0")
+    if args.workload == "risd":
+        return run_risd(args, I, Engine, torch, dev)
+    wl = I.QWEN3_32B_DECODE if args.model == "32b" else I.QWEN3_8B_DECODE
+    shape, N, T, propose = wl.model, wl.stride, wl.temperature, wl.propose
+    B = args.batch or wl.batch
+    pl = args.prompt_len or wl.prompt_len
+    gen = args.gen or wl.max_new
     t0 = time.perf_counter()
     weights, _ = I.weights_torch(shape, dev)
     torch.cuda.synchronize()
     log(f"weights generated in {time.perf_counter() - t0:.1f}s")
-    max_seq = args.prompt_len + args.gen + 2 * N + 8
-    chunk = 16
-    eng = Engine(shape, weights, stride=N, temperature=T, propose=wl.propose, seed=I.SEED_PHILOX, max_batch=B,
-                 max_seq_len=max_seq, max_prefill_tokens=chunk * args.prompt_len, device=dev)
-    log(f"engine: kv pool {eng.sizes[0] / 2**30:.1f} GiB, workspace {eng.sizes[1] / 2**30:.2f} GiB")
-    prompts = I.prompts(B, args.prompt_len, shape.vocab)
-    t0 = time.perf_counter()
-    for s0 in range(0, B, chunk):
-        sl = list(range(s0, min(B, s0 + chunk)))
-        eng.prefill(sl, [prompts[b] for b in sl], [args.gen] * len(sl))
-        torch.cuda.synchronize()
-        log(f"prefilled slots {sl[0]}..{sl[-1]}")
-    log(f"prefill {B}x{args.prompt_len} in {time.perf_counter() - t0:.1f}s")
-
-    eng.set_graphs(not args.no_graphs)
-    for _ in range(args.warmup):
-        eng.step()
-    torch.cuda.synchronize()
-    st0 = eng.slots_host()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        eng.step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    st1 = eng.slots_host()
-    committed = sum(s1["committed"] - s0["committed"] for s0, s1 in zip(st0, st1))
-    passes = sum(s1["passes"] - s0["passes"] for s0, s1 in zip(st0, st1))
-    verified = sum(s1["verified"] - s0["verified"] for s0, s1 in zip(st0, st1))
-    accepted = sum(s1["accepted"] - s0["accepted"] for s0, s1 in zip(st0, st1))
+    eng, _ = prefill_engine(I, Engine, torch, shape, weights, dev, B, N, T, propose, pl, gen)
+    elapsed, st0, st1 = timed_steps(eng, torch, args.steps, args.warmup, not args.no_graphs)
     live = sum(1 for s in st1 if s["state"] in (1, 2))
-    ms = 1e3 * elapsed / args.steps
-    log(f"timed {args.steps} steps: {ms:.3f} ms/step, {committed} tokens, live slots {live}")
-
-    # kernel timings: a separate phase with event pairs around every launch
-    ctx_rows = attn_keys = 0
-    eng.profile(True)
-    for _ in range(args.profile_steps):
-        before = eng.slots_host()
-        for s in before:
-            q = R if s["state"] == 1 else (N if s["state"] == 2 else 0)
-            if q:
-                ctx_rows += s["L"] + q
-                attn_keys += sum(s["L"] + i + 1 for i in range(q))
-        eng.step()
-    rep = eng.profile_report()
-    eng.profile(False)
-    P = max(1, args.profile_steps)
-    model = kernel_model(shape, B * R, N, ctx_rows / P, attn_keys / P)
-    kernels = {}
-    for name, (n, tot_ms) in rep.items():
-        per_pass = n / P
-        e = {"launches_per_step": per_pass, "avg_us": 1e3 * tot_ms / n, "ms_per_step": tot_ms / P}
-        if name in model:
-            b, f = model[name]
-            e["GBps"] = b / (e["avg_us"] * 1e-6) / 1e9
-            e["TFLOPs"] = f / (e["avg_us"] * 1e-6) / 1e12
-        kernels[name] = e
-    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
-    d = kernels[dom]
-    b, f = model.get(dom, (0.0, 0.0))
-    intensity = f / b if b else 0.0
-    if dom in model and intensity > MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9):
-        roof = {"bound": "mfma", "achieved": d["TFLOPs"], "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                "frac": d["TFLOPs"] / MFMA_BF16_PEAK_TFS, "traffic": None}
-    else:
-        gbs = d.get("GBps", 0.0)
-        roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": gbs / HBM_PEAK_GBS, "traffic": None}
-    roof["traffic"] = load_traffic(dom)
-    roof["kernel"] = dom
-    roof["per_launch"] = {"bytes": b, "flops": f, "avg_us": d["avg_us"]}
-    sb = step_bytes(shape, B * R, ctx_rows / P)
-    out = {
-        "metric": METRIC, "value": committed / elapsed, "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (random-init weights N(0,0.02), uniformly random prompt ids)",
-        "config": {"workload": wl.name, "batch": B, "stride": N, "prompt_len": args.prompt_len,
-                   "max_new": args.gen, "propose": wl.propose, "temperature": T, "parallelism": "single GPU",
-                   "hip_graphs": not args.no_graphs},
-        "isd_steps_per_s": args.steps / elapsed,
-        "tokens_per_forward": committed / max(1, passes),
-        "acceptance": accepted / max(1, verified),
-        "step_hbm_GBps": sb / (ms * 1e-3) / 1e9,
-        "step_hbm_frac": sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "step_algorithmic_bytes": sb,
-        "projected_tokens_per_s_at_p0.9": args.steps / elapsed * B * tpf_projection(0.9, N),
-        "roofline": roof,
-        "kernels": kernels,
-    }
+    log(f"timed {args.steps} steps: {1e3 * elapsed / args.steps:.3f} ms/step, "
+        f"{delta(st0, st1, 'committed')} tokens, live slots {live}")
+    kernels, roof, ctx = kernel_profile(eng, shape, B, N, args.profile_steps)
+    name = wl.name if B == wl.batch else wl.name.rsplit("-b", 1)[0] + f"-b{B}"
+    metric = METRIC if wl is I.QWEN3_8B_DECODE else f"committed tokens/s on 1 MI355X (32B-shape, batch {B}, N=4)"
+    out = report(args, name, shape, B, N, T, propose, pl, gen, elapsed, st0, st1, kernels, roof, ctx, metric)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, weights, eng, B, N, T)
-    line = json.dumps(out)
-    print(line, flush=True)
-    if args.out:
-        with open(args.out, "w") as f:
-            f.write(line + "\n")
+    emit(args, out)
 
 
 if __name__ == "__main__":
