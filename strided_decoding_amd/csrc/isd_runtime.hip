@@ -200,7 +200,7 @@ void derive(isd_ctx& x) {
   x.max_dec_rows = c.max_batch * x.R;
   x.max_rows = std::max(x.max_dec_rows, c.max_prefill_tokens);
   x.n_chunks = cdiv(c.vocab, kStatChunk);
-  x.attn_split = attn_split_len(c.max_batch);
+  x.attn_split = attn_split_len(c.max_batch, c.n_kv_heads, c.max_seq_len + 2 * c.stride_n);
   x.max_splits = cdiv(c.max_seq_len + 2 * c.stride_n, x.attn_split);
   const int G = c.n_q_heads / c.n_kv_heads;
   x.ncb = (x.R * G <= 32) ? 2 : 4;
@@ -767,7 +767,7 @@ isd_status isd_profile_report(isd_ctx* x, isd_prof_entry* out, int32_t cap, int3
 
 size_t isd_attn_workspace_bytes(const isd_attn_args* a) {
   if (!a) return 0;
-  const int splits = cdiv(std::max(1, a->max_ctx), attn_split_len(a->batch));
+  const int splits = cdiv(std::max(1, a->max_ctx), attn_split_len(a->batch, a->n_kv_heads, a->max_ctx));
   const size_t rows = (size_t)a->batch * a->rows;
   size_t off = 0;
   off = align_up(off + a->batch * sizeof(AttnItem));
@@ -786,7 +786,7 @@ isd_status isd_attn_paged(const isd_attn_args* a, void* stream) {
     return ISD_E_ARG;
   const int G = a->n_q_heads / a->n_kv_heads;
   if (a->head_dim != 128 || a->page_size != 16 || G * a->rows > 64) return ISD_E_SHAPE;
-  const int split = attn_split_len(a->batch);
+  const int split = attn_split_len(a->batch, a->n_kv_heads, a->max_ctx);
   const int splits = cdiv(a->max_ctx, split);
   const size_t rows = (size_t)a->batch * a->rows;
   char* w = (char*)a->workspace;

@@ -76,22 +76,25 @@ __global__ __launch_bounds__(64 * NCB) void attn_bf16_kernel(AttnArgs a) {
   const uint16_t* qsrc =
       (const uint16_t*)a.q + (size_t)(it.row0 + (qvalid ? qp : 0)) * q_stride + (size_t)(kvh * G + qh) * HD + g * 8;
 
-  // Page ids of the key range, lane l holding logical page win + l (a window of 64 pages,
-  // 1024 keys; longer ranges reload it), read out with readlane: no memory access inside the
-  // KV pipeline besides its own loads.
+  // Page ids of the key range, lane l holding logical pages win + l and win + 64 + l (a window
+  // of 128 pages, 2048 keys: a whole context split; longer ranges reload it), read out with
+  // readlane: no memory access inside the KV pipeline besides its own loads.
   const int32_t* pt = a.page_table + (size_t)it.slot * a.max_pages;
   const int last_page = (k_end - 1) >> 4;
   int win = k_begin >> 4;
-  int pid = pt[min(win + lane, last_page)];
+  int pid0 = pt[min(win + lane, last_page)];
+  int pid1 = pt[min(win + 64 + lane, last_page)];
   wait_vmcnt<0>();
   auto page_of = [&](int pg) -> int {
-    if (pg >= win + 64) {
+    if (pg >= win + 128) {
       wait_vmcnt<0>();
       win = pg;
-      pid = pt[min(win + lane, last_page)];
+      pid0 = pt[min(win + lane, last_page)];
+      pid1 = pt[min(win + 64 + lane, last_page)];
       wait_vmcnt<0>();
     }
-    return __builtin_amdgcn_readlane(pid, pg - win);
+    const int o = pg - win;
+    return o < 64 ? __builtin_amdgcn_readlane(pid0, o) : __builtin_amdgcn_readlane(pid1, o - 64);
   };
   const size_t page_elems = (size_t)a.Hkv * 16 * HD;
   const uint16_t* kbase = (const uint16_t*)a.k_pool + (size_t)kvh * 16 * HD;
@@ -380,7 +383,13 @@ __global__ void attn_setup_kernel(AttnItem* items, int32_t* row_pos, int32_t* ro
 
 }  // namespace
 
-int attn_split_len(int batch) { return batch <= 16 ? 128 : batch <= 32 ? 256 : 512; }
+int attn_split_len(int batch, int n_kv_heads, int max_ctx) {
+  // about 2048 (slot, KV head, split) workgroups at the longest context, 128 .. 2048 keys each
+  const long long want = ((long long)max_ctx * batch * n_kv_heads + 2047) / 2048;
+  int split = 128;
+  while (split < 2048 && split < want) split *= 2;
+  return split;
+}
 
 hipError_t launch_attn_setup(AttnItem* items, int32_t* row_pos, int32_t* row_slot, const int32_t* ctx_len,
                              const int32_t* q_len, int batch, int rows, hipStream_t s) {

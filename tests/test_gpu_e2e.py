@@ -176,10 +176,10 @@ def test_small_bf16_end_to_end():
 
 
 def test_small_bf16_long_prompt():
-    """A prompt longer than 1024 tokens: prefill attention spans more than one 64-page window of
+    """A prompt longer than 2048 tokens: prefill attention spans more than one 128-page window of
     page ids, and decode passes merge many context splits."""
     shape = I.SMALL_BF16
     w = I.weights_numpy(shape, seed=0, scale=20.0)
-    prompts = I.ragged_prompts([1300, 90], shape.vocab, seed=8)
+    prompts = I.ragged_prompts([2300, 90], shape.vocab, seed=8)
     teacher_forced(shape, w, 4, 1.0, "sample", prompts, [6, 6], steps=4, logits_tol=2e-2, rel=True,
                    on_gpu_logits=True)
