@@ -182,8 +182,11 @@ def lora_shapes(shape, rank):
     return {m: ((rank, io[m][0]), (io[m][1], rank)) for m in LORA_TARGETS}
 
 
-def lora_numpy(shape, rank, seed=SEED_LORA):
-    """Per layer {target: (A [r, d_in], B [d_out, r])}, generator PCG64([seed, index])."""
+def lora_numpy(shape, rank, seed=SEED_LORA, scale=1.0):
+    """Per layer {target: (A [r, d_in], B [d_out, r])}, generator PCG64([seed, index]).
+
+    scale (test-only) multiplies A and B, so that the adapter's contribution is of the order
+    of the base projection's and a wrong delta cannot hide inside a tolerance."""
     out = []
     idx = 0
     shp = lora_shapes(shape, rank)
@@ -192,7 +195,7 @@ def lora_numpy(shape, rank, seed=SEED_LORA):
         for m in LORA_TARGETS:
             pair = []
             for s in shp[m]:
-                a = _rng(seed, idx).standard_normal(s, dtype=np.float32) * np.float32(INIT_STD)
+                a = _rng(seed, idx).standard_normal(s, dtype=np.float32) * np.float32(INIT_STD * scale)
                 idx += 1
                 pair.append(bf16_bits(a) if shape.dtype == "bf16" else a)
             layer[m] = tuple(pair)

@@ -161,9 +161,26 @@ struct GemmArgs {
   void* norm_out;
   float norm_eps;
   int path;                  // bf16 kernel choice: GEMM_PATH_AUTO / _TILED / _SKINNY
+  // Segmented A (0 = off): output columns [seg_end[j-1], seg_end[j]) read A columns starting at
+  // seg_aoff[j], i.e. several products X_j W_j^T with stacked W_j in one launch.  Segment ends
+  // must be multiples of 256 (no column tile straddles two segments).
+  int nseg;
+  int seg_end[3];
+  int seg_aoff[3];
 };
 enum { GEMM_PATH_AUTO = 0, GEMM_PATH_TILED = 1, GEMM_PATH_SKINNY = 2 };
-constexpr int kSkinnyMaxRows = 64;   // the skinny kernel holds at most two 32-row MFMA tiles
+constexpr int kSkinnyMaxRows = 128;  // the skinny kernel holds at most four 32-row MFMA tiles
+
+// A column offset of the output columns starting at n0 (segmented products; 0 otherwise).
+ISD_DEV int gemm_seg_aoff(const GemmArgs& a, int n0) {
+  int off = 0;
+  for (int j = a.nseg - 1; j >= 0; --j)
+    if (j == 0 || n0 >= a.seg_end[j - 1]) {
+      off = a.seg_aoff[j];
+      break;
+    }
+  return off;
+}
 
 // Split-K factor of a bf16 projection: a function of the output width and K only (never of
 // the row count), so that a row's result is the same whatever the batch composition.

@@ -296,21 +296,48 @@ GemmArgs gargs(const void* A, int lda, const void* B0, int ldb, int M, int N, in
   return g;
 }
 
-// LoRA of one target on the MASK rows: S[:, so:so+r] = X[mask_rows] A^T; delta[:, do:do+n] = S B^T.
-isd_status lora_target(isd_ctx& x, int layer, int tgt, const void* Xsrc, int ldx, int k_in, int n_out, int s_off,
-                       int d_off, hipStream_t s) {
+// LoRA of nt targets sharing one input on the MASK rows (targets t0 .. t0+nt-1, output widths
+// n[j]): S[:, j r .. (j+1) r] = X[mask_rows] A_j^T, then delta[:, o_j .. o_j + n_j] = S_j B_j^T with
+// o_j = n_0 + .. + n_{j-1}.  When the targets' A (and B) matrices are stacked in memory the
+// shrinks run as one product and the expands as one segmented product.
+isd_status lora_group(isd_ctx& x, int layer, int t0, int nt, const void* Xsrc, int ldx, int k_in, const int* n,
+                      hipStream_t s) {
   const int r = x.cfg.lora_rank, M = x.n_mask;
-  const void* A = x.lora_a[(size_t)layer * 7 + tgt];
-  const void* Bm = x.lora_b[(size_t)layer * 7 + tgt];
-  GemmArgs g = gargs(Xsrc, ldx, A, k_in, M, r, k_in, EPI_STORE);
-  g.a_rows = x.mask_rows;
-  g.C = (char*)x.lora_s + (size_t)s_off * x.act;
-  g.ldc = 3 * r;
-  TIMED("lora_shrink", gemm(x, g, s));
-  GemmArgs e = gargs((const char*)x.lora_s + (size_t)s_off * x.act, 3 * r, Bm, r, M, n_out, r, EPI_STORE_F32);
-  e.C = x.lora_delta + d_off;
-  e.ldc = x.delta_w;
-  TIMED("lora_expand", gemm(x, e, s));
+  const char* const* A = (const char* const*)&x.lora_a[(size_t)layer * 7 + t0];
+  const char* const* Bm = (const char* const*)&x.lora_b[(size_t)layer * 7 + t0];
+  bool stackA = true, stackB = x.bf;     // segmented products: bf16 kernels only
+  for (int j = 1; j < nt; ++j) {
+    stackA = stackA && A[j] == A[j - 1] + (size_t)r * k_in * x.act;
+    stackB = stackB && Bm[j] == Bm[j - 1] + (size_t)n[j - 1] * r * x.act && n[j - 1] % 256 == 0;
+  }
+  for (int j = 0; j < nt; ++j) {
+    if (j > 0 && stackA) break;
+    GemmArgs g = gargs(Xsrc, ldx, A[j], k_in, M, stackA ? nt * r : r, k_in, EPI_STORE);
+    g.a_rows = x.mask_rows;
+    g.C = (char*)x.lora_s + (size_t)j * r * x.act;
+    g.ldc = 3 * r;
+    TIMED("lora_shrink", gemm(x, g, s));
+  }
+  int o = 0;
+  for (int j = 0; j < nt; ++j) {
+    if (j > 0 && stackB) break;
+    int n_out = n[j];
+    GemmArgs e = gargs((const char*)x.lora_s + (size_t)j * r * x.act, 3 * r, Bm[j], r, M, n_out, r, EPI_STORE_F32);
+    if (stackB && nt > 1) {
+      n_out = 0;
+      e.nseg = nt;
+      for (int i = 0; i < nt; ++i) {
+        n_out += n[i];
+        e.seg_end[i] = n_out;
+        e.seg_aoff[i] = i * r;
+      }
+      e.N = n_out;
+    }
+    e.C = x.lora_delta + o;
+    e.ldc = x.delta_w;
+    TIMED("lora_expand", gemm(x, e, s));
+    o += n_out;
+  }
   return ISD_OK;
 }
 
@@ -339,13 +366,9 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
       else TIMED("rmsnorm", launch_rmsnorm<float>(x.X, (const float*)x.attn_norm[0], (float*)x.Xn, M, d, c.rms_eps, s));
     }
     if (lora) {
-      const int r = c.lora_rank;
-      const char* wq = nullptr;
-      (void)wq;
-      isd_status st;
-      if ((st = lora_target(x, l, 0, x.Xn, d, d, x.qd, 0, 0, s)) != ISD_OK) return st;
-      if ((st = lora_target(x, l, 1, x.Xn, d, d, x.kd, r, x.qd, s)) != ISD_OK) return st;
-      if ((st = lora_target(x, l, 2, x.Xn, d, d, x.kd, 2 * r, x.qd + x.kd, s)) != ISD_OK) return st;
+      const int n[3] = {x.qd, x.kd, x.kd};
+      isd_status st = lora_group(x, l, 0, 3, x.Xn, d, d, n, s);
+      if (st != ISD_OK) return st;
     }
     {
       GemmArgs g = gargs(x.Xn, d, x.wqkv[l], d, M, x.qkvw, d, EPI_STORE);
@@ -409,7 +432,8 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
       }
     }
     if (lora) {
-      isd_status st = lora_target(x, l, 3, x.O, x.qd, x.qd, d, 0, 0, s);
+      const int n[1] = {d};
+      isd_status st = lora_group(x, l, 3, 1, x.O, x.qd, x.qd, n, s);
       if (st != ISD_OK) return st;
     }
     {
@@ -425,10 +449,9 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
     }
     // FFN block
     if (lora) {
-      const int r = c.lora_rank;
-      isd_status st;
-      if ((st = lora_target(x, l, 4, x.Xn, d, d, F, 0, 0, s)) != ISD_OK) return st;
-      if ((st = lora_target(x, l, 5, x.Xn, d, d, F, r, F, s)) != ISD_OK) return st;
+      const int n[2] = {F, F};
+      isd_status st = lora_group(x, l, 4, 2, x.Xn, d, d, n, s);
+      if (st != ISD_OK) return st;
     }
     {
       GemmArgs g = gargs(x.Xn, d, x.wg[l], d, M, F, d, EPI_SWIGLU);
@@ -440,7 +463,8 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
       TIMED("gemm_gate_up", gemm(x, g, s));
     }
     if (lora) {
-      isd_status st = lora_target(x, l, 6, x.H, F, F, d, 0, 0, s);
+      const int n[1] = {d};
+      isd_status st = lora_group(x, l, 6, 1, x.H, F, F, n, s);
       if (st != ISD_OK) return st;
     }
     {

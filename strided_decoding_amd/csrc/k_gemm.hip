@@ -32,8 +32,12 @@ constexpr int GROUP_BYTES = 16 * BK * 2;                 // 16 rows x 64 B
 #ifndef ISD_SKINNY_STAGES_2
 #define ISD_SKINNY_STAGES_2 8
 #endif
-// LDS ring depth of the skinny kernel for one / two 32-row tiles
-constexpr int kSkinnyStages1 = ISD_SKINNY_STAGES_1, kSkinnyStages2 = ISD_SKINNY_STAGES_2;
+#ifndef ISD_SKINNY_STAGES_4
+#define ISD_SKINNY_STAGES_4 5
+#endif
+// LDS ring depth of the skinny kernel for one / two / four 32-row tiles
+constexpr int kSkinnyStages1 = ISD_SKINNY_STAGES_1, kSkinnyStages2 = ISD_SKINNY_STAGES_2,
+              kSkinnyStages4 = ISD_SKINNY_STAGES_4;
 constexpr int STAGE_BYTES = (TM2 + TN2) / 16 * GROUP_BYTES;  // 30 KB
 
 template <typename T, int EPI>
@@ -94,6 +98,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_big_kernel(GemmArgs a, int n_mt
   // same 32 output columns (block t: matrix t%2, outputs 32 (t/2) ..).
   const int lrow = lane >> 2;
   const int chunk = (lane & 3) ^ ((lrow >> 2) & 3);
+  const int aoff = gemm_seg_aoff(a, n0);
   const uint16_t* src[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -105,7 +110,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_big_kernel(GemmArgs a, int n_mt
         srow = a.a_rows ? a.a_rows[m] : m;
         if (srow < 0) srow = 0;          // unused row (its outputs are never consumed)
       }
-      src[i] = (const uint16_t*)a.A + (size_t)srow * a.lda + kbase + chunk * 8;
+      src[i] = (const uint16_t*)a.A + (size_t)srow * a.lda + aoff + kbase + chunk * 8;
     } else {
       const int bg = g - AG;                      // B row group 0..15
       const uint16_t* bm = (const uint16_t*)a.B0;
@@ -297,7 +302,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_big_kernel(GemmArgs a, int n_mt
   }
 }
 
-// Skinny path for at most 64 rows (decode at small batch, where a projection is bound by
+// Skinny path for at most 128 rows (decode at small batch, where a projection is bound by
 // streaming its weights from HBM).  One single-wave workgroup per (output-column group, K
 // split); no barriers.  The wave streams its weight rows and the (L2-resident) activation
 // rows through a private SD-stage LDS ring filled by direct global->LDS loads, with the loads
@@ -328,6 +333,7 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_
   // operand reads below are free of bank conflicts.
   const int lrow = lane >> 2;
   const int chunk = (lane & 3) ^ ((lrow >> 2) & 3);
+  const int aoff = gemm_seg_aoff(a, n0);
   const uint16_t* src[OPS][2];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
@@ -339,7 +345,7 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_
         srow = a.a_rows ? a.a_rows[m] : m;
         if (srow < 0) srow = 0;               // unused row (its outputs are never consumed)
       }
-      src[i][g] = (const uint16_t*)a.A + (size_t)srow * a.lda + kbase + chunk * 8;
+      src[i][g] = (const uint16_t*)a.A + (size_t)srow * a.lda + aoff + kbase + chunk * 8;
     }
 #pragma unroll
   for (int j = 0; j < NB; ++j)
@@ -596,7 +602,7 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
 
 template <int EPI>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
-  constexpr int SD1 = kSkinnyStages1, SD2 = kSkinnyStages2;
+  constexpr int SD1 = kSkinnyStages1, SD2 = kSkinnyStages2, SD4 = kSkinnyStages4;
   const int tno = EPI == EPI_SWIGLU ? 32 : 64;
   const int n_nt = (a.N + tno - 1) / tno;
   const int S = (a.splits > 1 && a.part) ? a.splits : 1;
@@ -605,9 +611,12 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 32) {
     if (S > 1) hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, true, 1, SD1>), grid, dim3(64), 0, s, a, n_nt, S, part);
     else hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, false, 1, SD1>), grid, dim3(64), 0, s, a, n_nt, S, part);
-  } else {
+  } else if (a.M <= 64) {
     if (S > 1) hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, true, 2, SD2>), grid, dim3(64), 0, s, a, n_nt, S, part);
     else hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, false, 2, SD2>), grid, dim3(64), 0, s, a, n_nt, S, part);
+  } else {
+    if (S > 1) hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, true, 4, SD4>), grid, dim3(64), 0, s, a, n_nt, S, part);
+    else hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, false, 4, SD4>), grid, dim3(64), 0, s, a, n_nt, S, part);
   }
   return finish<EPI>(a, S, s);
 }
@@ -639,6 +648,9 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   const int S = (a.splits > 1 && a.part) ? a.splits : 1;
   if ((a.K / BK) % S != 0) return hipErrorInvalidValue;
   if (a.path == GEMM_PATH_SKINNY && a.M > kSkinnyMaxRows) return hipErrorInvalidValue;
+  if (a.nseg < 0 || a.nseg > 3 || (a.nseg > 1 && (S > 1 || a.epi == EPI_SWIGLU))) return hipErrorInvalidValue;
+  for (int j = 0; j + 1 < a.nseg; ++j)
+    if (a.seg_end[j] % TN2) return hipErrorInvalidValue;
   switch (a.epi) {
     case EPI_STORE: return launch_path<EPI_STORE>(a, s);
     case EPI_STORE_F32: return launch_path<EPI_STORE_F32>(a, s);

@@ -63,8 +63,21 @@ class Engine:
         self.wl = [{k: to_device(v, dt, dev) for k, v in layer.items()} for layer in weights["layers"]]
         self.lora = None
         if lora is not None:
-            self.lora = [{m: (to_device(layer[m][0], dt, dev), to_device(layer[m][1], dt, dev))
-                          for m in LORA_ORDER} for layer in lora]
+            # stacked per layer: A of (q, k, v) and of (gate, up) contiguous, and likewise B, so
+            # that the library runs each group's shrink (and expand) as one product
+            self.lora = []
+            for layer in lora:
+                ent = {}
+                for group in (("q", "k", "v"), ("o",), ("g", "u"), ("d",)):
+                    for which in (0, 1):
+                        parts = [to_device(layer[m][which], dt, dev) for m in group]
+                        flat = torch.cat([t.reshape(-1) for t in parts])
+                        off = 0
+                        for m, t in zip(group, parts):
+                            view = flat[off:off + t.numel()].view(t.shape)
+                            off += t.numel()
+                            ent.setdefault(m, [None, None])[which] = view
+                self.lora.append({m: tuple(v) for m, v in ent.items()})
 
         def arr(name):
             return (C.c_void_p * len(self.wl))(*[t[name].data_ptr() for t in self.wl])
@@ -223,7 +236,7 @@ def gemm(X, W, mode="store", W2=None, out=None, R=None, splits=0, workspace=None
     """Kernel-level projection (see isd_gemm): X [M, K], W [N, K] (bf16 or float32 on device).
 
     mode "resid" with norm_g / norm_out also writes RMSNorm(R) * norm_g into norm_out.
-    path: "auto", "tiled" or "skinny" (bf16 kernel choice; M <= 64 for skinny)."""
+    path: "auto", "tiled" or "skinny" (bf16 kernel choice; M <= 128 for skinny)."""
     lib = A.load()
     M, K = X.shape
     N = W.shape[0]

@@ -183,3 +183,20 @@ def test_small_bf16_long_prompt():
     prompts = I.ragged_prompts([2300, 90], shape.vocab, seed=8)
     teacher_forced(shape, w, 4, 1.0, "sample", prompts, [6, 6], steps=4, logits_tol=2e-2, rel=True,
                    on_gpu_logits=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_lora_mask_rows_end_to_end(dtype):
+    """Gated LoRA (R-ISD adapter) on q, k, v, o, gate, up, down at the MASK rows: the GPU
+    logits of every row, MASK rows included, follow the oracle's; the adapter is scaled up so
+    that its contribution is of the order of the base projections'."""
+    shape = I.TINY if dtype == "f32" else I.SMALL_BF16
+    rank = 8 if dtype == "f32" else 64
+    w = I.weights_numpy(shape, seed=0, scale=1.0 if dtype == "f32" else 20.0)
+    lora = I.lora_numpy(shape, rank, scale=15.0)
+    prompts = I.ragged_prompts([21, 9, 40], shape.vocab, seed=14)
+    if dtype == "f32":
+        teacher_forced(shape, w, 3, 1.0, "sample", prompts, [10, 12, 8], steps=10, lora=lora)
+    else:
+        teacher_forced(shape, w, 3, 1.0, "sample", prompts, [10, 12, 8], steps=8, lora=lora, logits_tol=2e-2,
+                       rel=True, on_gpu_logits=True)

@@ -126,7 +126,7 @@ def test_gemm_residual_with_fused_rmsnorm(splits):
     _check(y.float().cpu().numpy().ravel(), yref.ravel())
 
 
-SKINNY_ROWS = [1, 7, 28, 32, 33, 56, 64]
+SKINNY_ROWS = [1, 7, 28, 32, 33, 56, 64, 65, 112, 128]
 
 
 @pytest.mark.parametrize("M", SKINNY_ROWS)
@@ -148,7 +148,7 @@ def test_skinny_path_bit_identical_to_tiled(M, mode, N, K):
             outs.append(gemm(X, W, mode, W2=W2, path=path))
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1])
-    if M in (7, 56):
+    if M in (7, 56, 112):
         rows, cols = _pick(M, N, 300, 34)
         ref = _ref(X, W, rows, cols)
         if mode == "swiglu":
