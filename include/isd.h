@@ -84,7 +84,12 @@ typedef struct {
  *   wo[l] [d, Hq*hd]        ffn_norm[l] [d]
  *   wg[l], wu[l] [F, d]     wd[l] [d, F]
  *   lora_a[l*7+m] [r, d_in_m], lora_b[l*7+m] [d_out_m, r] for m = q,k,v,o,g,u,d
- *   (HOST arrays of n_layers*7 device pointers; NULL when lora_rank == 0). */
+ *   (HOST arrays of n_layers*7 device pointers; NULL when lora_rank == 0).
+ * The matrices are out x in.  With ISD_BF16 the projection matrices (lm_head, wqkv, wo, wg,
+ * wu, wd, lora_a, lora_b) are in the packed operand layout made by isd_pack_weights; embed and
+ * the norm gains, and every matrix of ISD_F32, are row-major.  The LoRA matrices of q, k, v
+ * (and of gate, up) may be stored back to back (packed): the library then runs each group's
+ * products as one. */
 typedef struct {
   const void* embed;
   const void* final_norm;
@@ -268,9 +273,22 @@ typedef struct {
 size_t isd_sample_workspace_bytes(int32_t batch, int32_t rows, int32_t vocab, int32_t q_rows);
 isd_status isd_sample(const isd_sample_args* a, void* stream);
 
-/* One projection of the decode step: Y = X W^T (X [M, K] row-major, W [N, K] row-major,
- * i.e. out x in) in the context's arithmetic, as isd_step runs it.
- *   dtype    ISD_BF16 (MFMA path, X and W bf16) or ISD_F32
+/* Packed operand layout of the bf16 projection weights (the MFMA B operands of the GEMMs,
+ * one contiguous kilobyte per 32x32x16 product): W [rows, cols] row-major bf16 becomes
+ * ceil(rows/32) x (cols/16) blocks of 64 x 8 elements, block (nb, kb) at element
+ * (nb * cols/16 + kb) * 512, whose lane-l part (8 elements) is row 32 nb + l%32, columns
+ * 16 kb + 8 (l/32) .. + 7; rows past `rows` are zero.
+ * isd_packed_weight_bytes: bytes of the packed matrix (0 if cols is not a positive multiple
+ * of 16 or rows < 1).  isd_pack_weights: converts src (device, row-major [rows, cols]) into
+ * dst (device, caller-owned, isd_packed_weight_bytes); both 16-byte aligned, not overlapping;
+ * enqueued on stream.  Errors: ISD_E_ARG (pointers), ISD_E_SHAPE (sizes), ISD_E_HIP. */
+size_t isd_packed_weight_bytes(int32_t rows, int32_t cols);
+isd_status isd_pack_weights(const void* src, void* dst, int32_t rows, int32_t cols, void* stream);
+
+/* One projection of the decode step: Y = X W^T (X [M, K] row-major, W [N, K], i.e. out x in)
+ * in the context's arithmetic, as isd_step runs it.
+ *   dtype    ISD_BF16 (MFMA path, X bf16 row-major, W and W2 bf16 packed by isd_pack_weights)
+ *            or ISD_F32 (W row-major)
  *   mode     ISD_GEMM_STORE: Y act [M, N]; ISD_GEMM_STORE_F32: Y float [M, N];
  *            ISD_GEMM_RESID: R float [M, N] += X W^T;
  *            ISD_GEMM_SWIGLU: Y act [M, N] = silu(X W^T) * (X W2^T), W2 [N, K]

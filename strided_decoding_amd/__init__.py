@@ -8,7 +8,7 @@ from ._abi import EXPORTS, LIB_PATH, IsdError, load  # noqa: F401
 
 
 def __getattr__(name):
-    if name in ("Engine", "attn_paged", "sample", "gemm"):
+    if name in ("Engine", "attn_paged", "sample", "gemm", "pack_weight", "PackedWeight"):
         from . import engine
         return getattr(engine, name)
     raise AttributeError(name)

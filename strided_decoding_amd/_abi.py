@@ -20,7 +20,8 @@ ISD_SLOT_EMPTY, ISD_SLOT_A, ISD_SLOT_B, ISD_SLOT_DONE = 0, 1, 2, 3
 # symbols the header declares (checked by the CPU test-suite)
 EXPORTS = ("isd_init", "isd_prefill", "isd_step", "isd_get_buffers", "isd_get_status", "isd_release",
            "isd_attn_workspace_bytes", "isd_attn_paged", "isd_sample_workspace_bytes", "isd_sample",
-           "isd_version", "isd_profile", "isd_profile_report", "isd_gemm", "isd_gemm_splits", "isd_set_graphs")
+           "isd_version", "isd_profile", "isd_profile_report", "isd_gemm", "isd_gemm_splits", "isd_set_graphs",
+           "isd_packed_weight_bytes", "isd_pack_weights")
 
 ISD_GEMM_STORE, ISD_GEMM_STORE_F32, ISD_GEMM_RESID, ISD_GEMM_SWIGLU = 0, 1, 2, 3
 
@@ -123,6 +124,9 @@ def load(path=LIB_PATH):
     lib.isd_gemm.restype = C.c_int
     lib.isd_gemm_splits.argtypes = [C.c_int32, C.c_int32, C.c_int32]
     lib.isd_gemm_splits.restype = C.c_int32
+    lib.isd_packed_weight_bytes.argtypes = [C.c_int32, C.c_int32]
+    lib.isd_packed_weight_bytes.restype = C.c_size_t
+    lib.isd_pack_weights.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p]
     lib.isd_profile.argtypes = [C.c_void_p, C.c_int32]
     lib.isd_set_graphs.argtypes = [C.c_void_p, C.c_int32]
     lib.isd_profile_report.argtypes = [C.c_void_p, C.POINTER(ProfEntry), C.c_int32, C.POINTER(C.c_int32)]

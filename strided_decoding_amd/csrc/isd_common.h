@@ -120,6 +120,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
+// Wait until every LDS read (and scalar load) of this wave has returned.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14)); }
+
 struct AttnItem {              // query rows row0 .. row0+nq-1 of one slot at positions pos0 ..
   int32_t slot, row0, nq, pos0;
 };
@@ -191,6 +194,10 @@ int gemm_splits(int n_out, int K, bool dual);
 namespace isd {
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
+// bf16 weights of the GEMMs are in the packed operand layout (k_gemm.hip): elements of a
+// packed [rows, cols] matrix, and the conversion from row-major
+size_t packed_weight_elems(int rows, int cols);
+hipError_t launch_pack_weights(const void* src, void* dst, int rows, int cols, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
 
 struct AttnArgs {

@@ -895,6 +895,19 @@ isd_status isd_gemm(const isd_gemm_args* a, void* stream) {
   return ISD_OK;
 }
 
+size_t isd_packed_weight_bytes(int32_t rows, int32_t cols) {
+  if (rows < 1 || cols < 16 || cols % 16) return 0;
+  return packed_weight_elems(rows, cols) * sizeof(uint16_t);
+}
+
+isd_status isd_pack_weights(const void* src, void* dst, int32_t rows, int32_t cols, void* stream) {
+  if (!src || !dst || src == dst) return ISD_E_ARG;
+  if ((((uintptr_t)src) | ((uintptr_t)dst)) % 16) return ISD_E_ARG;
+  if (rows < 1 || cols < 16 || cols % 16) return ISD_E_SHAPE;
+  HIP_OK(launch_pack_weights(src, dst, rows, cols, (hipStream_t)stream));
+  return ISD_OK;
+}
+
 size_t isd_sample_workspace_bytes(int32_t batch, int32_t rows, int32_t vocab, int32_t q_rows) {
   const int nc = cdiv(vocab, kStatChunk);
   return align_up((size_t)batch * rows * nc * sizeof(ChunkStat)) +

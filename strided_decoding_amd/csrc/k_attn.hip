@@ -40,9 +40,6 @@ constexpr int kAttnBufs = ISD_ATTN_NBUF;
 ISD_DEV u32x4_t ld16(const uint16_t* p) { return *(const u32x4_t*)p; }
 ISD_DEV u32x4_t lds16(const uint8_t* p) { return *(const u32x4_t*)p; }
 
-// Wait until no LDS (or scalar-memory) access of this wave is outstanding.
-ISD_DEV void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14)); }
-
 // One workgroup per (item, KV head, context split); wave w handles the 16 query columns
 // 16 w .. 16 w + 15 of the KV-head group and 16/NCB of the 16 loads of each KV block.
 template <int NCB, int NBUF>

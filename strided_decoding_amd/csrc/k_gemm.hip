@@ -2,18 +2,21 @@
 // (bf16 store, fp32 store, fp32 residual add, SwiGLU of a gate/up pair) and the MASK-row
 // LoRA delta.
 //
-// bf16 path: one 224 x 256 output tile per workgroup (4 waves side by side, each 224 x 64 =
-// 7 x 2 MFMA 32x32x16 tiles, 224 accumulators per lane).  224 = 448 / 2 makes the decode row count
-// (64 slots x 7 rows) exactly two row tiles.  K is streamed in 32-wide stages through a
-// 4-deep LDS ring filled by direct global->LDS loads (16 bytes per lane), so no staging
-// registers are needed and three stages are in flight while one is consumed.  Each 64-byte
-// LDS row keeps its four 16-byte k-chunks XOR-swizzled by (row/4)%4 so that the 16 rows an
-// MFMA operand read touches fall in distinct banks.
-// Split-K (decode row counts only): split s covers k-stages [s kt, (s+1) kt) and writes fp32
-// partials that splitk_reduce_kernel sums in split order - no atomics - so every output
-// element has a fixed accumulation order that depends only on K and the split count, never
-// on the number of rows.  Workgroup ids are ordered so that the row tiles sharing a weight
-// tile differ by a multiple of 8 and run on the same XCD (one L2).
+// bf16 path: the weights are in a packed operand layout (the B operand of one 32x32x16 MFMA
+// is one contiguous kilobyte), so every weight load is a full-rate contiguous 1 KB access.
+// Tiled kernel (more than 128 rows): one 224 x 256 output tile per workgroup of 4 waves, one
+// wave per SIMD, each 224 x 64 = 7 x 2 MFMA tiles (224 accumulators in AGPRs).  224 = 448 / 2
+// makes the decode row count (64 slots x 7 rows) exactly two row tiles.  The activation tile
+// is streamed in 32-wide k stages through a 10-deep LDS ring filled by direct global->LDS
+// loads and shared by the four waves; each wave loads its own weight operands straight into a
+// 4-stage register ring.  Each 64-byte LDS row keeps its four 16-byte k-chunks XOR-swizzled by
+// (row/4)%4 so that the 16 rows an MFMA operand read touches fall in distinct banks.
+// Skinny kernel (at most 128 rows): single-wave workgroups streaming 64 weight columns.
+// Split-K: split s covers k-stages [s kt, (s+1) kt) and writes fp32 partials that
+// splitk_reduce_kernel sums in split order - no atomics - so every output element has a fixed
+// accumulation order that depends only on K and the split count, never on the number of rows.
+// Workgroup ids are ordered so that the row tiles sharing a weight tile differ by a multiple
+// of 8 and run on the same XCD (one L2).
 // fp32 path: LDS-tiled FMA, same epilogues.
 #include <algorithm>
 
@@ -24,21 +27,42 @@ namespace {
 
 constexpr int BK = 32;            // k per pipeline stage (one MFMA k-step)
 constexpr int TM2 = 224, TN2 = 256;
-constexpr int NST = 5;            // LDS ring depth (5 x 30 KB)
 constexpr int GROUP_BYTES = 16 * BK * 2;                 // 16 rows x 64 B
-#ifndef ISD_SKINNY_STAGES_1
-#define ISD_SKINNY_STAGES_1 10
-#endif
-#ifndef ISD_SKINNY_STAGES_2
-#define ISD_SKINNY_STAGES_2 8
-#endif
-#ifndef ISD_SKINNY_STAGES_4
-#define ISD_SKINNY_STAGES_4 5
-#endif
+constexpr int AG = TM2 / 16;              // A row groups of 16 rows per tile
+constexpr int kALoads = 4;                // A loads per wave and stage (4 waves x 4 >= 14 groups)
+constexpr int kNsA = 10;                  // A ring depth (10 x 14 KB)
+constexpr int kAStage = AG * GROUP_BYTES;
+constexpr int kBRing = 4;                 // B operands: a register ring of this many stages,
+constexpr int kBDepth = kBRing - 1;       // loaded this many stages ahead
+constexpr int kEpiLds = 4 * 128 * 68 * 4; // epilogue staging: 4 waves x 128 rows x 68 floats
+constexpr int kBigLds = kNsA * kAStage > kEpiLds ? kNsA * kAStage : kEpiLds;
+static_assert(kBDepth <= kNsA - 2, "the B wait must cover the A wait");
 // LDS ring depth of the skinny kernel for one / two / four 32-row tiles
-constexpr int kSkinnyStages1 = ISD_SKINNY_STAGES_1, kSkinnyStages2 = ISD_SKINNY_STAGES_2,
-              kSkinnyStages4 = ISD_SKINNY_STAGES_4;
-constexpr int STAGE_BYTES = (TM2 + TN2) / 16 * GROUP_BYTES;  // 30 KB
+#ifndef ISD_SK_SD1
+#define ISD_SK_SD1 8
+#endif
+#ifndef ISD_SK_SD2
+#define ISD_SK_SD2 8
+#endif
+#ifndef ISD_SK_SD4
+#define ISD_SK_SD4 4
+#endif
+
+// Packed weight layout of the bf16 path: the B operand of one 32x32x16 MFMA is 1 KB contiguous.
+// Block (nb, kb) holds rows 32 nb .. 32 nb + 31 and k = 16 kb .. 16 kb + 15; its lane l part
+// (16 bytes) is row 32 nb + l%32, k = 16 kb + 8 (l/32) .. + 7, at element
+// ((nb (K/16) + kb) 64 + l) 8.  Rows are padded with zeros to a multiple of 32.
+__device__ __forceinline__ const uint16_t* packed_operand(const uint16_t* p, int nb, int K, int kb, int lane) {
+  return p + ((size_t)nb * (K / 16) + kb) * 512 + lane * 8;
+}
+// (a global-memory load: p points into device memory, never LDS or scratch)
+__device__ __forceinline__ bf16x8_t ld_operand(const uint16_t* p) {
+  return as_bf16x8(*(const __attribute__((address_space(1))) u32x4_t*)p);
+}
+
+// 1 KB of zeros: the operands of the padding stages that round a split's stage count up to a
+// whole number of operand-ring rounds (0 x 0 products leave every accumulator unchanged).
+__device__ __attribute__((aligned(1024))) uint16_t kZeroOperand[512] = {};
 
 template <typename T, int EPI>
 __device__ __forceinline__ void epilogue_store_t(const GemmArgs& a, int row, int col, float v, float v_up) {
@@ -72,12 +96,11 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_
 }
 
 template <int EPI, bool PARTIAL>
-__global__ __launch_bounds__(512) void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU);
   constexpr int TNO = DUAL ? TN2 / 2 : TN2;
-  constexpr int AG = TM2 / 16;                    // 14 A row groups of 16 rows
-  constexpr int NG = (TM2 + TN2) / 16;            // 30 row groups per stage
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kBigLds];
 
   const int id = blockIdx.x;
   const int grp = id / (8 * n_mt), rem = id % (8 * n_mt);
@@ -86,152 +109,169 @@ __global__ __launch_bounds__(512) void gemm_bf16_big_kernel(GemmArgs a, int n_mt
   const int nt = unit / S, sp = unit % S;
   const int kt_per = (a.K / BK) / S;
   const int kbase = sp * kt_per * BK;
+  // the stage count is rounded up to whole ring rounds with zero stages (indices >= kt_per
+  // load kZeroOperand)
+  const int kt_loop = (kt_per + kBRing - 1) / kBRing * kBRing;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = nt * TNO, m0 = mt * TM2;
+  const uint16_t* zero = kZeroOperand + lane * 8;
 
-  // Loader: wave w fills row groups w, w+8, w+16, min(w+24, 29) of the 30 (A groups 0..13,
-  // then the B groups; waves 6 and 7 both refill group 29 with the same bytes, so every wave
-  // issues 4 loads per stage).  Lane l writes LDS bytes [16 l, 16 l + 16) of its group: row l/4, slot l%4,
-  // which holds k-chunk (l%4) ^ ((row/4)%4) of that row.  B block t (rows 32t .. 32t+31 of
-  // the tile) is wave t's operand; for SwiGLU the blocks alternate gate and up rows of the
-  // same 32 output columns (block t: matrix t%2, outputs 32 (t/2) ..).
+  // A loader: wave w fills row groups min(w + 4 i, 13), i < 4, of the 14 (waves 1-3 all refill
+  // group 13 with the same bytes, so every wave issues 4 loads per stage).  Lane l writes LDS
+  // bytes [16 l, 16 l + 16) of its group: row l/4, slot l%4, which holds k-chunk
+  // (l%4) ^ ((row/4)%4) of that row.
   const int lrow = lane >> 2;
   const int chunk = (lane & 3) ^ ((lrow >> 2) & 3);
   const int aoff = gemm_seg_aoff(a, n0);
-  const uint16_t* src[4];
+  const uint16_t* asrc[kALoads];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int g = min(wave + 8 * i, NG - 1);
-    if (g < AG) {
-      const int m = m0 + g * 16 + lrow;
-      int srow = 0;
-      if (m < a.M) {
-        srow = a.a_rows ? a.a_rows[m] : m;
-        if (srow < 0) srow = 0;          // unused row (its outputs are never consumed)
-      }
-      src[i] = (const uint16_t*)a.A + (size_t)srow * a.lda + aoff + kbase + chunk * 8;
-    } else {
-      const int bg = g - AG;                      // B row group 0..15
-      const uint16_t* bm = (const uint16_t*)a.B0;
-      int n;
-      if (DUAL) {
-        const int blk = bg >> 1;
-        if (blk & 1) bm = (const uint16_t*)a.B1;
-        n = n0 + (blk >> 1) * 32 + (bg & 1) * 16 + lrow;
-      } else {
-        n = n0 + bg * 16 + lrow;
-      }
-      n = min(n, a.N - 1);
-      src[i] = bm + (size_t)n * a.ldb + kbase + chunk * 8;
+  for (int i = 0; i < kALoads; ++i) {
+    const int m = m0 + min(wave + 4 * i, AG - 1) * 16 + lrow;
+    int srow = 0;
+    if (m < a.M) {
+      srow = a.a_rows ? a.a_rows[m] : m;
+      if (srow < 0) srow = 0;            // unused row (its outputs are never consumed)
     }
+    asrc[i] = (const uint16_t*)a.A + (size_t)srow * a.lda + aoff + kbase + chunk * 8;
   }
-  // Stage kt goes to ring slot kt % NST.  Every step issues exactly one stage (past the last
-  // stage it re-loads the last one into the slot just freed, which is never read again), so
-  // the number of loads in flight is the same at every wait.
-  auto issue = [&](int kt, int slot) {
-    uint8_t* st = smem + slot * STAGE_BYTES;
-    const int koff = kt * BK;
+  // B: this wave's two 32-row operand blocks, straight from the packed weights into registers
+  // (one contiguous 1 KB operand per k-step and block).  Block j is output columns
+  // n0 + 64 w + 32 j .. (SwiGLU: gate block j = 0 and up block j = 1 of columns n0 + 32 w ..).
+  const uint16_t* bsrc[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(src[i] + koff),
-                                       (lds_void*)(st + min(wave + 8 * i, NG - 1) * GROUP_BYTES), 16, 0, 0);
+  for (int j = 0; j < 2; ++j) {
+    int nb = DUAL ? (n0 >> 5) + wave : (n0 >> 5) + 2 * wave + j;
+    nb = min(nb, ((a.N + 31) >> 5) - 1);        // past the last block: outputs are discarded
+    bsrc[j] = packed_operand((const uint16_t*)(DUAL && j ? a.B1 : a.B0), nb, a.K, kbase / 16, lane);
+  }
+  auto a_dma = [&](int i, uint8_t* st, int kt) {
+    __builtin_amdgcn_global_load_lds((const void*)(kt < kt_per ? asrc[i] + kt * BK : zero),
+                                     (lds_void*)(st + min(wave + 4 * i, AG - 1) * GROUP_BYTES), 16, 0, 0);
   };
-
-  f32x16_t acc[7];
+  // operand ring: stage kt's B fragments in slot kt % kBRing, loaded kBDepth stages ahead
+  bf16x8_t bq[kBRing][2][2];
+  auto b_load = [&](int slot, int kt) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) bq[slot][j][kk] = ld_operand(kt < kt_per ? bsrc[j] + (2 * kt + kk) * 512 : zero);
+  };
+  f32x16_t acc[7][2];
 #pragma unroll
   for (int i = 0; i < 7; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  for (int s = 0; s < NST - 1; ++s) issue(min(s, kt_per - 1), s);
+  // The loads follow a fixed pattern: pipeline step i issues 4 A loads (stage i + kNsA - 1)
+  // and then 4 B loads (stage i + kBDepth), and the prologue is the same pattern for the steps
+  // i = 1 - kNsA .. -1 without the B loads of negative stages.  Stages past the last one load
+  // zeros, so the pattern never changes: before step kt reads B stage kt exactly
+  // 8 (kBDepth - 1) loads were issued after it, and at least as many after A stage kt+1
+  // because kBDepth <= kNsA - 2.
+#pragma unroll
+  for (int i = 1 - kNsA; i < 0; ++i) {
+    const int sa = i + kNsA - 1, sb = i + kBDepth;
+#pragma unroll
+    for (int q = 0; q < kALoads; ++q) a_dma(q, smem + sa * kAStage, sa);
+    if (sb >= 0) b_load(sb, sb);
+  }
 
-  // operand read: row (lane%32) of a 32-row block, k-chunk 2 kk + lane/32 (swizzled)
+  // A operand read: row (lane%32) of a 32-row block, k-chunk 2 kk + lane/32 (swizzled)
   const int rig = lane & 15, half = (lane >> 4) & 1, khi = lane >> 5;
   const int rd0 = rig * (BK * 2) + half * GROUP_BYTES;
   const int sw = (rig >> 2) & 3;
-  // frags of k-step kk of stage kt: 7 A blocks and this wave's B block
-  auto read_frags = [&](int kt, int kk, bf16x8_t* af, bf16x8_t& bf) {
-    const uint8_t* st = smem + (kt % NST) * STAGE_BYTES;
-    const int off = rd0 + (((2 * kk + khi) ^ sw) * 16);
-    bf = as_bf16x8(*(const u32x4_t*)(st + (AG + 2 * wave) * GROUP_BYTES + off));
-#pragma unroll
-    for (int i = 0; i < 7; ++i) af[i] = as_bf16x8(*(const u32x4_t*)(st + (2 * i) * GROUP_BYTES + off));
+  auto frag = [&](int kt, int kk, int i) {
+    const uint8_t* st = smem + (kt % kNsA) * kAStage;
+    return as_bf16x8(*(const u32x4_t*)(st + 2 * i * GROUP_BYTES + rd0 + (((2 * kk + khi) ^ sw) * 16)));
   };
 
-  bf16x8_t a0[7], a1[7], b0, b1;
-  wait_vmcnt<4 * (NST - 2)>();                     // stage 0 has landed
+  bf16x8_t x0[7], x1[7];
+  wait_vmcnt<8 * (kBDepth - 1)>();                 // A stage 0 and B stage 0 have landed
   __builtin_amdgcn_s_barrier();
-  read_frags(0, 0, a0, b0);
-  // One pipeline step: make stage kt+1 visible (stages kt+2 .. kt+NST-2 stay in flight), then
-  // multiply stage kt's k-step 0 while reading its k-step 1, refill the slot of stage kt-1
-  // (every wave finished it before the barrier) and multiply k-step 1 while reading stage
-  // kt+1's k-step 0.  The loads are interleaved with the MFMAs so that a stalled load issue
-  // does not leave the matrix unit idle.
-  for (int kt = 0; kt < kt_per; ++kt) {
-    wait_vmcnt<4 * (NST - 3)>();
-    __builtin_amdgcn_s_barrier();        // no fence: the later stages' loads stay in flight
-    {
-      const uint8_t* st = smem + (kt % NST) * STAGE_BYTES;
-      const int off = rd0 + (((2 + khi) ^ sw) * 16);                   // k-step 1 of stage kt
-      uint8_t* dst = smem + ((kt + NST - 1) % NST) * STAGE_BYTES;
-      const int koff = min(kt + NST - 1, kt_per - 1) * BK;
 #pragma unroll
-      for (int i = 0; i < 7; ++i) {
-        acc[i] = mfma32x32x16(a0[i], b0, acc[i]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (i == 0) b1 = as_bf16x8(*(const u32x4_t*)(st + (AG + 2 * wave) * GROUP_BYTES + off));
-        a1[i] = as_bf16x8(*(const u32x4_t*)(st + (2 * i) * GROUP_BYTES + off));
-        if (i < 4)
-          __builtin_amdgcn_global_load_lds((const void*)(src[i] + koff),
-                                           (lds_void*)(dst + min(wave + 8 * i, NG - 1) * GROUP_BYTES), 16, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+  for (int i = 0; i < 7; ++i) x0[i] = frag(0, 0, i);
+  wait_lgkm0();
+  // One pipeline step per 32-k stage kt: make A stage kt+1 visible, then two halves of 14
+  // MFMAs.  One wave per SIMD keeps the matrix unit fed by itself: the MFMAs are interleaved
+  // with the LDS reads of the next k-step's A operands, the refill of the A slot of stage kt-1
+  // (every wave finished it before the barrier) and the B loads of stage kt+kBDepth into the
+  // ring slot of stage kt-1; a half ends by waiting for its LDS reads.
+  for (int kt0 = 0; kt0 < kt_loop; kt0 += kBRing) {
+#pragma unroll
+    for (int d = 0; d < kBRing; ++d) {
+      const int kt = kt0 + d;
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<8 * (kBDepth - 1)>();   // B stage kt and A stage kt+1 have landed
+      __builtin_amdgcn_s_barrier();      // no fence: the later stages' loads stay in flight
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        uint8_t* dst = smem + ((kt + kNsA - 1) % kNsA) * kAStage;
+        const int ka = kt + kNsA - 1, kb = kt + kBDepth;
+        const int nslot = (d + kBDepth) % kBRing;     // a constant once the loop is unrolled
+#pragma unroll
+        for (int m = 0; m < 14; ++m) {
+          acc[m >> 1][m & 1] = mfma32x32x16(x0[m >> 1], bq[d][m & 1][0], acc[m >> 1][m & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (m < 7) x1[m] = frag(kt, 1, m);
+          if (m >= 1 && m <= kALoads) a_dma(m - 1, dst, ka);
+          if (m >= 6 && m < 10) {
+            const int j = (m - 6) >> 1, kk = (m - 6) & 1;
+            bq[nslot][j][kk] = ld_operand(kb < kt_per ? bsrc[j] + (2 * kb + kk) * 512 : zero);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-    }
-    read_frags(kt + 1 < kt_per ? kt + 1 : kt, 0, a0, b0);
+      wait_lgkm0();
+      {
+        const int kn = kt + 1;                            // past the end: a slot of zeros
 #pragma unroll
-    for (int i = 0; i < 7; ++i) acc[i] = mfma32x32x16(a1[i], b1, acc[i]);
-#pragma unroll
-    for (int g = 0; g < 7; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        for (int m = 0; m < 14; ++m) {
+          acc[m >> 1][m & 1] = mfma32x32x16(x1[m >> 1], bq[d][m & 1][1], acc[m >> 1][m & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (m < 7) x0[m] = frag(kn, 0, m);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      wait_lgkm0();
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
-  wait_vmcnt<0>();                                 // the re-loads past the last stage
+  wait_vmcnt<0>();                                 // the loads past the last stage
 
-  // Epilogue through LDS: each wave's 224 x 32 fp32 tile is staged row-major (rows padded to
-  // 36 floats) in two halves (blocks 0-3, then 4-6), then written out in 16-byte row chunks.
-  // Accumulator register r of block i in lane l is tile row 32 i + 8 (r/4) + 4 (l/32) + r%4,
-  // column l%32.
+  // Epilogue through LDS: each wave's 224 x 64 fp32 tile is staged row-major (rows padded to
+  // 68 floats) in two halves (row blocks 0-3, then 4-6), then written out in 16-byte chunks.
+  // Accumulator register r of block (i, j) in lane l is tile row 32 i + 8 (r/4) + 4 (l/32) + r%4,
+  // column 32 j + l%32.  For SwiGLU columns 0-31 are the gate and 32-63 the up product.
   __syncthreads();                                 // every wave is done with the ring
-  constexpr int LD = 36;
+  constexpr int LD = 68;
   float* tile = (float*)smem + (size_t)wave * (128 * LD);
   const int cl = lane & 31;
-  const int wcol = DUAL ? n0 + 32 * (wave >> 1) : n0 + 32 * wave;   // first output column of this wave
+  const int wcol = n0 + (DUAL ? 32 : 64) * wave;   // first output column of this wave
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int i0 = 4 * h, nb = h ? 3 : 4, r0 = m0 + 128 * h;
+    if (h) __syncthreads();                        // the first half has been written out
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (i >= nb) break;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) tile[(32 * i + 8 * (r >> 2) + 4 * khi + (r & 3)) * LD + cl] = acc[i0 + i][r];
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          tile[(32 * i + 8 * (r >> 2) + 4 * khi + (r & 3)) * LD + 32 * j + cl] = acc[i0 + i][j][r];
     }
+    __syncthreads();
     if (DUAL && !PARTIAL) {
-      __syncthreads();                             // the partner wave's tile is staged too
-      // pair p = wave/2: gate tile in wave 2p, up tile in wave 2p+1; the two waves split the rows
-      const float* gt = (const float*)smem + (size_t)(wave & ~1) * (128 * LD);
-      const float* ut = gt + 128 * LD;
-      const int rows_h = nb * 32, rbeg = (wave & 1) * (rows_h / 2);
-      for (int q = lane; q < (rows_h / 2) * 4; q += 64) {
-        const int tr = rbeg + (q >> 2), c8 = (q & 3) * 8, row = r0 + tr, col = wcol + c8;
+      for (int q = lane; q < nb * 32 * 4; q += 64) {
+        const int tr = q >> 2, c8 = (q & 3) * 8, row = r0 + tr, col = wcol + c8;
         if (row >= a.M || col >= a.N) continue;
         float g[8], u[8];
-        *(f32x4_t*)&g[0] = *(const f32x4_t*)&gt[tr * LD + c8];
-        *(f32x4_t*)&g[4] = *(const f32x4_t*)&gt[tr * LD + c8 + 4];
-        *(f32x4_t*)&u[0] = *(const f32x4_t*)&ut[tr * LD + c8];
-        *(f32x4_t*)&u[4] = *(const f32x4_t*)&ut[tr * LD + c8 + 4];
+        *(f32x4_t*)&g[0] = *(const f32x4_t*)&tile[tr * LD + c8];
+        *(f32x4_t*)&g[4] = *(const f32x4_t*)&tile[tr * LD + c8 + 4];
+        *(f32x4_t*)&u[0] = *(const f32x4_t*)&tile[tr * LD + 32 + c8];
+        *(f32x4_t*)&u[4] = *(const f32x4_t*)&tile[tr * LD + 32 + c8 + 4];
         const int dr = a.delta_row ? a.delta_row[row] : -1;
         uint32_t pk[4];
 #pragma unroll
@@ -253,10 +293,9 @@ __global__ __launch_bounds__(512) void gemm_bf16_big_kernel(GemmArgs a, int n_mt
           for (int j = 0; j < 8 && col + j < a.N; ++j) dst[j] = (uint16_t)(pk[j >> 1] >> (16 * (j & 1)));
         }
       }
-      __syncthreads();                             // both tiles are read before the next half
     } else if (!PARTIAL && EPI == EPI_STORE) {
-      for (int q = lane; q < nb * 32 * 4; q += 64) {
-        const int tr = q >> 2, c8 = (q & 3) * 8, row = r0 + tr, col = wcol + c8;
+      for (int q = lane; q < nb * 32 * 8; q += 64) {
+        const int tr = q >> 3, c8 = (q & 7) * 8, row = r0 + tr, col = wcol + c8;
         if (row >= a.M || col >= a.N) continue;
         float v[8];
         *(f32x4_t*)&v[0] = *(const f32x4_t*)&tile[tr * LD + c8];
@@ -279,12 +318,14 @@ __global__ __launch_bounds__(512) void gemm_bf16_big_kernel(GemmArgs a, int n_mt
       }
     } else {
       // fp32 outputs: split-K partials (raw sums), fp32 store or residual add (with delta)
-      for (int q = lane; q < nb * 32 * 8; q += 64) {
-        const int tr = q >> 3, c4 = (q & 7) * 4, row = r0 + tr, col = wcol + c4;
+      for (int q = lane; q < nb * 32 * 16; q += 64) {
+        const int tr = q >> 4, c4 = (q & 15) * 4, row = r0 + tr;
+        // SwiGLU partials: columns 0-31 of the tile are gate sums, 32-63 up sums
+        const int col = DUAL ? wcol + (c4 & 31) : wcol + c4;
         if (row >= a.M || col >= a.N) continue;
         f32x4_t v = *(const f32x4_t*)&tile[tr * LD + c4];
         if (PARTIAL) {
-          float* dst = DUAL ? part + ((size_t)sp * a.M + row) * (2 * (size_t)a.N) + (wave & 1) * a.N + col
+          float* dst = DUAL ? part + ((size_t)sp * a.M + row) * (2 * (size_t)a.N) + (c4 >> 5) * a.N + col
                             : part + ((size_t)sp * a.M + row) * (size_t)a.N + col;
           *(f32x4_t*)dst = v;
         } else {
@@ -304,19 +345,20 @@ __global__ __launch_bounds__(512) void gemm_bf16_big_kernel(GemmArgs a, int n_mt
 
 // Skinny path for at most 128 rows (decode at small batch, where a projection is bound by
 // streaming its weights from HBM).  One single-wave workgroup per (output-column group, K
-// split); no barriers.  The wave streams its weight rows and the (L2-resident) activation
-// rows through a private SD-stage LDS ring filled by direct global->LDS loads, with the loads
-// of SD-1 stages in flight under explicit vmcnt waits while one stage is multiplied.  The MFMA (32x32x16), the k-chunk held by each lane, the k-step order, the split
-// rule and the partial layout are those of the tiled kernel, so every output element is
-// accumulated in exactly the same order and the two paths give bit-identical results.
+// split); no barriers.  The wave streams its packed weight operands (one contiguous 1 KB
+// direct load per block and k-step) and the (L2-resident) activation rows through a private
+// SD-stage LDS ring filled by direct global->LDS loads, with the loads of SD-1 stages in flight
+// under explicit vmcnt waits while one stage is multiplied.  The MFMA (32x32x16), the k-chunk
+// held by each lane, the k-step order, the split rule and the partial layout are those of the
+// tiled kernel, so every output element is accumulated in exactly the same order and the two
+// paths give bit-identical results.
 template <int EPI, bool PARTIAL, int MT, int SD>
 __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_nt, int S, float* part) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU);
   constexpr int NB = 2;                     // 32-column MFMA tiles per wave (gate + up for SwiGLU)
   constexpr int TNO = DUAL ? 32 : 64;       // output columns per wave
-  constexpr int OPS = MT + NB;              // operand tiles per 16-k step
-  constexpr int STAGE = OPS * 2 * 1024;     // bytes per 32-k stage: OPS tiles x 2 row groups x 1 KB
-  constexpr int PER_STAGE = OPS * 2;        // direct loads per stage
+  constexpr int STAGE = (MT + NB) * 2048;   // bytes per 32-k stage: activation tiles, then weight operands
+  constexpr int PER_STAGE = 2 * (MT + NB);  // direct loads per stage
   static_assert((SD - 1) * PER_STAGE < 64, "vmcnt counts at most 63 outstanding loads");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SD * STAGE];
   const int lane = threadIdx.x;
@@ -326,15 +368,15 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_
   const int kbase = sp * kt_per * BK;
   const int n0 = nt * TNO;
   const int r32 = lane & 31, khi = lane >> 5;
+  const uint16_t* zero = kZeroOperand + lane * 8;
 
-  // Loader (the tiled kernel's 16-row group layout): one direct load per 16-row group and
-  // stage; lane l fills LDS bytes [16 l, 16 l + 16) of the group with row l/4, k-chunk
-  // (l%4) ^ ((row/4)%4), so every instruction reads 64 contiguous bytes of 16 rows and the
-  // operand reads below are free of bank conflicts.
+  // Activation loader (the tiled kernel's 16-row group layout): one direct load per 16-row
+  // group and stage; lane l fills LDS bytes [16 l, 16 l + 16) of the group with row l/4,
+  // k-chunk (l%4) ^ ((row/4)%4), so the operand reads below are free of bank conflicts.
   const int lrow = lane >> 2;
   const int chunk = (lane & 3) ^ ((lrow >> 2) & 3);
   const int aoff = gemm_seg_aoff(a, n0);
-  const uint16_t* src[OPS][2];
+  const uint16_t* xsrc[MT][2];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -345,28 +387,34 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_
         srow = a.a_rows ? a.a_rows[m] : m;
         if (srow < 0) srow = 0;               // unused row (its outputs are never consumed)
       }
-      src[i][g] = (const uint16_t*)a.A + (size_t)srow * a.lda + aoff + kbase + chunk * 8;
+      xsrc[i][g] = (const uint16_t*)a.A + (size_t)srow * a.lda + aoff + kbase + chunk * 8;
     }
+  // weight operand blocks: columns n0 + 32 j .. (SwiGLU: gate j = 0 and up j = 1 of n0 ..)
+  const uint16_t* wsrc[NB];
 #pragma unroll
-  for (int j = 0; j < NB; ++j)
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const uint16_t* bm = (const uint16_t*)((DUAL && j) ? a.B1 : a.B0);
-      const int r = 16 * g + lrow;
-      const int n = min(DUAL ? n0 + r : n0 + 32 * j + r, a.N - 1);
-      src[MT + j][g] = bm + (size_t)n * a.ldb + kbase + chunk * 8;
-    }
+  for (int j = 0; j < NB; ++j) {
+    const int nb = min(DUAL ? (n0 >> 5) : (n0 >> 5) + j, ((a.N + 31) >> 5) - 1);
+    wsrc[j] = packed_operand((const uint16_t*)((DUAL && j) ? a.B1 : a.B0), nb, a.K, kbase / 16, lane);
+  }
 
-  // stage kt -> ring slot kt % SD; tile t, row group g at slot + (2 t + g) KB
+  // stage kt -> ring slot kt % SD: activation tile t, row group g at + (2 t + g) KB, then the
+  // weight operand of block j and k-step kk at + (2 MT + 2 j + kk) KB.  Stages past the last
+  // one load zeros.
   auto issue = [&](int kt) {
     uint8_t* st = smem + (kt % SD) * STAGE;
-    const int koff = kt * BK;
+    const bool live = kt < kt_per;
 #pragma unroll
-    for (int t = 0; t < OPS; ++t)
+    for (int t = 0; t < MT; ++t)
 #pragma unroll
       for (int g = 0; g < 2; ++g)
-        __builtin_amdgcn_global_load_lds((const void*)(src[t][g] + koff), (lds_void*)(st + (2 * t + g) * 1024), 16, 0,
-                                         0);
+        __builtin_amdgcn_global_load_lds((const void*)(live ? xsrc[t][g] + kt * BK : zero),
+                                         (lds_void*)(st + (2 * t + g) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        __builtin_amdgcn_global_load_lds((const void*)(live ? wsrc[j] + (2 * kt + kk) * 512 : zero),
+                                         (lds_void*)(st + (2 * MT + 2 * j + kk) * 1024), 16, 0, 0);
   };
   f32x16_t acc[MT][NB];
 #pragma unroll
@@ -375,38 +423,37 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  // operand of lane L: row r32 (group r32/16, row r32%16), k-chunk 2 kk + khi, swizzled
+  // activation operand of lane L: row r32 (group r32/16, row r32%16), k-chunk 2 kk + khi, swizzled
   const int rig = r32 & 15;
   const int rd0 = (r32 >> 4) * 1024 + rig * 64;
   const int sw = (rig >> 2) & 3;
   auto mul = [&](int kt) {
-    const uint8_t* st = smem + (kt % SD) * STAGE + rd0;
+    const uint8_t* st = smem + (kt % SD) * STAGE;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int off = ((2 * kk + khi) ^ sw) * 16;
-      bf16x8_t x[OPS];
+      bf16x8_t x[MT], w[NB];
 #pragma unroll
-      for (int t = 0; t < OPS; ++t) x[t] = as_bf16x8(*(const u32x4_t*)(st + 2 * t * 1024 + off));
+      for (int t = 0; t < MT; ++t) x[t] = as_bf16x8(*(const u32x4_t*)(st + rd0 + 2 * t * 1024 + off));
+#pragma unroll
+      for (int j = 0; j < NB; ++j) w[j] = as_bf16x8(*(const u32x4_t*)(st + (2 * MT + 2 * j + kk) * 1024 + lane * 16));
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = mfma32x32x16(x[i], x[MT + j], acc[i][j]);
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma32x32x16(x[i], w[j], acc[i][j]);
     }
   };
 
   // Stage kt is issued SD-1 steps before it is multiplied; before multiplying it, at most the
   // loads of the stages issued after it may be outstanding.
-  const int pro = min(SD - 1, kt_per);
-  for (int kt = 0; kt < pro; ++kt) issue(kt);
-  int kt = 0;
-  for (; kt + SD - 1 < kt_per; ++kt) {
+  for (int kt = 0; kt < SD - 1; ++kt) issue(kt);
+  for (int kt = 0; kt < kt_per; ++kt) {
     issue(kt + SD - 1);
     wait_vmcnt<(SD - 1) * PER_STAGE>();
     mul(kt);
     __builtin_amdgcn_sched_barrier(0);
   }
-  wait_vmcnt<0>();
-  for (; kt < kt_per; ++kt) mul(kt);
+  wait_vmcnt<0>();                               // the loads past the last stage
 
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
@@ -593,31 +640,34 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
   const int S = (a.splits > 1 && a.part) ? a.splits : 1;
   const int units = n_nt * S;
   dim3 grid(((units + 7) / 8) * 8 * n_mt);
+  // the full B ring when the stage count of a split allows it, else a two-stage ring
   if (S > 1)
-    hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, true>), grid, dim3(512), 0, s, a, n_mt, units, S, a.part);
+    hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, true>), grid, dim3(256), 0, s, a, n_mt, units, S, a.part);
   else
-    hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, false>), grid, dim3(512), 0, s, a, n_mt, units, 1, nullptr);
+    hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, false>), grid, dim3(256), 0, s, a, n_mt, units, 1, nullptr);
   return finish<EPI>(a, S, s);
 }
 
 template <int EPI>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
-  constexpr int SD1 = kSkinnyStages1, SD2 = kSkinnyStages2, SD4 = kSkinnyStages4;
   const int tno = EPI == EPI_SWIGLU ? 32 : 64;
   const int n_nt = (a.N + tno - 1) / tno;
   const int S = (a.splits > 1 && a.part) ? a.splits : 1;
   dim3 grid(n_nt * S);
   float* part = S > 1 ? a.part : nullptr;
+#define ISD_SKINNY(P, MT, SD) \
+  hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, P, MT, SD>), grid, dim3(64), 0, s, a, n_nt, S, part)
   if (a.M <= 32) {
-    if (S > 1) hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, true, 1, SD1>), grid, dim3(64), 0, s, a, n_nt, S, part);
-    else hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, false, 1, SD1>), grid, dim3(64), 0, s, a, n_nt, S, part);
+    if (S > 1) ISD_SKINNY(true, 1, ISD_SK_SD1);
+    else ISD_SKINNY(false, 1, ISD_SK_SD1);
   } else if (a.M <= 64) {
-    if (S > 1) hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, true, 2, SD2>), grid, dim3(64), 0, s, a, n_nt, S, part);
-    else hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, false, 2, SD2>), grid, dim3(64), 0, s, a, n_nt, S, part);
+    if (S > 1) ISD_SKINNY(true, 2, ISD_SK_SD2);
+    else ISD_SKINNY(false, 2, ISD_SK_SD2);
   } else {
-    if (S > 1) hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, true, 4, SD4>), grid, dim3(64), 0, s, a, n_nt, S, part);
-    else hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, false, 4, SD4>), grid, dim3(64), 0, s, a, n_nt, S, part);
+    if (S > 1) ISD_SKINNY(true, 4, ISD_SK_SD4);
+    else ISD_SKINNY(false, 4, ISD_SK_SD4);
   }
+#undef ISD_SKINNY
   return finish<EPI>(a, S, s);
 }
 
@@ -658,6 +708,34 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
     case EPI_SWIGLU: return launch_path<EPI_SWIGLU>(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Row-major bf16 W [rows, cols] -> the packed operand layout (rows padded with zeros to a
+// multiple of 32): thread e writes the 16 bytes of lane e%64 of operand block e/64.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* src, uint16_t* dst, int rows, int cols,
+                                                           size_t n16) {
+  const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n16) return;
+  const int lane = (int)(e & 63);
+  const size_t blk = e >> 6;
+  const int kbn = cols / 16;
+  const int kb = (int)(blk % kbn);
+  const size_t nb = blk / kbn;
+  const size_t row = nb * 32 + (lane & 31);
+  const int k0 = kb * 16 + 8 * (lane >> 5);
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (row < (size_t)rows) v = *(const u32x4_t*)(src + row * cols + k0);
+  *(u32x4_t*)(dst + e * 8) = v;
+}
+
+size_t packed_weight_elems(int rows, int cols) { return (size_t)((rows + 31) / 32) * 32 * cols; }
+
+hipError_t launch_pack_weights(const void* src, void* dst, int rows, int cols, hipStream_t s) {
+  if (rows < 1 || cols < 16 || cols % 16) return hipErrorInvalidValue;
+  const size_t n16 = packed_weight_elems(rows, cols) / 8;
+  hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s, (const uint16_t*)src,
+                     (uint16_t*)dst, rows, cols, n16);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s) {

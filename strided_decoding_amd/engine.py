@@ -27,6 +27,37 @@ def to_device(a, dtype, device):
     return t.to(device=device, dtype=_dt(dtype)).contiguous()
 
 
+class PackedWeight:
+    """A bf16 weight [rows, cols] in the packed MFMA-operand layout of the bf16 GEMMs (see
+    isd_pack_weights); `data` is the device buffer, rows padded to a multiple of 32."""
+
+    def __init__(self, data, rows, cols):
+        self.data, self.rows, self.cols = data, rows, cols
+
+    def data_ptr(self):
+        return self.data.data_ptr()
+
+
+def pack_weight(W, stream=None):
+    """Row-major bf16 device tensor [rows, cols] -> PackedWeight (isd_pack_weights)."""
+    lib = A.load()
+    if W.dtype != torch.bfloat16 or W.dim() != 2:
+        raise TypeError("pack_weight takes a 2-D bfloat16 device tensor")
+    W = W.contiguous()
+    rows, cols = W.shape
+    nbytes = lib.isd_packed_weight_bytes(rows, cols)
+    if nbytes == 0:
+        raise ValueError(f"cannot pack a [{rows}, {cols}] weight (cols must be a positive multiple of 16)")
+    out = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=W.device)
+    stream = stream if stream is not None else torch.cuda.current_stream(W.device)
+    A.check("isd_pack_weights", lib.isd_pack_weights(W.data_ptr(), out.data_ptr(), rows, cols,
+                                                     C.c_void_p(stream.cuda_stream)))
+    return PackedWeight(out, rows, cols)
+
+
+PACKED = ("wqkv", "wo", "wg", "wu", "wd")
+
+
 class Engine:
     """One decoding context: weights, KV pool and workspace resident on `device`.
 
@@ -59,8 +90,13 @@ class Engine:
         self.cfg = cfg
         # weights (kept alive by this object)
         dev = self.device
-        self.w = {k: to_device(weights[k], dt, dev) for k in ("embed", "final_norm", "lm_head")}
-        self.wl = [{k: to_device(v, dt, dev) for k, v in layer.items()} for layer in weights["layers"]]
+        bf = dt == "bf16"
+        # bf16 projection weights go to the library in the packed operand layout
+        pk = (lambda t: pack_weight(t, self.stream).data) if bf else (lambda t: t)
+        self.w = {k: to_device(weights[k], dt, dev) for k in ("embed", "final_norm")}
+        self.w["lm_head"] = pk(to_device(weights["lm_head"], dt, dev))
+        self.wl = [{k: pk(to_device(v, dt, dev)) if k in PACKED else to_device(v, dt, dev) for k, v in layer.items()}
+                   for layer in weights["layers"]]
         self.lora = None
         if lora is not None:
             # stacked per layer: A of (q, k, v) and of (gate, up) contiguous, and likewise B, so
@@ -71,7 +107,7 @@ class Engine:
                 for group in (("q", "k", "v"), ("o",), ("g", "u"), ("d",)):
                     for which in (0, 1):
                         parts = [to_device(layer[m][which], dt, dev) for m in group]
-                        flat = torch.cat([t.reshape(-1) for t in parts])
+                        flat = torch.cat([pk(t).reshape(-1) for t in parts])
                         off = 0
                         for m, t in zip(group, parts):
                             view = flat[off:off + t.numel()].view(t.shape)
@@ -233,17 +269,20 @@ GEMM_PATHS = {"auto": 0, "tiled": 1, "skinny": 2}
 
 def gemm(X, W, mode="store", W2=None, out=None, R=None, splits=0, workspace=None, stream=None,
          norm_g=None, norm_out=None, norm_eps=1e-6, path="auto"):
-    """Kernel-level projection (see isd_gemm): X [M, K], W [N, K] (bf16 or float32 on device).
+    """Kernel-level projection (see isd_gemm): X [M, K]; W [N, K] a PackedWeight for bf16
+    (pack_weight) or a float32 device tensor.
 
     mode "resid" with norm_g / norm_out also writes RMSNorm(R) * norm_g into norm_out.
     path: "auto", "tiled" or "skinny" (bf16 kernel choice; M <= 128 for skinny)."""
     lib = A.load()
     M, K = X.shape
-    N = W.shape[0]
+    bf = X.dtype == torch.bfloat16
+    if bf != isinstance(W, PackedWeight) or (W2 is not None and bf != isinstance(W2, PackedWeight)):
+        raise TypeError("bf16 products take PackedWeight operands (pack_weight), float32 ones plain tensors")
+    N = W.rows if bf else W.shape[0]
     modes = {"store": A.ISD_GEMM_STORE, "store_f32": A.ISD_GEMM_STORE_F32, "resid": A.ISD_GEMM_RESID,
              "swiglu": A.ISD_GEMM_SWIGLU}
     md = modes[mode]
-    bf = X.dtype == torch.bfloat16
     if out is None and md != A.ISD_GEMM_RESID:
         out = torch.empty((M, N), dtype=torch.float32 if md == A.ISD_GEMM_STORE_F32 else X.dtype, device=X.device)
     S = splits or (lib.isd_gemm_splits(N, K, 1 if md == A.ISD_GEMM_SWIGLU else 0) if bf else 1)

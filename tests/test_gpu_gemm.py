@@ -18,6 +18,12 @@ def _rand(shape, seed, scale=1.0, dtype=torch.bfloat16):
     return (torch.randn(shape, generator=g, device=DEV, dtype=torch.float32) * scale).to(dtype)
 
 
+def _pk(W):
+    """bf16 weights go to the library in the packed operand layout."""
+    from strided_decoding_amd import pack_weight
+    return pack_weight(W) if W.dtype == torch.bfloat16 else W
+
+
 def _ref(X, W, rows, cols):
     x = X.float().cpu().numpy().astype(np.float64)
     w = W.float().cpu().numpy().astype(np.float64)
@@ -48,7 +54,7 @@ def test_gemm_decode_shapes(name, M, N, K):
     print(f"gemm {name} {M}x{N}x{K}", flush=True)
     X = _rand((M, K), 1, 1.0)
     W = _rand((N, K), 2, 0.02)
-    Y = gemm(X, W, "store_f32" if name == "lm_head" else "store")
+    Y = gemm(X, _pk(W), "store_f32" if name == "lm_head" else "store")
     torch.cuda.synchronize()
     rows, cols = _pick(M, N, 400, 3)
     got = Y.float().cpu().numpy()[rows, cols]
@@ -61,7 +67,7 @@ def test_gemm_swiglu_and_residual():
     X = _rand((M, K), 4, 1.0)
     Wg = _rand((F, K), 5, 0.02)
     Wu = _rand((F, K), 6, 0.02)
-    H = gemm(X, Wg, "swiglu", W2=Wu)
+    H = gemm(X, _pk(Wg), "swiglu", W2=_pk(Wu))
     torch.cuda.synchronize()
     rows, cols = _pick(M, F, 400, 7)
     g = _ref(X, Wg, rows, cols)
@@ -71,7 +77,7 @@ def test_gemm_swiglu_and_residual():
     Wd = _rand((K, F), 8, 0.02)
     R0 = _rand((M, K), 9, 1.0, torch.float32)
     R = R0.clone()
-    gemm(H, Wd, "resid", R=R)
+    gemm(H, _pk(Wd), "resid", R=R)
     torch.cuda.synchronize()
     rows, cols = _pick(M, K, 400, 10)
     ref = R0.cpu().numpy().astype(np.float64)[rows, cols] + _ref(H, Wd, rows, cols)
@@ -84,7 +90,7 @@ def test_gemm_edge_shapes(M, N, K, splits):
     from strided_decoding_amd import gemm
     X = _rand((M, K), 11, 1.0)
     W = _rand((N, K), 12, 0.05)
-    Y = gemm(X, W, "store_f32", splits=splits)
+    Y = gemm(X, _pk(W), "store_f32", splits=splits)
     torch.cuda.synchronize()
     ref = X.double() @ W.double().T
     err = (Y.double() - ref).abs().max().item()
@@ -97,9 +103,10 @@ def test_gemm_row_invariance():
     K, N = 4096, 6144
     X = _rand((448, K), 13, 1.0)
     W = _rand((N, K), 14, 0.02)
-    big = gemm(X, W, "store")
-    small = gemm(X[:64].contiguous(), W, "store")
-    one = gemm(X[5:6].contiguous(), W, "store")
+    Wp = _pk(W)
+    big = gemm(X, Wp, "store")
+    small = gemm(X[:64].contiguous(), Wp, "store")
+    one = gemm(X[5:6].contiguous(), Wp, "store")
     torch.cuda.synchronize()
     assert torch.equal(big[:64], small)
     assert torch.equal(big[5:6], one)
@@ -116,7 +123,7 @@ def test_gemm_residual_with_fused_rmsnorm(splits):
     g = (1.0 + 0.1 * _rand((d,), 20, 1.0, torch.float32)).to(torch.bfloat16)
     R = R0.clone()
     y = torch.empty((M, d), dtype=torch.bfloat16, device=DEV)
-    gemm(H, Wd, "resid", R=R, splits=splits, norm_g=g, norm_out=y, norm_eps=1e-6)
+    gemm(H, _pk(Wd), "resid", R=R, splits=splits, norm_g=g, norm_out=y, norm_eps=1e-6)
     torch.cuda.synchronize()
     rows, cols = _pick(M, d, 400, 21)
     ref = R0.cpu().numpy().astype(np.float64)[rows, cols] + _ref(H, Wd, rows, cols)
@@ -143,9 +150,9 @@ def test_skinny_path_bit_identical_to_tiled(M, mode, N, K):
     for path in ("tiled", "skinny"):
         if mode == "resid":
             R = _rand((M, N), 33, 1.0, torch.float32)
-            outs.append(gemm(X, W, mode, R=R, path=path))
+            outs.append(gemm(X, _pk(W), mode, R=R, path=path))
         else:
-            outs.append(gemm(X, W, mode, W2=W2, path=path))
+            outs.append(gemm(X, _pk(W), mode, W2=None if W2 is None else _pk(W2), path=path))
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1])
     if M in (7, 56, 112):
@@ -171,7 +178,7 @@ def test_skinny_fused_rmsnorm_and_row_gather(splits):
     for path in ("tiled", "skinny"):
         R = _rand((M, d), 43, 1.0, torch.float32)
         y = torch.empty((M, d), dtype=torch.bfloat16, device=DEV)
-        gemm(H, Wd, "resid", R=R, splits=splits, norm_g=g, norm_out=y, norm_eps=1e-6, path=path)
+        gemm(H, _pk(Wd), "resid", R=R, splits=splits, norm_g=g, norm_out=y, norm_eps=1e-6, path=path)
         res.append((R, y))
     torch.cuda.synchronize()
     assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
@@ -185,3 +192,18 @@ def test_gemm_fp32_path():
     torch.cuda.synchronize()
     ref = X.double() @ W.double().T
     assert (Y.double() - ref).abs().max().item() <= 1e-5 * ref.abs().max().item()
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 16), (33, 48), (64, 4096), (200, 96)])
+def test_pack_weights_layout(rows, cols):
+    """The packed operand layout: block (nb, kb), lane l holds row 32 nb + l%32, k = 16 kb +
+    8 (l/32) .. + 7; rows padded with zeros to a multiple of 32."""
+    from strided_decoding_amd import pack_weight
+    W = _rand((rows, cols), 50 + rows, 1.0)
+    got = pack_weight(W).data.view(torch.int16).cpu().numpy()
+    w = W.view(torch.int16).cpu().numpy()
+    rp = -(-rows // 32) * 32
+    wp = np.zeros((rp, cols), np.int16)
+    wp[:rows] = w
+    want = wp.reshape(rp // 32, 32, cols // 16, 2, 8).transpose(0, 2, 3, 1, 4).reshape(-1)
+    assert np.array_equal(got, want)
