@@ -2,17 +2,18 @@
 // of consecutive prompt positions).  Keys and values are read only from the KV pages, the
 // block's own K/V having been appended first, and a row at position p sees keys 0 .. p.
 //
-// bf16 path (head_dim 128): one single-wave workgroup per (item, KV head, context split).
-// The up to 64 query rows of a KV-head group (positions x G query heads) are the columns of
-// two MFMA products
+// bf16 path (head_dim 128): one workgroup of NCB waves per (item, KV head, context split);
+// wave w owns 16 of the up to 16 NCB query columns of the KV-head group (positions x G query
+// heads), which are the columns of two MFMA products
 //   S^T = K Q^T          (A = 16 keys x 32 dims per step, B = Q^T)
 //   O^T += V^T P^T       (A = V^T rows = dims, k = 32 keys; B = P^T)
 // K pages are [token][dim] and V pages [dim][token] (transposed within a page), so both
-// operands are 16-byte row chunks.  The wave streams its 32-key blocks (two 16-token pages of
-// K and of V, 16 KB) through a private NBUF-block LDS ring with direct global->LDS loads,
-// NBUF-1 blocks in flight under explicit vmcnt waits while one is multiplied; every load
-// instruction reads 1 KB of one page contiguously, and the chunks are XOR-swizzled in LDS so
-// the operand reads are free of bank conflicts.  The key order inside a block is permuted so
+// operands are 16-byte row chunks.  The workgroup streams its 32-key blocks (two 16-token
+// pages of K and of V, 16 KB) through an NBUF-block LDS ring shared by its waves (each wave
+// issues 16/NCB of a block's 16 direct global->LDS loads, one barrier per block), NBUF-1 blocks
+// in flight under explicit vmcnt waits while one is multiplied; every load instruction reads
+// 1 KB of one page contiguously, and the chunks are XOR-swizzled in LDS so the operand reads
+// are free of bank conflicts.  The key order inside a block is permuted so
 // that the S^T accumulator registers of a lane are exactly the P^T operand slots of the next
 // product (no cross-lane traffic).  Online softmax in the log2 domain with wave reductions
 // over the 4 lane groups sharing a column.  Context splits begin at multiples of the split
