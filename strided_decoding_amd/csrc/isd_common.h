@@ -170,6 +170,9 @@ struct GemmArgs {
   int nseg;
   int seg_end[3];
   int seg_aoff[3];
+  // Split-K (splits > 1) only: leave the fp32 partials for the consumer (the fused QKV reduce
+  // in rope_append) instead of reducing them into C.
+  int keep_part;
 };
 enum { GEMM_PATH_AUTO = 0, GEMM_PATH_TILED = 1, GEMM_PATH_SKINNY = 2 };
 constexpr int kSkinnyMaxRows = 128;  // the skinny kernel holds at most four 32-row MFMA tiles
@@ -247,6 +250,14 @@ struct RopeAppendArgs {
   const float* cos_t;        // [max_pos, hd/2]
   const float* sin_t;
   int rows, Hq, Hkv, hd, P;
+  // Optional: read the projection from its split-K partials (part != null: fp32
+  // [splits, rows, (Hq+2Hkv)*hd], summed in split order, plus the LoRA delta of MASK rows,
+  // rounded to act) instead of qkv - the same values the split-K reduce would store.
+  const float* part;
+  int splits;
+  const int32_t* delta_row;  // -1 / null: no delta
+  const float* delta;
+  int ldd;
 };
 template <typename T>
 hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s);

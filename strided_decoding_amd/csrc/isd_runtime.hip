@@ -220,7 +220,8 @@ void derive(isd_ctx& x) {
     size_t p = std::max({need(M, x.qkvw, d, false), need(M, d, x.qd, false), need(M, F, d, true),
                          need(M, d, F, false), need(M, c.vocab, d, false)});
     if (c.lora_rank > 0)
-      p = std::max({p, need(Mm, r, d, false), need(Mm, r, x.qd, false), need(Mm, r, F, false)});
+      p = std::max({p, need(Mm, 3 * r, d, false), need(Mm, 2 * r, d, false), need(Mm, r, d, false),
+                    need(Mm, r, x.qd, false), need(Mm, r, F, false)});
     x.part_floats = x.bf ? p : 0;
   }
   x.kv_layer_bytes = (size_t)c.n_pages * x.kd * c.page_size * x.act;
@@ -268,11 +269,10 @@ StepMeta meta(isd_ctx& x) {
 
 // Launch a projection.  bf16 GEMMs with at most a decode pass's rows use the split-K factor
 // of their (N, K); larger row counts (prefill) run unsplit.
-hipError_t gemm(const isd_ctx& x, GemmArgs g, hipStream_t s) {
-  if (!x.bf) return launch_gemm_f32(g, s);
+GemmArgs plan_gemm(const isd_ctx& x, GemmArgs g) {
   g.splits = 1;
   g.part = nullptr;
-  if (g.M <= x.max_dec_rows && x.gemm_part) {
+  if (x.bf && g.M <= x.max_dec_rows && x.gemm_part) {
     const bool dual = g.epi == EPI_SWIGLU;
     const int S = gemm_splits(g.N, g.K, dual);
     if ((size_t)S * g.M * g.N * (dual ? 2 : 1) <= x.part_floats) {
@@ -280,7 +280,12 @@ hipError_t gemm(const isd_ctx& x, GemmArgs g, hipStream_t s) {
       g.part = x.gemm_part;
     }
   }
-  return launch_gemm_bf16(g, s);
+  return g;
+}
+
+hipError_t gemm(const isd_ctx& x, GemmArgs g, hipStream_t s) {
+  if (!x.bf) return launch_gemm_f32(g, s);
+  return launch_gemm_bf16(plan_gemm(x, g), s);
 }
 
 GemmArgs gargs(const void* A, int lda, const void* B0, int ldb, int M, int N, int K, int epi) {
@@ -370,15 +375,23 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
       isd_status st = lora_group(x, l, 0, 3, x.Xn, d, d, n, s);
       if (st != ISD_OK) return st;
     }
-    {
-      GemmArgs g = gargs(x.Xn, d, x.wqkv[l], d, M, x.qkvw, d, EPI_STORE);
-      g.C = x.QKV;
-      g.ldc = x.qkvw;
-      with_delta(x, g, lora);
-      TIMED("gemm_qkv", gemm(x, g, s));
-    }
+    // QKV projection; with split-K its partials are reduced by rope_append itself
+    GemmArgs gq = plan_gemm(x, gargs(x.Xn, d, x.wqkv[l], d, M, x.qkvw, d, EPI_STORE));
+    gq.C = x.QKV;
+    gq.ldc = x.qkvw;
+    with_delta(x, gq, lora);
+    gq.keep_part = 1;
+    if (x.bf) TIMED("gemm_qkv", launch_gemm_bf16(gq, s));
+    else TIMED("gemm_qkv", launch_gemm_f32(gq, s));
     {
       RopeAppendArgs ra{};
+      if (x.bf && gq.splits > 1) {
+        ra.part = gq.part;
+        ra.splits = gq.splits;
+        ra.delta_row = gq.delta_row;
+        ra.delta = gq.delta;
+        ra.ldd = gq.ldd;
+      }
       ra.qkv = x.QKV;
       ra.q_out = x.Qr;
       ra.k_pool = kl;

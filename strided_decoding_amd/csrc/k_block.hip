@@ -9,6 +9,8 @@
 // in ascending order, frees the pages beyond ceil(L'/P), ascending logical order.  Both
 // orders come from block-wide prefix sums, so the page tables are a deterministic function
 // of the slot states.
+#include <algorithm>
+
 #include "isd_common.h"
 
 namespace isd {
@@ -233,47 +235,78 @@ __global__ __launch_bounds__(1024) void rmsnorm_kernel(const float* X, const T* 
 }
 
 // RoPE (rotate-half) on q and k, write q to q_out and k, v into the slot's pages at `pos`.
-// K page layout [Hkv][P][hd]; V page layout [Hkv][hd][P].
+// K page layout [Hkv][P][hd]; V page layout [Hkv][hd][P].  One thread per group of 4 elements
+// (a RoPE group is 4 elements and their 4 partners half a head away); with split-K partials
+// the projection's reduction (in split order, plus the LoRA delta, rounded to act) happens
+// here, so the QKV projection is never stored.
 template <typename T>
 __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
-  const int r = blockIdx.x;
-  const int pos = a.row_pos[r];
-  const int hd = a.hd, half = hd / 2, P = a.P;
-  const int qd = a.Hq * hd, kd = a.Hkv * hd;
-  const T* src = (const T*)a.qkv + (size_t)r * (qd + 2 * kd);
-  T* qo = (T*)a.q_out + (size_t)r * qd;
-  if (pos < 0) {
-    for (int i = threadIdx.x; i < qd; i += 256) qo[i] = from_f<T>(0.f);
-    return;
-  }
-  const float* cs = a.cos_t + (size_t)pos * half;
-  const float* sn = a.sin_t + (size_t)pos * half;
-  const int slot = a.row_slot[r];
-  const int page = a.page_table[(size_t)slot * a.max_pages + pos / P];
-  const int tok = pos % P;
-  T* kp = (T*)a.k_pool;
-  T* vp = (T*)a.v_pool;
-  const int pairs_q = a.Hq * half, pairs_k = a.Hkv * half;
-  for (int i = threadIdx.x; i < pairs_q + pairs_k; i += 256) {
-    const bool isq = i < pairs_q;
-    const int j = isq ? i : i - pairs_q;
-    const int h = j / half, e = j % half;
-    const T* x = src + (isq ? 0 : qd) + (size_t)h * hd;
-    const float x1 = to_f(x[e]), x2 = to_f(x[e + half]);
-    const float c = cs[e], s = sn[e];
-    const float y1 = x1 * c - x2 * s, y2 = x2 * c + x1 * s;
-    if (isq) {
-      qo[h * hd + e] = from_f<T>(y1);
-      qo[h * hd + e + half] = from_f<T>(y2);
+  const int hd = a.hd, half = hd / 2, P = a.P, h4 = half / 4;
+  const int qd = a.Hq * hd, kd = a.Hkv * hd, width = qd + 2 * kd;
+  const int qi = a.Hq * h4, ki = a.Hkv * h4, vi = a.Hkv * (hd / 4);
+  const int per_row = qi + ki + vi;
+  const size_t total = (size_t)a.rows * per_row;
+  const size_t split_stride = (size_t)a.rows * width;
+  for (size_t it = (size_t)blockIdx.x * blockDim.x + threadIdx.x; it < total; it += (size_t)gridDim.x * blockDim.x) {
+    const int r = (int)(it / per_row), w = (int)(it % per_row);
+    const int pos = a.row_pos[r];
+    const int dr = (a.part && a.delta_row) ? a.delta_row[r] : -1;
+    // columns c .. c+3 of row r's projection as stored in act (or as the split-K reduce stores them)
+    auto load4 = [&](int c, float* v) {
+      if (a.part) {
+        const float* pr = a.part + (size_t)r * width + c;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < a.splits; ++sp) acc += *(const f32x4_t*)(pr + sp * split_stride);
+        if (dr >= 0) acc += *(const f32x4_t*)(a.delta + (size_t)dr * a.ldd + c);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) v[jj] = to_f(from_f<T>(acc[jj]));
+      } else {
+        const T* x = (const T*)a.qkv + (size_t)r * width + c;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) v[jj] = to_f(x[jj]);
+      }
+    };
+    if (w < qi + ki) {
+      // RoPE group: head h, elements e0 .. e0+3 and their partners e0+half ..
+      const bool isq = w < qi;
+      const int j = isq ? w : w - qi;
+      const int h = j / h4, e0 = (j % h4) * 4;
+      T* qo = (T*)a.q_out + (size_t)r * qd + h * hd + e0;
+      if (pos < 0) {                           // dead row: zero q, no cache write
+        if (isq)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) qo[jj] = qo[jj + half] = from_f<T>(0.f);
+        continue;
+      }
+      float x1[4], x2[4];
+      const int c0 = (isq ? 0 : qd) + h * hd + e0;
+      load4(c0, x1);
+      load4(c0 + half, x2);
+      const float* cs = a.cos_t + (size_t)pos * half + e0;
+      const float* sn = a.sin_t + (size_t)pos * half + e0;
+      T* dst = qo;
+      if (!isq) {
+        const int page = a.page_table[(size_t)a.row_slot[r] * a.max_pages + pos / P];
+        dst = (T*)a.k_pool + (((size_t)page * a.Hkv + h) * P + pos % P) * hd + e0;
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float c = cs[jj], sv = sn[jj];
+        dst[jj] = from_f<T>(x1[jj] * c - x2[jj] * sv);
+        dst[jj + half] = from_f<T>(x2[jj] * c + x1[jj] * sv);
+      }
     } else {
-      T* kr = kp + (((size_t)page * a.Hkv + h) * P + tok) * hd;
-      kr[e] = from_f<T>(y1);
-      kr[e + half] = from_f<T>(y2);
+      // V: dims d0 .. d0+3 of KV head h, written into the page's transposed layout
+      if (pos < 0) continue;
+      const int j = w - qi - ki;
+      const int h = j / (hd / 4), d0 = (j % (hd / 4)) * 4;
+      float v[4];
+      load4(qd + kd + h * hd + d0, v);
+      const int page = a.page_table[(size_t)a.row_slot[r] * a.max_pages + pos / P];
+      T* vp = (T*)a.v_pool + (((size_t)page * a.Hkv + h) * hd + d0) * P + pos % P;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) vp[(size_t)jj * P] = from_f<T>(v[jj]);
     }
-  }
-  for (int i = threadIdx.x; i < kd; i += 256) {
-    const int h = i / hd, d = i % hd;
-    vp[(((size_t)page * a.Hkv + h) * hd + d) * P + tok] = src[qd + kd + i];
   }
 }
 
@@ -341,7 +374,10 @@ hipError_t launch_rmsnorm(const float* X, const T* g, T* Y, int rows, int d, flo
 template <typename T>
 hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rope_append_kernel<T>, dim3(a.rows), dim3(256), 0, s, a);
+  if (a.hd % 8) return hipErrorInvalidValue;
+  const size_t items = (size_t)a.rows * ((a.Hq + a.Hkv) * (a.hd / 8) + a.Hkv * (a.hd / 4));
+  const unsigned blocks = (unsigned)std::min<size_t>((items + 255) / 256, 4096);
+  hipLaunchKernelGGL(rope_append_kernel<T>, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -455,8 +455,33 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_
   }
   wait_vmcnt<0>();                               // the loads past the last stage
 
+  // The MASK-row LoRA delta of a row tile is loaded before any of its stores, so that the
+  // loads are issued together rather than one round trip per output.
+  GemmArgs b = a;
+  b.delta_row = nullptr;
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
+    float dl[16][NB];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) dl[r][j] = -0.f;   // x + (-0) == x for every x
+    if (!PARTIAL && a.delta_row) {
+      int dr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * i + 8 * (r >> 2) + 4 * khi + (r & 3);
+        dr[r] = row < a.M ? a.delta_row[row] : -1;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int col = DUAL ? n0 + r32 : n0 + 32 * j + r32;
+          if (dr[r] >= 0 && col < a.N)
+            dl[r][j] = a.delta[(size_t)dr[r] * a.ldd + (DUAL && j ? a.delta_off2 : 0) + col];
+        }
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 32 * i + 8 * (r >> 2) + 4 * khi + (r & 3);
@@ -470,7 +495,7 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_
             pr[a.N + col] = acc[i][1][r];
           }
         } else {
-          epilogue_store_t<bf16, EPI>(a, row, col, acc[i][0][r], acc[i][1][r]);
+          epilogue_store_t<bf16, EPI>(b, row, col, acc[i][0][r] + dl[r][0], acc[i][1][r] + dl[r][1]);
         }
       } else {
 #pragma unroll
@@ -479,7 +504,7 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_
           if (PARTIAL) {
             if (col < a.N) part[((size_t)sp * a.M + row) * (size_t)a.N + col] = acc[i][j][r];
           } else {
-            epilogue_store_t<bf16, EPI>(a, row, col, acc[i][j][r], 0.f);
+            epilogue_store_t<bf16, EPI>(b, row, col, acc[i][j][r] + dl[r][j], 0.f);
           }
         }
       }
@@ -513,7 +538,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a, int S, c
 // both paths give the same normalized row for the same residual row.
 constexpr int kNormThreads = 1024;
 constexpr int kNormMaxGroups = 2;         // rows up to 8192 wide
-constexpr int kMaxSplits = 8;
+constexpr int kMaxSplits = 16;
 __global__ __launch_bounds__(kNormThreads) void splitk_resid_norm_kernel(GemmArgs a, int S, const float* part) {
   __shared__ float sh[kNormThreads / 64];
   const int row = blockIdx.x, tid = threadIdx.x;
@@ -617,6 +642,7 @@ template <int EPI>
 hipError_t finish(const GemmArgs& a, int S, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (S > 1 && a.keep_part) return hipSuccess;       // the consumer reduces the partials
   const bool norm = EPI == EPI_RESID && a.norm_out;
   if (S > 1) {
     if (norm) {
@@ -673,7 +699,10 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
 
 template <int EPI>
 hipError_t launch_path(const GemmArgs& a, hipStream_t s) {
-  const bool skinny = a.path == GEMM_PATH_SKINNY || (a.path == GEMM_PATH_AUTO && a.M <= kSkinnyMaxRows);
+  // automatic: the skinny kernel up to 64 rows, and up to 128 rows unless the product is so
+  // wide (the LM head) that the tiled kernel's 224-row tiles have work for every CU
+  const bool skinny = a.path == GEMM_PATH_SKINNY ||
+                      (a.path == GEMM_PATH_AUTO && (a.M <= 64 || (a.M <= kSkinnyMaxRows && a.N <= 65536)));
   return skinny ? launch_skinny<EPI>(a, s) : launch_big<EPI>(a, s);
 }
 
@@ -684,7 +713,10 @@ int gemm_splits(int n_out, int K, bool dual) {
   const int tno = dual ? isd::TN2 / 2 : isd::TN2;
   const int tiles = (n_out + tno - 1) / tno;
   int S = 1;
-  while (S < 8 && 2 * tiles * (2 * S) <= 256 && (K / isd::BK) % (2 * S) == 0 && K / (2 * S) >= 512) S *= 2;
+  // split while there are fewer than 256 workgroups of 256 columns (x2 row tiles) and every
+  // split keeps at least 4 k-stages
+  while (S < isd::kMaxSplits && 2 * tiles * (2 * S) <= 256 && (K / isd::BK) % (2 * S) == 0 && K / (2 * S) >= 128)
+    S *= 2;
   return S;
 }
 
