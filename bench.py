@@ -38,6 +38,7 @@ def parse():
                    help="isd: decode throughput (default); risd: R-ISD == AR check and overhead factor")
     p.add_argument("--model", choices=("8b", "32b"), default="8b", help="model shape of the isd workload")
     p.add_argument("--batch", type=int, default=None, help="slots (default: the workload's)")
+    p.add_argument("--stride", type=int, default=None, help="ISD stride N (default: the workload's, 4)")
     p.add_argument("--prompt-len", type=int, default=None)
     p.add_argument("--gen", type=int, default=None)
     p.add_argument("--profile-steps", type=int, default=6)
@@ -79,7 +80,9 @@ def kernel_model(shape, M, N, ctx_rows, attn_keys):
 
 def tpf_projection(p, N):
     """Tokens per forward of the ISD state machine at a per-token acceptance p (a projection for
-    trained weights; random-init weights accept almost nothing)."""
+    trained weights; random-init weights accept almost nothing).  N = 1 is plain AR."""
+    if N == 1:
+        return 1.0
     return (2 + sum(p ** k for k in range(1, N - 1))) / (2 - p ** (N - 1))
 
 
@@ -389,7 +392,10 @@ def report(args, wl_name, shape, B, N, T, propose, prompt_len, gen, elapsed, st0
         "step_hbm_GBps": sb / (ms * 1e-3) / 1e9,
         "step_hbm_frac": sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "step_algorithmic_bytes": sb,
+        "tpf_formula_at_measured_acceptance": tpf_projection(
+            delta(st0, st1, "accepted") / max(1, delta(st0, st1, "verified")), N),
         "projected_tokens_per_s_at_p0.9": args.steps / elapsed * B * tpf_projection(0.9, N),
+        "stride_efficiency_at_p0.9": tpf_projection(0.9, N) ** 2 / (2 * N - 1),
         "roofline": roof,
         "kernels": kernels,
     }
@@ -424,7 +430,7 @@ def run_risd(args, I, Engine, torch, dev):
     exactly the tokens of greedy AR decoding (N = 1) with the base weights; the overhead factor
     alpha is the R-ISD step time over the step time of ISD without the adapter (same shapes)."""
     wl = I.RISD_8B
-    shape, N, T, propose = wl.model, wl.stride, wl.temperature, wl.propose
+    shape, N, T, propose = wl.model, args.stride or wl.stride, wl.temperature, wl.propose
     B = args.batch or wl.batch
     pl = args.prompt_len or wl.prompt_len
     gen = args.gen or wl.max_new
@@ -494,7 +500,7 @@ def main():
     if args.workload == "risd":
         return run_risd(args, I, Engine, torch, dev)
     wl = I.QWEN3_32B_DECODE if args.model == "32b" else I.QWEN3_8B_DECODE
-    shape, N, T, propose = wl.model, wl.stride, wl.temperature, wl.propose
+    shape, N, T, propose = wl.model, args.stride or wl.stride, wl.temperature, wl.propose
     B = args.batch or wl.batch
     pl = args.prompt_len or wl.prompt_len
     gen = args.gen or wl.max_new
@@ -509,7 +515,10 @@ def main():
         f"{delta(st0, st1, 'committed')} tokens, live slots {live}")
     kernels, roof, ctx = kernel_profile(eng, shape, B, N, args.profile_steps)
     name = wl.name if B == wl.batch else wl.name.rsplit("-b", 1)[0] + f"-b{B}"
-    metric = METRIC if wl is I.QWEN3_8B_DECODE else f"committed tokens/s on 1 MI355X (32B-shape, batch {B}, N=4)"
+    if N != wl.stride:
+        name += f"-n{N}"
+    metric = METRIC if wl is I.QWEN3_8B_DECODE and N == wl.stride else \
+        f"committed tokens/s on 1 MI355X ({'8B' if wl is I.QWEN3_8B_DECODE else '32B'}-shape, batch {B}, N={N})"
     out = report(args, name, shape, B, N, T, propose, pl, gen, elapsed, st0, st1, kernels, roof, ctx, metric)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, weights, eng, B, N, T)
