@@ -34,8 +34,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", choices=("isd", "risd"), default="isd",
-                   help="isd: decode throughput (default); risd: R-ISD == AR check and overhead factor")
+    p.add_argument("--workload", choices=("isd", "risd", "meter"), default="isd",
+                   help="isd: decode throughput (default); risd: R-ISD == AR check and overhead factor; "
+                        "meter: introspective acceptance rate of the model's own proposals (teacher-forced)")
     p.add_argument("--model", choices=("8b", "32b"), default="8b", help="model shape of the isd workload")
     p.add_argument("--batch", type=int, default=None, help="slots (default: the workload's)")
     p.add_argument("--stride", type=int, default=None, help="ISD stride N (default: the workload's, 4)")
@@ -480,6 +481,39 @@ def run_risd(args, I, Engine, torch, dev):
     emit(args, out)
 
 
+def run_meter(args, I, Engine, torch, dev):
+    """Introspective acceptance meter on the 8B shape: every pending token (the model's own
+    MASK-row proposal) is committed untested and re-scored by the next pass's anchor; the
+    rate is the mean acceptance probability (p(x) for argmax proposals at T = 1)."""
+    wl = I.QWEN3_8B_DECODE
+    shape, N, T, propose = wl.model, args.stride or wl.stride, wl.temperature, wl.propose
+    B = args.batch or wl.batch
+    pl = args.prompt_len or wl.prompt_len
+    gen = args.gen or wl.max_new
+    weights, _ = I.weights_torch(shape, dev)
+    eng, _ = prefill_engine(I, Engine, torch, shape, weights, dev, B, N, T, propose, pl, gen)
+    eng.set_meter(True)
+    elapsed, st0, st1 = timed_steps(eng, torch, args.steps, args.warmup, not args.no_graphs)
+    s_sum = sum(s["meter_sum"] for s in st1) - sum(s["meter_sum"] for s in st0)
+    s_n = delta(st0, st1, "meter_n")
+    rate = s_sum / max(1, s_n)
+    log(f"meter: {s_n} re-scored tokens, introspective acceptance {rate:.6f}, "
+        f"{1e3 * elapsed / args.steps:.3f} ms/step")
+    out = {
+        "metric": f"introspective acceptance rate (8B-shape, batch {B}, N={N}, {propose} proposals, T={T}; "
+                  "teacher-forced re-scoring of the model's own proposals)",
+        "value": rate, "unit": "probability", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": 1e3 * elapsed / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (random-init weights N(0,0.02), uniformly random prompt ids)",
+        "config": {"workload": f"qwen3-8b-meter-b{B}", "batch": B, "stride": N, "prompt_len": pl,
+                   "max_new": gen, "propose": propose, "temperature": T, "parallelism": "single GPU",
+                   "hip_graphs": not args.no_graphs},
+        "rescored_tokens": s_n,
+    }
+    emit(args, out)
+
+
 def main():
     args = parse()
     if args.trace_summary:
@@ -499,6 +533,8 @@ def main():
     dev = torch.device("cuda:0")
     if args.workload == "risd":
         return run_risd(args, I, Engine, torch, dev)
+    if args.workload == "meter":
+        return run_meter(args, I, Engine, torch, dev)
     wl = I.QWEN3_32B_DECODE if args.model == "32b" else I.QWEN3_8B_DECODE
     shape, N, T, propose = wl.model, args.stride or wl.stride, wl.temperature, wl.propose
     B = args.batch or wl.batch

@@ -123,7 +123,9 @@ typedef struct {
   int32_t q_row[ISD_MAX_STRIDE - 1];     /* logits row (previous pass) that proposed pending[i];
                                             -1: delta q (argmax proposal) */
   int32_t passes, accepted, verified, committed;   /* cumulative counters */
-  int32_t pad[6];
+  double meter_sum;                      /* introspective acceptance meter (isd_set_meter): sum of */
+  int32_t meter_n;                       /* the acceptance probabilities of meter_n re-scored tokens */
+  int32_t pad[3];
 } isd_slot;
 
 typedef struct isd_ctx isd_ctx;
@@ -268,10 +270,23 @@ typedef struct {
   int32_t* n_commit;
   int32_t* n_accept;
   void* workspace;
+  int32_t meter;           /* 1: introspective acceptance meter mode (see isd_set_meter) */
 } isd_sample_args;
 
 size_t isd_sample_workspace_bytes(int32_t batch, int32_t rows, int32_t vocab, int32_t q_rows);
 isd_status isd_sample(const isd_sample_args* a, void* stream);
+
+/* Introspective acceptance meter (wiki note, TL;DR and Key claims: the introspective
+ * acceptance rate - whether a model accepts, under argmax or sampling, its own previously
+ * generated tokens when it re-evaluates them; AR models ~0.98).  With the meter on, every
+ * pending token of an A-state pass - the model's own proposal from the previous pass - is
+ * committed without a test (teacher forcing of the model's own generation, so that no
+ * rejection cuts the block short) and re-scored by the pass's anchor distribution: the slot
+ * adds its acceptance probability to meter_sum and 1 to meter_n.  The probability is
+ * min(1, p(x)/q(x)) for a sampled proposal, p(x) for an argmax proposal (q = delta), and
+ * [x == argmax p] at temperature 0.  Off (default): ordinary ISD.  Changing it drops
+ * captured graphs.  Errors: ISD_E_ARG. */
+isd_status isd_set_meter(isd_ctx* ctx, int32_t enable);
 
 /* Packed operand layout of the bf16 projection weights (the MFMA B operands of the GEMMs,
  * one contiguous kilobyte per 32x32x16 product): W [rows, cols] row-major bf16 becomes

@@ -28,6 +28,13 @@ L = cached tokens and c = newest committed token (not yet cached):
 
 Proposals: 'sample' draws z ~ q = softmax_T(row); 'argmax' takes z = argmax(row) and
 q := delta_z (so acceptance is u < p(z) and the residual is p with z removed).
+
+Introspective acceptance meter (wiki note, TL;DR and Key claims: introspective consistency
+is whether a model accepts, under argmax or sampling, its own previously generated tokens
+when it re-evaluates them).  With meter=True every pending token - the model's own proposal
+- is committed without a test, so the model's own generation is teacher-forced through the
+passes, and the pass's anchor re-scores it: the slot accumulates the acceptance probability
+min(1, p(x)/q(x)) (p(x) for an argmax proposal, [x == argmax p] at T = 0).
 T = 0 is greedy: every decision is an argmax (accept iff v_i == argmax p_i).
 N = 1 is plain AR decoding.  R-ISD is the same machine with the LoRA active on MASK
 rows.  A slot stops after exactly max_new generated tokens (the prefill's token
@@ -58,6 +65,8 @@ class SlotState:
     max_new: int = 0
     n_gen: int = 0
     cache: list = None
+    meter_sum: float = 0.0          # meter mode: sum of the pending tokens' acceptance probabilities
+    meter_n: int = 0
 
     @property
     def generated(self):
@@ -95,6 +104,8 @@ class Outcome:
     new_state: str
     new_pending: list
     new_q: list
+    meter_sum: float = 0.0
+    meter_n: int = 0
 
 
 def draw(logits, u, T):
@@ -114,17 +125,19 @@ def propose_token(logits, u, T, propose):
     return j, (w, S), margin
 
 
-def decide(state, L, t, slot, pending, pending_q, logits, N, T, propose, seed):
+def decide(state, L, t, slot, pending, pending_q, logits, N, T, propose, seed, meter=False):
     """The decisions of one pass of one slot, given the pass's logits rows.
 
     state 'A': rows [c, v_1 .. v_{N-1}, MASK x (N-1)]; 'B': rows [c, MASK x (N-1)].
     pending_q[i] is (w, S) of the MASK row that proposed pending[i], or None (delta q).
     Returns an Outcome (tokens committed in order, accepted count, decisions with margins,
     and the slot's next L, c, state, pending tokens and their q records).
+    meter: commit every pending token untested and sum their acceptance probabilities.
     """
     u = lambda pos, purpose: philox.uniform(seed, slot, t, pos, purpose)
     dec, tokens = [], []
     n_acc = 0
+    msum, mn = 0.0, 0
     if state == STATE_A:
         for i in range(1, N):
             v = pending[i - 1]
@@ -132,11 +145,18 @@ def decide(state, L, t, slot, pending, pending_q, logits, N, T, propose, seed):
             qrec = pending_q[i - 1] if pending_q else None
             if T == 0.0:
                 ok, margin = (v == sampler.argmax(row)), sampler.top2_gap(row)
+                if meter:
+                    msum += 1.0 if ok else 0.0
             else:
                 w, S, _ = sampler.weights_T(row, T)
                 px = float(w[v]) / S
                 qx = 1.0 if qrec is None else float(qrec[0][v]) / qrec[1]
-                ok, margin = sampler.accept(px, qx, u(L + i, philox.PURPOSE_ACCEPT))
+                if meter:
+                    msum += min(1.0, px / qx)
+                else:
+                    ok, margin = sampler.accept(px, qx, u(L + i, philox.PURPOSE_ACCEPT))
+            if meter:
+                ok, margin, mn = True, float("inf"), mn + 1
             dec.append(Decision("accept", L + i, v, margin, ok))
             if ok:
                 tokens.append(v)
@@ -165,7 +185,7 @@ def decide(state, L, t, slot, pending, pending_q, logits, N, T, propose, seed):
             dec.append(Decision("propose", L + N + j, z, mz))
             new_pending.append(z)
             new_q.append(qrec)
-        return Outcome(tokens, n_acc, dec, L + N, z1, STATE_A, new_pending, new_q)
+        return Outcome(tokens, n_acc, dec, L + N, z1, STATE_A, new_pending, new_q, msum, mn)
     z1, m1 = draw(logits[0], u(L + 1, philox.PURPOSE_DRAW), T)
     dec.append(Decision("z1", L + 1, z1, m1))
     tokens.append(z1)
@@ -180,8 +200,9 @@ def decide(state, L, t, slot, pending, pending_q, logits, N, T, propose, seed):
 
 class Decoder:
     def __init__(self, model, N, temperature, propose="sample", seed=1,
-                 page_size=16, n_pages=1 << 20, keep_logits=False):
+                 page_size=16, n_pages=1 << 20, keep_logits=False, meter=False):
         assert N >= 1
+        self.meter = bool(meter)
         self.m = model
         self.spec = model.spec
         self.N = int(N)
@@ -260,7 +281,10 @@ class Decoder:
         pos = L + np.arange(len(ids))
         logits, kv = self.m.forward(ids, pos, st.cache, is_mask=is_mask if self.use_lora else None)
         state_before = st.state
-        out = decide(st.state, L, t, slot, st.pending, st.pending_q, logits, N, self.T, self.propose, self.seed)
+        out = decide(st.state, L, t, slot, st.pending, st.pending_q, logits, N, self.T, self.propose, self.seed,
+                     meter=self.meter)
+        st.meter_sum += out.meter_sum
+        st.meter_n += out.meter_n
         tokens, n_acc, dec = out.tokens, out.n_accept, out.decisions
         new_L, new_c, new_state = out.new_L, out.new_c, out.new_state
         new_pending, new_q = out.new_pending, out.new_q

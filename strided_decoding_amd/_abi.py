@@ -21,7 +21,7 @@ ISD_SLOT_EMPTY, ISD_SLOT_A, ISD_SLOT_B, ISD_SLOT_DONE = 0, 1, 2, 3
 EXPORTS = ("isd_init", "isd_prefill", "isd_step", "isd_get_buffers", "isd_get_status", "isd_release",
            "isd_attn_workspace_bytes", "isd_attn_paged", "isd_sample_workspace_bytes", "isd_sample",
            "isd_version", "isd_profile", "isd_profile_report", "isd_gemm", "isd_gemm_splits", "isd_set_graphs",
-           "isd_packed_weight_bytes", "isd_pack_weights")
+           "isd_packed_weight_bytes", "isd_pack_weights", "isd_set_meter")
 
 ISD_GEMM_STORE, ISD_GEMM_STORE_F32, ISD_GEMM_RESID, ISD_GEMM_SWIGLU = 0, 1, 2, 3
 
@@ -68,7 +68,9 @@ class Sizes(C.Structure):
 SLOT_INTS = 32   # isd_slot is 32 int32 words
 SLOT_FIELDS = ["state", "L", "c", "t", "n_gen", "max_new", "n_pages", "status"] + \
     [f"pending{i}" for i in range(ISD_MAX_STRIDE - 1)] + [f"q_row{i}" for i in range(ISD_MAX_STRIDE - 1)] + \
-    ["passes", "accepted", "verified", "committed"] + [f"pad{i}" for i in range(6)]
+    ["passes", "accepted", "verified", "committed", "meter_sum_lo", "meter_sum_hi", "meter_n"] + \
+    [f"pad{i}" for i in range(3)]
+METER_SUM_WORD = 26   # meter_sum: a double in words 26-27
 
 
 class Buffers(C.Structure):
@@ -90,7 +92,7 @@ class SampleArgs(C.Structure):
     _fields_ = [("batch", C.c_int32), ("stride_n", C.c_int32), ("vocab", C.c_int32), ("propose", C.c_int32),
                 ("q_rows", C.c_int32), ("temperature", C.c_float), ("seed", C.c_uint64), ("slots", C.c_void_p),
                 ("logits", C.c_void_p), ("q_logits", C.c_void_p), ("tokens", C.c_void_p),
-                ("n_commit", C.c_void_p), ("n_accept", C.c_void_p), ("workspace", C.c_void_p)]
+                ("n_commit", C.c_void_p), ("n_accept", C.c_void_p), ("workspace", C.c_void_p), ("meter", C.c_int32)]
 
 
 _lib = None
@@ -127,6 +129,7 @@ def load(path=LIB_PATH):
     lib.isd_packed_weight_bytes.argtypes = [C.c_int32, C.c_int32]
     lib.isd_packed_weight_bytes.restype = C.c_size_t
     lib.isd_pack_weights.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p]
+    lib.isd_set_meter.argtypes = [C.c_void_p, C.c_int32]
     lib.isd_profile.argtypes = [C.c_void_p, C.c_int32]
     lib.isd_set_graphs.argtypes = [C.c_void_p, C.c_int32]
     lib.isd_profile_report.argtypes = [C.c_void_p, C.POINTER(ProfEntry), C.c_int32, C.POINTER(C.c_int32)]

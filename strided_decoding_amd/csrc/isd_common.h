@@ -297,6 +297,8 @@ struct PrefillCall {
 hipError_t launch_prefill_setup(const StepMeta& m, const PrefillCall& c, const int32_t* prompt_ids,
                                 int q_tile, int32_t* order_out, hipStream_t s);
 
+static_assert(sizeof(isd_slot) == 128, "slot record layout is part of the ABI");
+
 struct SampleArgs {
   isd_slot* slots;
   int n_slots;
@@ -316,6 +318,7 @@ struct SampleArgs {
   int32_t* n_accept;
   int prefill;               // 1: draw the first token only (t = 0, position L)
   int32_t* first_tok;        // prefill output [n_slots]
+  int meter;                 // 1: commit pending tokens untested, accumulate their acceptance
 };
 hipError_t launch_row_stats(const float* logits, int rows, int V, float T, ChunkStat* stats, hipStream_t s);
 hipError_t launch_decide(const SampleArgs& a, hipStream_t s);

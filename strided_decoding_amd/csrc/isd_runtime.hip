@@ -83,6 +83,7 @@ struct isd_ctx {
   // graph replay of isd_step (isd_set_graphs): one executable graph per logits-buffer parity,
   // valid for the output pointers it was captured with
   bool graphs = false;
+  bool meter = false;           // introspective acceptance meter (isd_set_meter)
   hipStream_t cap_stream = nullptr;
   struct StepGraph {
     hipGraphExec_t exec = nullptr;
@@ -509,6 +510,7 @@ SampleArgs sargs(isd_ctx& x) {
   a.T = x.cfg.temperature;
   a.seed = x.cfg.seed;
   a.n_chunks = x.n_chunks;
+  a.meter = x.meter ? 1 : 0;
   return a;
 }
 
@@ -721,6 +723,13 @@ isd_status isd_set_graphs(isd_ctx* x, int32_t enable) {
   if (enable && !x->cap_stream) HIP_OK(hipStreamCreateWithFlags(&x->cap_stream, hipStreamNonBlocking));
   if (!enable) drop_graphs(x);
   x->graphs = enable != 0;
+  return ISD_OK;
+}
+
+isd_status isd_set_meter(isd_ctx* x, int32_t enable) {
+  if (!x) return ISD_E_ARG;
+  if ((enable != 0) != x->meter) drop_graphs(x);   // the decide launch is captured by value
+  x->meter = enable != 0;
   return ISD_OK;
 }
 
@@ -961,6 +970,7 @@ isd_status isd_sample(const isd_sample_args* a, void* stream) {
   sa.tokens = a->tokens;
   sa.n_commit = a->n_commit;
   sa.n_accept = a->n_accept;
+  sa.meter = a->meter != 0;
   HIP_OK(launch_decide(sa, s));
   return ISD_OK;
 }

@@ -381,9 +381,13 @@ __global__ void attn_setup_kernel(AttnItem* items, int32_t* row_pos, int32_t* ro
 
 }  // namespace
 
+#ifndef ISD_ATTN_ITEMS
+#define ISD_ATTN_ITEMS 2048
+#endif
 int attn_split_len(int batch, int n_kv_heads, int max_ctx) {
-  // about 2048 (slot, KV head, split) workgroups at the longest context, 128 .. 2048 keys each
-  const long long want = ((long long)max_ctx * batch * n_kv_heads + 2047) / 2048;
+  // about kAttnItems (slot, KV head, split) workgroups at the longest context, 128 .. 2048 keys each
+  constexpr long long kAttnItems = ISD_ATTN_ITEMS;
+  const long long want = ((long long)max_ctx * batch * n_kv_heads + kAttnItems - 1) / kAttnItems;
   int split = 128;
   while (split < 2048 && split < want) split *= 2;
   return split;

@@ -175,6 +175,8 @@ __global__ __launch_bounds__(256) void prefill_setup_kernel(StepMeta m, PrefillC
         st->q_row[j] = -1;
       }
       st->passes = st->accepted = st->verified = st->committed = 0;
+      st->meter_sum = 0.0;
+      st->meter_n = 0;
       m.ctx_len[b] = len;
       m.last_rows[i] = c.off[i + 1] - 1;
       order_out[i] = b;

@@ -389,6 +389,7 @@ __global__ __launch_bounds__(NT) void decide_kernel(SampleArgs a) {
   const int R = a.rows_per_slot, base_row = b * R;
   const int L = st->L, t = st->t;
   int ncommit = 0, nacc = 0, nver = 0;
+  double msum = 0.0;                   // meter: acceptance probabilities of the pending tokens
   bool failed = false;
   int newL = L, newc = st->c, newstate = ISD_SLOT_A;
   int npend = 0;
@@ -436,6 +437,10 @@ __global__ __launch_bounds__(NT) void decide_kernel(SampleArgs a) {
       const bool sampled_q = a.propose == ISD_PROPOSE_SAMPLE && qr >= 0 && a.q_logits;
       if (greedy) {
         ok = (v == ps.arg);
+        if (a.meter) {
+          msum += ok ? 1.0 : 0.0;
+          ok = true;
+        }
       } else {
         const double px = weight_of(a.logits[(size_t)row * a.V + v], ps.m, a.T) / ps.S;
         double qx = 1.0;
@@ -447,8 +452,13 @@ __global__ __launch_bounds__(NT) void decide_kernel(SampleArgs a) {
           }
           qx = weight_of(a.q_logits[(size_t)qr * a.V + v], qs.m, a.T) / qs.S;
         }
-        const double u = philox_uniform(a.seed, b, t, L + k, 0);
-        ok = u < px / qx;
+        if (a.meter) {
+          msum += fmin(1.0, px / qx);
+          ok = true;
+        } else {
+          const double u = philox_uniform(a.seed, b, t, L + k, 0);
+          ok = u < px / qx;
+        }
       }
       if (ok) {
         commit(v);
@@ -520,6 +530,10 @@ __global__ __launch_bounds__(NT) void decide_kernel(SampleArgs a) {
     st->passes += 1;
     st->verified += nver;
     st->accepted += nacc;
+    if (a.meter) {
+      st->meter_sum += msum;
+      st->meter_n += nver;
+    }
     st->committed += ncommit;
     for (int k = 0; k < N; ++k) a.tokens[(size_t)b * N + k] = k < ncommit ? s_tok[k] : -1;
     a.n_commit[b] = ncommit;

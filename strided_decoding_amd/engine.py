@@ -184,6 +184,11 @@ class Engine:
     def profile(self, enable):
         A.check("isd_profile", self.lib.isd_profile(self.ctx, 1 if enable else 0))
 
+    def set_meter(self, enable):
+        """Introspective acceptance meter (isd_set_meter): pending tokens are committed untested
+        and their acceptance probabilities accumulate in the slot records (meter_sum, meter_n)."""
+        A.check("isd_set_meter", self.lib.isd_set_meter(self.ctx, 1 if enable else 0))
+
     def set_graphs(self, enable):
         """Replay isd_step from captured HIP graphs (see isd_set_graphs)."""
         A.check("isd_set_graphs", self.lib.isd_set_graphs(self.ctx, 1 if enable else 0))
@@ -208,8 +213,12 @@ class Engine:
     def slots_host(self):
         """Per-slot state as a list of dicts (synchronizes)."""
         torch.cuda.synchronize(self.device)
-        a = self.slots_view().cpu().numpy()
-        return [dict(zip(A.SLOT_FIELDS, row.tolist())) for row in a]
+        a = np.ascontiguousarray(self.slots_view().cpu().numpy())
+        out = [dict(zip(A.SLOT_FIELDS, row.tolist())) for row in a]
+        msum = a[:, A.METER_SUM_WORD:A.METER_SUM_WORD + 2].copy().view(np.float64)[:, 0]
+        for d, m in zip(out, msum):
+            d["meter_sum"] = float(m)
+        return out
 
     def page_table(self):
         mp = self._buf.max_pages_per_slot
@@ -300,8 +309,9 @@ def gemm(X, W, mode="store", W2=None, out=None, R=None, splits=0, workspace=None
 
 
 def sample(slots, logits, q_logits, stride, temperature, propose, seed, tokens, n_commit, n_accept,
-           workspace=None, stream=None):
-    """Kernel-level acceptance step (see isd_sample).  slots: int32 [B, 32] device tensor (in/out)."""
+           workspace=None, stream=None, meter=False):
+    """Kernel-level acceptance step (see isd_sample).  slots: int32 [B, 32] device tensor (in/out);
+    meter: the introspective acceptance meter mode (see isd_set_meter)."""
     lib = A.load()
     B, R, V = logits.shape
     q_rows = 0 if q_logits is None else q_logits.shape[0]
@@ -311,7 +321,7 @@ def sample(slots, logits, q_logits, stride, temperature, propose, seed, tokens, 
     args = A.SampleArgs(B, stride, V, A.ISD_PROPOSE_ARGMAX if propose == "argmax" else A.ISD_PROPOSE_SAMPLE,
                         q_rows, float(temperature), int(seed), slots.data_ptr(), logits.data_ptr(),
                         0 if q_logits is None else q_logits.data_ptr(), tokens.data_ptr(), n_commit.data_ptr(),
-                        n_accept.data_ptr(), workspace.data_ptr())
+                        n_accept.data_ptr(), workspace.data_ptr(), 1 if meter else 0)
     stream = stream if stream is not None else torch.cuda.current_stream(logits.device)
     A.check("isd_sample", lib.isd_sample(C.byref(args), C.c_void_p(stream.cuda_stream)))
     return workspace

@@ -200,3 +200,39 @@ def test_lora_mask_rows_end_to_end(dtype):
     else:
         teacher_forced(shape, w, 3, 1.0, "sample", prompts, [10, 12, 8], steps=8, lora=lora, logits_tol=2e-2,
                        rel=True, on_gpu_logits=True)
+
+
+@pytest.mark.parametrize("N,T,propose", [(3, 0.0, "argmax"), (4, 1.0, "argmax")])
+def test_meter_mode_end_to_end(N, T, propose):
+    """Introspective acceptance meter through isd_step: the model's own proposals are
+    committed untested and re-scored; the committed sequences and the per-slot meter sums
+    equal the oracle decoder's in meter mode (tiny fp32 model, peaky weights so that no
+    decision is near a tie)."""
+    shape = I.ModelShape("tiny-gqa", 2, 128, 4, 2, 32, 256, 512, "f32")
+    w = I.weights_numpy(shape, seed=4, scale=40.0, sticky=(0.0, 10.0, 2.0, 7))
+    prompts = I.ragged_prompts([5, 17, 33], shape.vocab, seed=6)
+    max_new = [20, 9, 15]
+    B = len(prompts)
+    eng = make_engine(shape, w, N, T, propose, B, max(len(p) for p in prompts) + max(max_new) + 2 * N + 2)
+    eng.set_meter(True)
+    model = M.Model(spec_of(shape), w, None)
+    dec = OI.Decoder(model, N, T, propose=propose, seed=1, page_size=16, n_pages=eng.cfg.n_pages, meter=True)
+    print(f"meter e2e N={N} T={T} {propose}", flush=True)
+    first = eng.prefill(list(range(B)), prompts, max_new).cpu().numpy()
+    assert list(first) == dec.prefill(list(range(B)), prompts, max_new)
+    gen = [[int(first[b])] for b in range(B)]
+    for _ in range(40):
+        if all(st.state == OI.STATE_DONE for st in dec.slots.values()):
+            break
+        tok, nc, _ = eng.step()
+        dec.step()
+        torch.cuda.synchronize()
+        t, n = tok.cpu().numpy(), nc.cpu().numpy()
+        for b in range(B):
+            gen[b] += [int(x) for x in t[b, :n[b]]]
+    gs = eng.slots_host()
+    for b in range(B):
+        st = dec.slots[b]
+        assert gen[b] == st.generated, b
+        assert gs[b]["meter_n"] == st.meter_n and st.meter_n > 0
+        np.testing.assert_allclose(gs[b]["meter_sum"], st.meter_sum, rtol=1e-5, atol=1e-9)

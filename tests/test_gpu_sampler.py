@@ -58,7 +58,7 @@ def _case(B, N, V, T, propose, seed, states, max_new=None):
     return dict(p=p, q=q.reshape(B * (N - 1), V), L=L, t=t, pending=pending, slots=slots, states=states, mx=mx)
 
 
-def _run_gpu(cs, N, T, propose, seed):
+def _run_gpu(cs, N, T, propose, seed, meter=False):
     from strided_decoding_amd import sample
     B = cs["p"].shape[0]
     slots = torch.from_numpy(cs["slots"]).to(DEV)
@@ -68,12 +68,12 @@ def _run_gpu(cs, N, T, propose, seed):
     nc = torch.zeros(B, dtype=torch.int32, device=DEV)
     na = torch.zeros(B, dtype=torch.int32, device=DEV)
     print(f"sampler case B={B} N={N} V={p.shape[2]} T={T} {propose}", flush=True)
-    sample(slots, p, q, N, T, propose, seed, tok, nc, na)
+    sample(slots, p, q, N, T, propose, seed, tok, nc, na, meter=meter)
     torch.cuda.synchronize()
     return slots.cpu().numpy(), tok.cpu().numpy(), nc.cpu().numpy(), na.cpu().numpy()
 
 
-def _compare(cs, N, T, propose, seed, gpu):
+def _compare(cs, N, T, propose, seed, gpu, meter=False):
     g_slots, g_tok, g_nc, g_na = gpu
     B = cs["p"].shape[0]
     near = 0
@@ -87,7 +87,7 @@ def _compare(cs, N, T, propose, seed, gpu):
         if T > 0 and propose == "sample":
             pq = [sampler.weights_T(cs["q"][b * (N - 1) + i], T)[:2] for i in range(N - 1)]
         out = OI.decide(st, int(cs["L"][b]), int(cs["t"][b]), b, list(cs["pending"][b]), pq, cs["p"][b], N, T,
-                        propose, seed)
+                        propose, seed, meter=meter)
         gs = g_slots[b]
         g_pend = list(gs[8:8 + N - 1]) if gs[0] == 1 else None
         div = first_divergence(out.decisions, st, N, g_tok[b, :g_nc[b]], int(g_na[b]), g_pend)
@@ -103,6 +103,10 @@ def _compare(cs, N, T, propose, seed, gpu):
         assert list(g_tok[b, :len(toks)]) == toks, (b, g_tok[b], toks)
         assert np.all(g_tok[b, len(toks):] == -1)
         assert g_na[b] == out.n_accept
+        if meter:
+            g_msum = gs[26:28].copy().view(np.float64)[0]
+            assert gs[28] == out.meter_n and out.meter_n == (N - 1 if st == "A" else 0)
+            np.testing.assert_allclose(g_msum, out.meter_sum, rtol=1e-6, atol=1e-12)
         assert gs[1] == out.new_L and gs[2] == out.new_c and gs[3] == cs["t"][b] + 1
         done = 1 + len(toks) >= cs["mx"][b]
         exp_state = 3 if done else ST[out.new_state]
@@ -148,3 +152,15 @@ def test_sampler_full_vocab_microbench(propose):
     B, N, V = 64, 4, 151936
     cs = _case(B, N, V, 1.0, propose, 5, ["A"] * B)
     _compare(cs, N, 1.0, propose, 1, _run_gpu(cs, N, 1.0, propose, 1))
+
+
+@pytest.mark.parametrize("T,propose", [(1.0, "sample"), (1.0, "argmax"), (0.0, "argmax")])
+def test_sampler_meter_mode(T, propose):
+    """Introspective acceptance meter: pending tokens are committed untested and their
+    acceptance probabilities (min(1, p/q), p(x) for argmax proposals, argmax agreement at
+    T = 0) accumulate in the slot record, as in the oracle."""
+    B, N, V = 32, 4, 5000
+    rng = np.random.default_rng(2)
+    states = list(rng.choice(["A", "A", "B", "DONE"], size=B))
+    cs = _case(B, N, V, T, propose, 6, states)
+    _compare(cs, N, T, propose, 1, _run_gpu(cs, N, T, propose, 1, meter=True), meter=True)

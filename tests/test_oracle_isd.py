@@ -227,3 +227,89 @@ def test_page_invariants_during_decoding():
         lens = {s: (st.L if st.state != isd.STATE_DONE else 0) for s, st in dec.slots.items()}
         dec.pool.check(lens)
     assert dec.pool.n_free == 64
+
+
+def _meter_run(m, N, T, propose, n_new=30):
+    """Meter-mode decode of two prompts; returns (decoder, {slot: [(position, token)] of the
+    re-scored pending tokens})."""
+    ps = I.ragged_prompts([7, 12], m.spec.vocab, seed=13)
+    dec = isd.Decoder(m, N, T, propose=propose, seed=6, page_size=4, meter=True)
+    dec.prefill([0, 1], ps, [n_new, n_new])
+    scored = {0: [], 1: []}
+    for _ in range(40):
+        if all(st.state == isd.STATE_DONE for st in dec.slots.values()):
+            break
+        for s, r in dec.step().items():
+            scored[s] += [(d.position, d.token) for d in r.decisions if d.kind == "accept"]
+    return dec, scored
+
+
+def _extended(committed, scored):
+    """The committed sequence followed by the re-scored tokens that max_new dropped (the last
+    pass re-scores its pending tokens before the output is truncated)."""
+    seq = list(committed)
+    for pos, tok in sorted(scored):
+        if pos == len(seq):
+            seq.append(tok)
+    return seq
+
+
+@pytest.mark.parametrize("sticky", STICKY)
+@pytest.mark.parametrize("N", [2, 4])
+def test_meter_greedy_counts_ar_agreement(N, sticky):
+    """At T = 0 the meter counts the re-scored tokens equal to the AR greedy token of their
+    prefix, recomputed here by one full forward of the committed sequence."""
+    m = _model(sticky=sticky)
+    dec, scored = _meter_run(m, N, 0.0, "argmax")
+    total = 0
+    for s, st in dec.slots.items():
+        seq = _extended(st.committed, scored[s])
+        logits, _ = m.forward(seq, np.arange(len(seq)), M.empty_cache(m.spec))
+        agree = sum(1 for pos, tok in scored[s] if seq[pos] == tok and tok == int(np.argmax(logits[pos - 1])))
+        assert st.meter_n == len(scored[s]) and st.meter_n > 0
+        assert st.meter_sum == agree
+        total += agree
+    if sticky is not None:
+        assert total > 0                # the sticky model's own proposals are often AR tokens
+
+
+@pytest.mark.parametrize("sticky", STICKY)
+def test_meter_argmax_proposals_sum_ar_probabilities(sticky):
+    """At T = 1 with argmax proposals (q = delta) the meter sums p(x), the AR probability of
+    each re-scored token given its prefix (one full forward of the committed sequence)."""
+    m = _model(sticky=sticky)
+    dec, scored = _meter_run(m, 3, 1.0, "argmax")
+    for s, st in dec.slots.items():
+        seq = _extended(st.committed, scored[s])
+        logits, _ = m.forward(seq, np.arange(len(seq)), M.empty_cache(m.spec))
+        want = 0.0
+        for pos, tok in scored[s]:
+            assert seq[pos] == tok
+            z = logits[pos - 1].astype(np.float64)
+            p = np.exp(z - z.max())
+            want += p[tok] / p.sum()
+        assert st.meter_n == len(scored[s]) and st.meter_n > 0
+        np.testing.assert_allclose(st.meter_sum, want, rtol=1e-5)
+
+
+def test_meter_commits_the_models_own_proposals():
+    """Meter mode never rejects: after the first pass every pass commits N tokens, the
+    pending tokens of the previous pass followed by the new z_1."""
+    m = _model()
+    N = 4
+    ps = I.ragged_prompts([9], m.spec.vocab, seed=14)
+    dec = isd.Decoder(m, N, 1.0, propose="sample", seed=8, page_size=4, meter=True)
+    dec.prefill([0], ps, [60])
+    first = True
+    while dec.slots[0].state != isd.STATE_DONE:
+        st = dec.slots[0]
+        pend = list(st.pending)
+        r = dec.step()[0]
+        if first:
+            assert len(r.tokens) == 1
+            first = False
+            continue
+        if dec.slots[0].state == isd.STATE_DONE:
+            break
+        assert r.tokens[:N - 1] == pend and len(r.tokens) == N
+    assert dec.slots[0].meter_n > 0 and 0.0 <= dec.slots[0].meter_sum <= dec.slots[0].meter_n
