@@ -173,8 +173,39 @@ struct GemmArgs {
   // Split-K (splits > 1) only: leave the fp32 partials for the consumer (the fused QKV reduce
   // in rope_append) instead of reducing them into C.
   int keep_part;
+  // Fused LoRA expand (bf16 kernels; lora_r = 0: off).  For an output row m with
+  // lora_rows[m] >= 0 the product runs over lora_r more k values: row lora_rows[m] of lora_a
+  // (bf16, row stride ld_la) times the packed lora_b0 [N, lora_r]; rows with lora_rows[m] < 0
+  // add exact zeros.  Column segment i ([lora_seg_end[i-1], lora_seg_end[i])) reads lora_a
+  // columns i*lora_r ..; SwiGLU: the gate block reads columns 0 .. with lora_b0, then the up
+  // block columns lora_r .. with lora_b1.  The extra k-stages belong to the last split.
+  const int32_t* lora_rows;
+  const void* lora_a;
+  int ld_la;
+  const void* lora_b0;
+  const void* lora_b1;
+  int lora_r;
+  int lora_nseg;
+  int lora_seg_end[3];
 };
 enum { GEMM_PATH_AUTO = 0, GEMM_PATH_TILED = 1, GEMM_PATH_SKINNY = 2 };
+
+// Fused-LoRA stage plan of a workgroup: its number of extra k-stages (32 k each) and, for
+// extra stage ls, the lora_a column offset and the group (SwiGLU: 0 gate, 1 up; else 0).
+struct LoraPlan {
+  int n = 0, per = 0, seg_off = 0;
+};
+ISD_DEV LoraPlan lora_plan(const GemmArgs& a, int n0, bool dual, bool last_split) {
+  LoraPlan p;
+  if (a.lora_r <= 0 || !last_split) return p;
+  p.per = a.lora_r / 32;
+  p.n = dual ? 2 * p.per : p.per;
+  int seg = 0;
+  for (int j = 0; j + 1 < a.lora_nseg; ++j)
+    if (n0 >= a.lora_seg_end[j]) seg = j + 1;
+  p.seg_off = seg * a.lora_r;
+  return p;
+}
 constexpr int kSkinnyMaxRows = 128;  // the skinny kernel holds at most four 32-row MFMA tiles
 
 // A column offset of the output columns starting at n0 (segmented products; 0 otherwise).

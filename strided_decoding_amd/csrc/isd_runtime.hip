@@ -304,10 +304,13 @@ GemmArgs gargs(const void* A, int lda, const void* B0, int ldb, int M, int N, in
 
 // LoRA of nt targets sharing one input on the MASK rows (targets t0 .. t0+nt-1, output widths
 // n[j]): S[:, j r .. (j+1) r] = X[mask_rows] A_j^T, then delta[:, o_j .. o_j + n_j] = S_j B_j^T with
-// o_j = n_0 + .. + n_{j-1}.  When the targets' A (and B) matrices are stacked in memory the
-// shrinks run as one product and the expands as one segmented product.
+// o_j = n_0 + .. + n_{j-1}, added to the MASK rows of `base`, the group's projection.  When the
+// targets' A (and B) matrices are stacked in memory the shrinks run as one product; on the
+// bf16 path with stacked B the expand is fused into `base` itself (its MASK rows run r more k
+// values over S and B, the other rows add zeros), else it runs as separate products into an
+// fp32 delta that base's epilogue adds.
 isd_status lora_group(isd_ctx& x, int layer, int t0, int nt, const void* Xsrc, int ldx, int k_in, const int* n,
-                      hipStream_t s) {
+                      hipStream_t s, GemmArgs& base) {
   const int r = x.cfg.lora_rank, M = x.n_mask;
   const char* const* A = (const char* const*)&x.lora_a[(size_t)layer * 7 + t0];
   const char* const* Bm = (const char* const*)&x.lora_b[(size_t)layer * 7 + t0];
@@ -323,6 +326,22 @@ isd_status lora_group(isd_ctx& x, int layer, int t0, int nt, const void* Xsrc, i
     g.C = (char*)x.lora_s + (size_t)j * r * x.act;
     g.ldc = 3 * r;
     TIMED("lora_shrink", gemm(x, g, s));
+  }
+  if (stackB && r % 32 == 0) {
+    base.lora_rows = x.delta_row;
+    base.lora_a = x.lora_s;
+    base.ld_la = 3 * r;
+    base.lora_r = r;
+    base.lora_b0 = Bm[0];
+    if (base.epi == EPI_SWIGLU) {
+      base.lora_b1 = Bm[1];
+      base.lora_nseg = 1;
+    } else {
+      base.lora_nseg = nt;
+      int o = 0;
+      for (int j = 0; j < nt; ++j) base.lora_seg_end[j] = (o += n[j]);
+    }
+    return ISD_OK;
   }
   int o = 0;
   for (int j = 0; j < nt; ++j) {
@@ -344,15 +363,13 @@ isd_status lora_group(isd_ctx& x, int layer, int t0, int nt, const void* Xsrc, i
     TIMED("lora_expand", gemm(x, e, s));
     o += n_out;
   }
+  base.delta = x.lora_delta;
+  base.delta_row = x.delta_row;
+  base.ldd = x.delta_w;
+  if (base.epi == EPI_SWIGLU) base.delta_off2 = n[0];
   return ISD_OK;
 }
 
-void with_delta(const isd_ctx& x, GemmArgs& g, bool on) {
-  if (!on) return;
-  g.delta = x.lora_delta;
-  g.delta_row = x.delta_row;
-  g.ldd = x.delta_w;
-}
 
 // The transformer body over M rows.  decode: split-context attention over the decode items;
 // prefill: one pass per item.  lm_rows: rows fed to the LM head (gather list or null = all).
@@ -371,16 +388,15 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
       if (x.bf) TIMED("rmsnorm", launch_rmsnorm<bf16>(x.X, (const bf16*)x.attn_norm[0], (bf16*)x.Xn, M, d, c.rms_eps, s));
       else TIMED("rmsnorm", launch_rmsnorm<float>(x.X, (const float*)x.attn_norm[0], (float*)x.Xn, M, d, c.rms_eps, s));
     }
-    if (lora) {
-      const int n[3] = {x.qd, x.kd, x.kd};
-      isd_status st = lora_group(x, l, 0, 3, x.Xn, d, d, n, s);
-      if (st != ISD_OK) return st;
-    }
     // QKV projection; with split-K its partials are reduced by rope_append itself
     GemmArgs gq = plan_gemm(x, gargs(x.Xn, d, x.wqkv[l], d, M, x.qkvw, d, EPI_STORE));
     gq.C = x.QKV;
     gq.ldc = x.qkvw;
-    with_delta(x, gq, lora);
+    if (lora) {
+      const int n[3] = {x.qd, x.kd, x.kd};
+      isd_status st = lora_group(x, l, 0, 3, x.Xn, d, d, n, s, gq);
+      if (st != ISD_OK) return st;
+    }
     gq.keep_part = 1;
     if (x.bf) TIMED("gemm_qkv", launch_gemm_bf16(gq, s));
     else TIMED("gemm_qkv", launch_gemm_f32(gq, s));
@@ -445,11 +461,6 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
         TIMED("attention", launch_attn_bf16(aa, s));
       }
     }
-    if (lora) {
-      const int n[1] = {d};
-      isd_status st = lora_group(x, l, 3, 1, x.O, x.qd, x.qd, n, s);
-      if (st != ISD_OK) return st;
-    }
     {
       // O projection + residual, then the FFN input norm of the updated rows
       GemmArgs g = gargs(x.O, x.qd, x.wo[l], x.qd, M, d, x.qd, EPI_RESID);
@@ -458,28 +469,25 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
       g.norm_g = x.ffn_norm[l];
       g.norm_out = x.Xn;
       g.norm_eps = c.rms_eps;
-      with_delta(x, g, lora);
+      if (lora) {
+        const int n[1] = {d};
+        isd_status st = lora_group(x, l, 3, 1, x.O, x.qd, x.qd, n, s, g);
+        if (st != ISD_OK) return st;
+      }
       TIMED("gemm_o", gemm(x, g, s));
     }
     // FFN block
-    if (lora) {
-      const int n[2] = {F, F};
-      isd_status st = lora_group(x, l, 4, 2, x.Xn, d, d, n, s);
-      if (st != ISD_OK) return st;
-    }
     {
       GemmArgs g = gargs(x.Xn, d, x.wg[l], d, M, F, d, EPI_SWIGLU);
       g.B1 = x.wu[l];
       g.C = x.H;
       g.ldc = F;
-      with_delta(x, g, lora);
-      g.delta_off2 = F;
+      if (lora) {
+        const int n[2] = {F, F};
+        isd_status st = lora_group(x, l, 4, 2, x.Xn, d, d, n, s, g);
+        if (st != ISD_OK) return st;
+      }
       TIMED("gemm_gate_up", gemm(x, g, s));
-    }
-    if (lora) {
-      const int n[1] = {d};
-      isd_status st = lora_group(x, l, 6, 1, x.H, F, F, n, s);
-      if (st != ISD_OK) return st;
     }
     {
       // down projection + residual, then the next layer's input norm (the final norm last)
@@ -489,7 +497,11 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
       g.norm_g = l + 1 < c.n_layers ? x.attn_norm[l + 1] : x.final_norm;
       g.norm_out = x.Xn;
       g.norm_eps = c.rms_eps;
-      with_delta(x, g, lora);
+      if (lora) {
+        const int n[1] = {d};
+        isd_status st = lora_group(x, l, 6, 1, x.H, F, F, n, s, g);
+        if (st != ISD_OK) return st;
+      }
       TIMED("gemm_down", gemm(x, g, s));
     }
   }

@@ -19,6 +19,7 @@
 // of 8 and run on the same XCD (one L2).
 // fp32 path: LDS-tiled FMA, same epilogues.
 #include <algorithm>
+#include <type_traits>
 
 #include "isd_common.h"
 
@@ -64,6 +65,11 @@ __device__ __forceinline__ bf16x8_t ld_operand(const uint16_t* p) {
 // whole number of operand-ring rounds (0 x 0 products leave every accumulator unchanged).
 __device__ __attribute__((aligned(1024))) uint16_t kZeroOperand[512] = {};
 
+// How a pipeline step picks its load sources: every stage inside the product (plain
+// addresses), or product / zero stages, or product / fused LoRA / zero stages.
+constexpr int kPlainStages = 0, kZeroTail = 1, kLoraTail = 2;
+template <int M> using StageMode = std::integral_constant<int, M>;
+
 template <typename T, int EPI>
 __device__ __forceinline__ void epilogue_store_t(const GemmArgs& a, int row, int col, float v, float v_up) {
   if (row >= a.M || col >= a.N) return;
@@ -95,7 +101,9 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int EPI, bool PARTIAL>
+// LORA: the instance that can run fused LoRA stages (a separate instance, so that each one
+// holds only two versions of the pipeline loop: a third does not fit the registers)
+template <int EPI, bool PARTIAL, bool LORA>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU);
@@ -109,13 +117,14 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
   const int nt = unit / S, sp = unit % S;
   const int kt_per = (a.K / BK) / S;
   const int kbase = sp * kt_per * BK;
-  // the stage count is rounded up to whole ring rounds with zero stages (indices >= kt_per
-  // load kZeroOperand)
-  const int kt_loop = (kt_per + kBRing - 1) / kBRing * kBRing;
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = nt * TNO, m0 = mt * TM2;
   const uint16_t* zero = kZeroOperand + lane * 8;
+  // stages kt_per .. kt_end-1: the fused LoRA expand (last split only); the stage count is
+  // rounded up to whole ring rounds with zero stages (kZeroOperand)
+  const LoraPlan lp = LORA ? lora_plan(a, n0, DUAL, sp == S - 1) : LoraPlan{};
+  const int kt_end = kt_per + lp.n;
+  const int kt_loop = (kt_end + kBRing - 1) / kBRing * kBRing;
 
   // A loader: wave w fills row groups min(w + 4 i, 13), i < 4, of the 14 (waves 1-3 all refill
   // group 13 with the same bytes, so every wave issues 4 loads per stage).  Lane l writes LDS
@@ -125,28 +134,53 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
   const int chunk = (lane & 3) ^ ((lrow >> 2) & 3);
   const int aoff = gemm_seg_aoff(a, n0);
   const uint16_t* asrc[kALoads];
+  const uint16_t* lsrc[kALoads];         // fused LoRA: the row's lora_a row (null: zeros)
+  {
+    // every row-index load is issued before any is used (one wait, not one per row group)
+    int sr[kALoads], lr[kALoads];
 #pragma unroll
-  for (int i = 0; i < kALoads; ++i) {
-    const int m = m0 + min(wave + 4 * i, AG - 1) * 16 + lrow;
-    int srow = 0;
-    if (m < a.M) {
-      srow = a.a_rows ? a.a_rows[m] : m;
-      if (srow < 0) srow = 0;            // unused row (its outputs are never consumed)
+    for (int i = 0; i < kALoads; ++i) {
+      const int mc = min(m0 + min(wave + 4 * i, AG - 1) * 16 + lrow, a.M - 1);
+      sr[i] = a.a_rows ? a.a_rows[mc] : mc;
+      lr[i] = (LORA && lp.n) ? a.lora_rows[mc] : -1;
     }
-    asrc[i] = (const uint16_t*)a.A + (size_t)srow * a.lda + aoff + kbase + chunk * 8;
+#pragma unroll
+    for (int i = 0; i < kALoads; ++i) {
+      const bool valid = m0 + min(wave + 4 * i, AG - 1) * 16 + lrow < a.M;
+      const int srow = valid ? max(sr[i], 0) : 0;   // unused rows: their outputs are never consumed
+      const int l = valid ? lr[i] : -1;
+      asrc[i] = (const uint16_t*)a.A + (size_t)srow * a.lda + aoff + kbase + chunk * 8;
+      lsrc[i] = l >= 0 ? (const uint16_t*)a.lora_a + (size_t)l * a.ld_la + lp.seg_off + chunk * 8 : nullptr;
+    }
   }
   // B: this wave's two 32-row operand blocks, straight from the packed weights into registers
   // (one contiguous 1 KB operand per k-step and block).  Block j is output columns
   // n0 + 64 w + 32 j .. (SwiGLU: gate block j = 0 and up block j = 1 of columns n0 + 32 w ..).
   const uint16_t* bsrc[2];
+  const uint16_t* lbsrc[2];              // fused LoRA: the packed lora_b blocks of the same columns
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     int nb = DUAL ? (n0 >> 5) + wave : (n0 >> 5) + 2 * wave + j;
     nb = min(nb, ((a.N + 31) >> 5) - 1);        // past the last block: outputs are discarded
     bsrc[j] = packed_operand((const uint16_t*)(DUAL && j ? a.B1 : a.B0), nb, a.K, kbase / 16, lane);
+    lbsrc[j] = packed_operand((const uint16_t*)(DUAL && j ? a.lora_b1 : a.lora_b0), nb, a.lora_r, 0, lane);
   }
+  // stage kt's sources: the product, then the LoRA stages, then zeros.  LoRA stage ls reads
+  // k-step ls of the row's lora_a segment (SwiGLU: the gate and up halves follow each other, so
+  // the offset is ls BK for both) and, per weight block j, its own k-step ls - j per (SwiGLU:
+  // gate stages 0 .. per-1, up stages per .. 2 per-1; the other block's operand is zero).
+  auto a_src = [&](int i, int kt) {
+    const int ls = kt - kt_per;
+    const uint16_t* l = (ls >= 0 && ls < lp.n && lsrc[i]) ? lsrc[i] + ls * BK : zero;
+    return kt < kt_per ? asrc[i] + kt * BK : l;
+  };
+  auto b_src = [&](int j, int kt, int kk) {
+    const int lk = kt - kt_per - (DUAL ? j * lp.per : 0);
+    const uint16_t* l = (lk >= 0 && lk < (DUAL ? lp.per : lp.n)) ? lbsrc[j] + (2 * lk + kk) * 512 : zero;
+    return kt < kt_per ? bsrc[j] + (2 * kt + kk) * 512 : l;
+  };
   auto a_dma = [&](int i, uint8_t* st, int kt) {
-    __builtin_amdgcn_global_load_lds((const void*)(kt < kt_per ? asrc[i] + kt * BK : zero),
+    __builtin_amdgcn_global_load_lds((const void*)a_src(i, kt),
                                      (lds_void*)(st + min(wave + 4 * i, AG - 1) * GROUP_BYTES), 16, 0, 0);
   };
   // operand ring: stage kt's B fragments in slot kt % kBRing, loaded kBDepth stages ahead
@@ -155,7 +189,7 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) bq[slot][j][kk] = ld_operand(kt < kt_per ? bsrc[j] + (2 * kt + kk) * 512 : zero);
+      for (int kk = 0; kk < 2; ++kk) bq[slot][j][kk] = ld_operand(b_src(j, kt, kk));
   };
   f32x16_t acc[7][2];
 #pragma unroll
@@ -199,7 +233,10 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
   // with the LDS reads of the next k-step's A operands, the refill of the A slot of stage kt-1
   // (every wave finished it before the barrier) and the B loads of stage kt+kBDepth into the
   // ring slot of stage kt-1; a half ends by waiting for its LDS reads.
-  for (int kt0 = 0; kt0 < kt_loop; kt0 += kBRing) {
+  // The rounds whose loads all fall inside the product run with plain addresses; the last
+  // rounds select zero stages (no fused LoRA) or the LoRA and zero stages.
+  auto round = [&](auto mode, int kt0) {
+    constexpr int MODE = decltype(mode)::value;
 #pragma unroll
     for (int d = 0; d < kBRing; ++d) {
       const int kt = kt0 + d;
@@ -216,10 +253,20 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
           acc[m >> 1][m & 1] = mfma32x32x16(x0[m >> 1], bq[d][m & 1][0], acc[m >> 1][m & 1]);
           __builtin_amdgcn_sched_barrier(0);
           if (m < 7) x1[m] = frag(kt, 1, m);
-          if (m >= 1 && m <= kALoads) a_dma(m - 1, dst, ka);
+          if (m >= 1 && m <= kALoads) {
+            const int q = m - 1;
+            const uint16_t* src = MODE == kPlainStages ? asrc[q] + ka * BK
+                                : MODE == kZeroTail   ? (ka < kt_per ? asrc[q] + ka * BK : zero)
+                                                      : a_src(q, ka);
+            __builtin_amdgcn_global_load_lds((const void*)src,
+                                             (lds_void*)(dst + min(wave + 4 * q, AG - 1) * GROUP_BYTES), 16, 0, 0);
+          }
           if (m >= 6 && m < 10) {
             const int j = (m - 6) >> 1, kk = (m - 6) & 1;
-            bq[nslot][j][kk] = ld_operand(kb < kt_per ? bsrc[j] + (2 * kb + kk) * 512 : zero);
+            const uint16_t* src = MODE == kPlainStages ? bsrc[j] + (2 * kb + kk) * 512
+                                : MODE == kZeroTail   ? (kb < kt_per ? bsrc[j] + (2 * kb + kk) * 512 : zero)
+                                                      : b_src(j, kb, kk);
+            bq[nslot][j][kk] = ld_operand(src);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -237,7 +284,11 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
       }
       wait_lgkm0();
     }
-  }
+  };
+  const int fast_end = max(0, (kt_per - (kNsA - 1)) / kBRing * kBRing);
+  int kt0 = 0;
+  for (; kt0 < fast_end; kt0 += kBRing) round(StageMode<kPlainStages>{}, kt0);
+  for (; kt0 < kt_loop; kt0 += kBRing) round(StageMode<LORA ? kLoraTail : kZeroTail>{}, kt0);
   wait_vmcnt<0>();                                 // the loads past the last stage
 
   // Epilogue through LDS: each wave's 224 x 64 fp32 tile is staged row-major (rows padded to
@@ -369,6 +420,9 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_
   const int n0 = nt * TNO;
   const int r32 = lane & 31, khi = lane >> 5;
   const uint16_t* zero = kZeroOperand + lane * 8;
+  // stages kt_per .. kt_end-1: the fused LoRA expand (last split only)
+  const LoraPlan lp = lora_plan(a, n0, DUAL, sp == S - 1);
+  const int kt_end = kt_per + lp.n;
 
   // Activation loader (the tiled kernel's 16-row group layout): one direct load per 16-row
   // group and stage; lane l fills LDS bytes [16 l, 16 l + 16) of the group with row l/4,
@@ -377,44 +431,69 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_
   const int chunk = (lane & 3) ^ ((lrow >> 2) & 3);
   const int aoff = gemm_seg_aoff(a, n0);
   const uint16_t* xsrc[MT][2];
+  const uint16_t* lsrc[MT][2];              // fused LoRA: the row's lora_a row (null: zeros)
+  {
+    // every row-index load is issued before any is used (one wait, not one per row group)
+    int sr[MT][2], lr[MT][2];
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const int m = 32 * i + 16 * g + lrow;
-      int srow = 0;
-      if (m < a.M) {
-        srow = a.a_rows ? a.a_rows[m] : m;
-        if (srow < 0) srow = 0;               // unused row (its outputs are never consumed)
+      for (int g = 0; g < 2; ++g) {
+        const int mc = min(32 * i + 16 * g + lrow, a.M - 1);
+        sr[i][g] = a.a_rows ? a.a_rows[mc] : mc;
+        lr[i][g] = lp.n ? a.lora_rows[mc] : -1;
       }
-      xsrc[i][g] = (const uint16_t*)a.A + (size_t)srow * a.lda + aoff + kbase + chunk * 8;
-    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const bool valid = 32 * i + 16 * g + lrow < a.M;
+        const int srow = valid ? max(sr[i][g], 0) : 0;   // unused rows: their outputs are never consumed
+        const int l = valid ? lr[i][g] : -1;
+        xsrc[i][g] = (const uint16_t*)a.A + (size_t)srow * a.lda + aoff + kbase + chunk * 8;
+        lsrc[i][g] = l >= 0 ? (const uint16_t*)a.lora_a + (size_t)l * a.ld_la + lp.seg_off + chunk * 8 : nullptr;
+      }
+  }
   // weight operand blocks: columns n0 + 32 j .. (SwiGLU: gate j = 0 and up j = 1 of n0 ..)
   const uint16_t* wsrc[NB];
+  const uint16_t* lwsrc[NB];                // fused LoRA: the packed lora_b blocks of the same columns
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const int nb = min(DUAL ? (n0 >> 5) : (n0 >> 5) + j, ((a.N + 31) >> 5) - 1);
     wsrc[j] = packed_operand((const uint16_t*)((DUAL && j) ? a.B1 : a.B0), nb, a.K, kbase / 16, lane);
+    lwsrc[j] = packed_operand((const uint16_t*)((DUAL && j) ? a.lora_b1 : a.lora_b0), nb, a.lora_r, 0, lane);
   }
 
   // stage kt -> ring slot kt % SD: activation tile t, row group g at + (2 t + g) KB, then the
   // weight operand of block j and k-step kk at + (2 MT + 2 j + kk) KB.  Stages past the last
   // one load zeros.
-  auto issue = [&](int kt) {
+  // (stages kt_per .. kt_end-1 are the LoRA stages: SwiGLU per gate of the up group, with the
+  // other block's operand zero; later stages load zeros)
+  // MODE: a stage inside the product (plain addresses), or any stage without (kZeroTail) or
+  // with (kLoraTail) fused LoRA stages
+  auto issue = [&](auto mode, int kt) {
+    constexpr int MODE = decltype(mode)::value;
     uint8_t* st = smem + (kt % SD) * STAGE;
-    const bool live = kt < kt_per;
+    const bool live = MODE == kPlainStages || kt < kt_per;
+    const int ls = kt - kt_per;                 // LoRA stage offsets as in the tiled kernel
+    const bool lora = ls >= 0 && ls < lp.n;
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
-        __builtin_amdgcn_global_load_lds((const void*)(live ? xsrc[t][g] + kt * BK : zero),
+      for (int g = 0; g < 2; ++g) {
+        const uint16_t* l = (MODE == kLoraTail && lora && lsrc[t][g]) ? lsrc[t][g] + ls * BK : zero;
+        __builtin_amdgcn_global_load_lds((const void*)(live ? xsrc[t][g] + kt * BK : l),
                                          (lds_void*)(st + (2 * t + g) * 1024), 16, 0, 0);
+      }
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        __builtin_amdgcn_global_load_lds((const void*)(live ? wsrc[j] + (2 * kt + kk) * 512 : zero),
+      for (int kk = 0; kk < 2; ++kk) {
+        const int lk = ls - (DUAL ? j * lp.per : 0);
+        const uint16_t* l = (MODE == kLoraTail && lk >= 0 && lk < (DUAL ? lp.per : lp.n)) ? lwsrc[j] + (2 * lk + kk) * 512 : zero;
+        __builtin_amdgcn_global_load_lds((const void*)(live ? wsrc[j] + (2 * kt + kk) * 512 : l),
                                          (lds_void*)(st + (2 * MT + 2 * j + kk) * 1024), 16, 0, 0);
+      }
   };
   f32x16_t acc[MT][NB];
 #pragma unroll
@@ -446,13 +525,27 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_
 
   // Stage kt is issued SD-1 steps before it is multiplied; before multiplying it, at most the
   // loads of the stages issued after it may be outstanding.
-  for (int kt = 0; kt < SD - 1; ++kt) issue(kt);
-  for (int kt = 0; kt < kt_per; ++kt) {
-    issue(kt + SD - 1);
+  for (int kt = 0; kt < SD - 1; ++kt) issue(StageMode<kLoraTail>{}, kt);
+  const int fast_end = max(0, kt_per - (SD - 1));   // steps whose issued stage is a product stage
+  int kt = 0;
+  for (; kt < fast_end; ++kt) {
+    issue(StageMode<kPlainStages>{}, kt + SD - 1);
     wait_vmcnt<(SD - 1) * PER_STAGE>();
     mul(kt);
     __builtin_amdgcn_sched_barrier(0);
   }
+  auto tail = [&](auto mode) {
+    for (; kt < kt_end; ++kt) {
+      issue(mode, kt + SD - 1);
+      wait_vmcnt<(SD - 1) * PER_STAGE>();
+      mul(kt);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  if (lp.n == 0)
+    tail(StageMode<kZeroTail>{});
+  else
+    tail(StageMode<kLoraTail>{});
   wait_vmcnt<0>();                               // the loads past the last stage
 
   // The MASK-row LoRA delta of a row tile is loaded before any of its stores, so that the
@@ -667,10 +760,17 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
   const int units = n_nt * S;
   dim3 grid(((units + 7) / 8) * 8 * n_mt);
   // the full B ring when the stage count of a split allows it, else a two-stage ring
-  if (S > 1)
-    hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, true>), grid, dim3(256), 0, s, a, n_mt, units, S, a.part);
-  else
-    hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, false>), grid, dim3(256), 0, s, a, n_mt, units, 1, nullptr);
+#define ISD_BIG(P, L) \
+  hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, P, L>), grid, dim3(256), 0, s, a, n_mt, units, S, P ? a.part : nullptr)
+  const bool lora = a.lora_r > 0;
+  if (S > 1) {
+    if (lora) ISD_BIG(true, true);
+    else ISD_BIG(true, false);
+  } else {
+    if (lora) ISD_BIG(false, true);
+    else ISD_BIG(false, false);
+  }
+#undef ISD_BIG
   return finish<EPI>(a, S, s);
 }
 
@@ -733,6 +833,13 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.nseg < 0 || a.nseg > 3 || (a.nseg > 1 && (S > 1 || a.epi == EPI_SWIGLU))) return hipErrorInvalidValue;
   for (int j = 0; j + 1 < a.nseg; ++j)
     if (a.seg_end[j] % TN2) return hipErrorInvalidValue;
+  if (a.lora_r > 0) {
+    if (a.lora_r % BK || !a.lora_rows || !a.lora_a || !a.lora_b0 || (a.epi == EPI_SWIGLU && !a.lora_b1))
+      return hipErrorInvalidValue;
+    if (a.lora_nseg < 1 || a.lora_nseg > 3 || (a.epi == EPI_SWIGLU && a.lora_nseg != 1)) return hipErrorInvalidValue;
+    for (int j = 0; j + 1 < a.lora_nseg; ++j)
+      if (a.lora_seg_end[j] % TN2) return hipErrorInvalidValue;
+  }
   switch (a.epi) {
     case EPI_STORE: return launch_path<EPI_STORE>(a, s);
     case EPI_STORE_F32: return launch_path<EPI_STORE_F32>(a, s);
