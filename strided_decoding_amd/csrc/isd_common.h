@@ -230,6 +230,26 @@ namespace isd {
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
 // bf16 weights of the GEMMs are in the packed operand layout (k_gemm.hip): elements of a
 // packed [rows, cols] matrix, and the conversion from row-major
+// MASK-row LoRA shrink: out[m, 0:N] = X[rows[m], 0:K] A^T in bf16 (A packed bf16 [N, K],
+// N % 32 == 0, K % 128 == 0, K <= 32768; rows[m] < 0: the output row is unused).  One launch; with
+// lora_shrink_splits(K) > 1 k-splits it needs part (>= splits * M * N floats) and cnt
+// (>= ceil(M / 64) * N / 32 counters, zero before the first call and left zero by every call).
+struct ShrinkArgs {
+  const void* X;
+  int ldx;
+  const int32_t* rows;
+  int M;
+  const void* A;
+  int N, K;
+  void* out;
+  int ldo;
+  float* part;
+  size_t part_floats;
+  int32_t* cnt;
+  int n_cnt;
+};
+int lora_shrink_splits(int K);
+hipError_t launch_lora_shrink(const ShrinkArgs& a, hipStream_t s);
 size_t packed_weight_elems(int rows, int cols);
 hipError_t launch_pack_weights(const void* src, void* dst, int rows, int cols, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
@@ -310,6 +330,8 @@ struct StepMeta {            // device buffers of the block / page machinery
   int items_per_slot, q_max;   // decode: attention items per slot, query positions per item
   int max_batch, N, P, mask_id;
   int32_t* last_rows;        // prefill: last row of each prompt
+  int32_t* zero_words;       // cleared once at init (arrival counters)
+  int n_zero_words;
 };
 hipError_t launch_init_state(const StepMeta& m, int n_pages, hipStream_t s);
 hipError_t launch_assemble(const StepMeta& m, hipStream_t s);

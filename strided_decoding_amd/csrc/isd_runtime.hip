@@ -69,6 +69,8 @@ struct isd_ctx {
   float *cos_t = nullptr, *sin_t = nullptr;
   void* lora_s = nullptr;
   float* lora_delta = nullptr;
+  int32_t* tile_cnt = nullptr;  // arrival counters of the k-split LoRA shrink
+  int n_cnt = 0;
   int cur = 0;            // logits buffer the next pass writes
   bool prefilled = false;
   std::vector<long long> reserved;   // admission reservation per slot (pages)
@@ -185,6 +187,7 @@ size_t carve(isd_ctx& x, char* base) {
   if (c.lora_rank > 0) {
     x.lora_s = cv.take<char>((size_t)std::max(1, x.n_mask) * 3 * c.lora_rank * x.act);
     x.lora_delta = cv.take<float>((size_t)std::max(1, x.n_mask) * x.delta_w);
+    x.tile_cnt = cv.take<int32_t>(x.n_cnt);
   }
   return align_up(cv.off);
 }
@@ -220,12 +223,17 @@ void derive(isd_ctx& x) {
     };
     size_t p = std::max({need(M, x.qkvw, d, false), need(M, d, x.qd, false), need(M, F, d, true),
                          need(M, d, F, false), need(M, c.vocab, d, false)});
-    if (c.lora_rank > 0)
+    if (c.lora_rank > 0) {
       p = std::max({p, need(Mm, 3 * r, d, false), need(Mm, 2 * r, d, false), need(Mm, r, d, false),
                     need(Mm, r, x.qd, false), need(Mm, r, F, false)});
+      // the single-launch shrink: lora_shrink_splits(K) partials of the stacked width
+      p = std::max({p, (size_t)lora_shrink_splits(d) * Mm * 3 * r, (size_t)lora_shrink_splits(x.qd) * Mm * r,
+                    (size_t)lora_shrink_splits(F) * Mm * r});
+    }
     x.part_floats = x.bf ? p : 0;
   }
   x.kv_layer_bytes = (size_t)c.n_pages * x.kd * c.page_size * x.act;
+  x.n_cnt = c.lora_rank > 0 ? cdiv(std::max(1, x.n_mask), 32) * cdiv(3 * c.lora_rank, 32) : 0;
 }
 
 StepMeta meta(isd_ctx& x) {
@@ -249,6 +257,8 @@ StepMeta meta(isd_ctx& x) {
   m.P = x.cfg.page_size;
   m.mask_id = x.cfg.vocab;
   m.last_rows = x.last_rows;
+  m.zero_words = x.tile_cnt;
+  m.n_zero_words = x.n_cnt;
   return m;
 }
 
@@ -321,7 +331,26 @@ isd_status lora_group(isd_ctx& x, int layer, int t0, int nt, const void* Xsrc, i
   }
   for (int j = 0; j < nt; ++j) {
     if (j > 0 && stackA) break;
-    GemmArgs g = gargs(Xsrc, ldx, A[j], k_in, M, stackA ? nt * r : r, k_in, EPI_STORE);
+    const int ncols = stackA ? nt * r : r;
+    if (x.bf && k_in % 128 == 0 && lora_shrink_splits(k_in) <= 32 && ncols % 32 == 0 && x.tile_cnt) {
+      ShrinkArgs sa{};
+      sa.X = Xsrc;
+      sa.ldx = ldx;
+      sa.rows = x.mask_rows;
+      sa.M = M;
+      sa.A = A[j];
+      sa.N = ncols;
+      sa.K = k_in;
+      sa.out = (char*)x.lora_s + (size_t)j * r * x.act;
+      sa.ldo = 3 * r;
+      sa.part = x.gemm_part;
+      sa.part_floats = x.part_floats;
+      sa.cnt = x.tile_cnt;
+      sa.n_cnt = x.n_cnt;
+      TIMED("lora_shrink", launch_lora_shrink(sa, s));
+      continue;
+    }
+    GemmArgs g = gargs(Xsrc, ldx, A[j], k_in, M, ncols, k_in, EPI_STORE);
     g.a_rows = x.mask_rows;
     g.C = (char*)x.lora_s + (size_t)j * r * x.act;
     g.ldc = 3 * r;

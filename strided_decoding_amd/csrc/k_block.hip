@@ -333,6 +333,7 @@ __global__ void init_state_kernel(StepMeta m, int n_pages) {
   for (size_t i = t0; i < (size_t)m.max_batch * m.max_pages; i += stride) m.page_table[i] = -1;
   int32_t* sw = (int32_t*)m.slots;
   for (size_t i = t0; i < (size_t)m.max_batch * (sizeof(isd_slot) / 4); i += stride) sw[i] = 0;
+  for (size_t i = t0; i < (size_t)m.n_zero_words; i += stride) m.zero_words[i] = 0;
   if (t0 == 0) *m.n_free = n_pages;
 }
 

@@ -202,6 +202,18 @@ def test_lora_mask_rows_end_to_end(dtype):
                        rel=True, on_gpu_logits=True)
 
 
+def test_lora_split_shrink_end_to_end():
+    """The MASK-row shrink as several k-splits: at d_model 2048 and d_ffn 4096 the q/k/v and
+    gate/up shrinks run as 2 splits and the down shrink as 4, summed by the last workgroup of
+    each tile to arrive; the GPU logits of every row follow the oracle's."""
+    shape = I.ModelShape("mid-bf16", 1, 2048, 16, 4, 128, 4096, 4096, "bf16")
+    w = I.weights_numpy(shape, seed=2, scale=20.0)
+    lora = I.lora_numpy(shape, 64, scale=3.0)   # delta of the order of the base projection at d 2048
+    prompts = I.ragged_prompts([19, 33], shape.vocab, seed=15)
+    teacher_forced(shape, w, 4, 1.0, "sample", prompts, [10, 8], steps=6, lora=lora, logits_tol=2e-2, rel=True,
+                   on_gpu_logits=True)
+
+
 @pytest.mark.parametrize("N,T,propose", [(3, 0.0, "argmax"), (4, 1.0, "argmax")])
 def test_meter_mode_end_to_end(N, T, propose):
     """Introspective acceptance meter through isd_step: the model's own proposals are
