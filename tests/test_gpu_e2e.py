@@ -214,6 +214,19 @@ def test_lora_split_shrink_end_to_end():
                    on_gpu_logits=True)
 
 
+def test_lora_8b_widths_end_to_end():
+    """One layer at the 8B shape's widths (d_model 4096, 32 x 128 query heads, 8 KV heads,
+    d_ffn 12288) with the rank-128 adapter: the shrinks run as 4 (q/k/v, o, gate/up) and 12
+    (down) k-splits, the expands are fused into the projections at their real widths, and
+    the GPU logits of every row follow the oracle's."""
+    shape = I.ModelShape("8b-widths-1-layer", 1, 4096, 32, 8, 128, 12288, 4096, "bf16")
+    w = I.weights_numpy(shape, seed=3, scale=20.0)
+    lora = I.lora_numpy(shape, 128, scale=2.0)   # delta of the order of the base projection at d 4096
+    prompts = I.ragged_prompts([17, 29], shape.vocab, seed=16)
+    teacher_forced(shape, w, 4, 1.0, "sample", prompts, [8, 8], steps=4, lora=lora, logits_tol=2e-2, rel=True,
+                   on_gpu_logits=True)
+
+
 @pytest.mark.parametrize("N,T,propose", [(3, 0.0, "argmax"), (4, 1.0, "argmax")])
 def test_meter_mode_end_to_end(N, T, propose):
     """Introspective acceptance meter through isd_step: the model's own proposals are
