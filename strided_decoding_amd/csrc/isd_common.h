@@ -278,9 +278,9 @@ struct AttnArgs {
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_combine_bf16(const AttnArgs& a, hipStream_t s);
 // Keys per context split of a decode pass, from the slots, KV heads and longest context the
-// context serves: about 2048 workgroups at the longest context (short splits when few slots
-// must still fill the chip, long ones when the partials would cost bytes).  Fixed per
-// context, so a row's attention never depends on the other rows of a pass.
+// context serves: 2048 when the (slot, KV head) pairs alone fill the chip, else about 2048
+// workgroups at the longest context (short splits when few slots must still fill the chip).
+// Fixed per context, so a row's attention never depends on the other rows of a pass.
 int attn_split_len(int batch, int n_kv_heads, int max_ctx);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 
