@@ -32,6 +32,13 @@ LoRA per layer and target m in (q, k, v, o, g, u, d):
 Matrices may be float32 arrays or bf16 bit patterns (uint16); the latter are
 widened to float32 (exactly) before use, so the oracle computes in fp32 on the
 same values the bf16 GPU path stores.
+
+Model(..., act_bf16=True) is a precision model of that path, not a second reference:
+activations are rounded to bfloat16 (nearest, ties to even) where the bf16 path stores
+them between kernels (the two RMSNorm outputs of a layer and the final one, q/k/v after
+RoPE and hence the KV cache, the attention output, the SwiGLU product); everything else
+stays fp32.  Its distance from the fp32 forward is the error that bf16 storage alone
+causes, the yardstick for the GPU path's deviation at depth.
 """
 from dataclasses import dataclass
 
@@ -67,6 +74,13 @@ def f32(a):
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << np.uint32(16)).view(np.float32)
     return a.astype(np.float32, copy=False)
+
+
+def round_bf16(x):
+    """float32 -> the nearest bfloat16 value (ties to even), returned as float32 (finite x)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
 
 
 def rmsnorm(x, g, eps):
@@ -155,10 +169,11 @@ class Model:
     weights["layers"][l].  lora: None or list (per layer) of dicts {m: (a, b)}.
     """
 
-    def __init__(self, spec, weights, lora=None):
+    def __init__(self, spec, weights, lora=None, act_bf16=False):
         self.spec = spec
         self.w = weights
         self.lora = lora
+        self.rd = round_bf16 if act_bf16 else (lambda a: a)
 
     def embed(self, ids):
         return f32(self.w["embed"])[np.asarray(ids, dtype=np.int64)].astype(np.float32)
@@ -192,26 +207,28 @@ class Model:
                 a, b = lo[tgt]
                 return _lin(inp, w, a, b, is_mask)
 
-            h = rmsnorm(x, L["attn_norm"], s.rms_eps)
+            rd = self.rd
+            h = rd(rmsnorm(x, L["attn_norm"], s.rms_eps))
             wqkv = f32(L["wqkv"])
             q = lin(h, wqkv[:qd], "q").reshape(R, s.n_q_heads, s.head_dim)
             k = lin(h, wqkv[qd:qd + kd], "k").reshape(R, s.n_kv_heads, s.head_dim)
             v = lin(h, wqkv[qd + kd:], "v").reshape(R, s.n_kv_heads, s.head_dim)
-            q = apply_rope(q, positions, s.rope_base)
-            k = apply_rope(k, positions, s.rope_base)
+            q = rd(apply_rope(q, positions, s.rope_base))
+            k = rd(apply_rope(k, positions, s.rope_base))
+            v = rd(v)
             block_kv.append((k, v))
             ck, cv = cache[li] if cache is not None else (np.zeros((0,) + k.shape[1:], np.float32),) * 2
             k_all = np.concatenate([ck, k], axis=0)
             v_all = np.concatenate([cv, v], axis=0)
             k_pos = np.concatenate([np.arange(len(ck)), positions])
-            o = causal_attention(q, k_all, v_all, positions, k_pos, s.group)
+            o = rd(causal_attention(q, k_all, v_all, positions, k_pos, s.group))
             attn_out.append(o)
             x = x + lin(o.reshape(R, qd), L["wo"], "o")
-            h2 = rmsnorm(x, L["ffn_norm"], s.rms_eps)
+            h2 = rd(rmsnorm(x, L["ffn_norm"], s.rms_eps))
             g = lin(h2, L["wg"], "g")
             u = lin(h2, L["wu"], "u")
-            x = x + lin((silu(g) * u).astype(np.float32), L["wd"], "d")
-        logits = rmsnorm(x, self.w["final_norm"], s.rms_eps) @ f32(self.w["lm_head"]).T
+            x = x + lin(rd((silu(g) * u).astype(np.float32)), L["wd"], "d")
+        logits = self.rd(rmsnorm(x, self.w["final_norm"], s.rms_eps)) @ f32(self.w["lm_head"]).T
         logits = logits.astype(np.float32)
         if return_hidden:
             return logits, block_kv, attn_out

@@ -227,3 +227,31 @@ def test_lora_gating_clean_rows_bit_identical_and_mask_rows_merged():
     g2, _ = m.forward(allmask, np.arange(4), M.empty_cache(m.spec), is_mask=np.ones(4, bool))
     r2, _ = M.Model(m.spec, merged, None).forward(allmask, np.arange(4), M.empty_cache(m.spec))
     np.testing.assert_allclose(g2, r2, atol=2e-5, rtol=1e-4)
+
+
+def test_round_bf16_is_nearest_even():
+    """The precision model's rounding: ties to even on hand-made halfway cases, and torch's
+    float32 -> bfloat16 conversion on random values over many binades."""
+    h = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -20, -(1 + 3 * 2 ** -8)], np.float32)
+    want = np.array([1.0, 1.0, 1 + 2 ** -6, 1 + 2 ** -7, -(1 + 2 ** -6)], np.float32)
+    np.testing.assert_array_equal(M.round_bf16(h), want)
+    g = np.random.default_rng(5)
+    x = (g.standard_normal(100000) * np.exp2(g.integers(-40, 40, 100000))).astype(np.float32)
+    np.testing.assert_array_equal(M.round_bf16(x), torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_act_bf16_mode_rounds_stored_activations():
+    """act_bf16 = True: the attention outputs it reports are bfloat16 values, the KV it returns
+    too, and the logits stay within the bf16 storage error of the fp32 forward."""
+    shape = I.SMALL_BF16
+    w = I.weights_numpy(shape, seed=0)
+    spec = M.Spec(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.d_ffn,
+                  shape.vocab, shape.rope_base, shape.rms_eps)
+    ids = I.ragged_prompts([9], shape.vocab, seed=4)[0]
+    pos = np.arange(len(ids))
+    l32, _ = M.Model(spec, w).forward(ids, pos, M.empty_cache(spec))
+    l16, kv, att = M.Model(spec, w, act_bf16=True).forward(ids, pos, M.empty_cache(spec), return_hidden=True)
+    for a in att + [t for pair in kv for t in pair]:
+        assert not (np.ascontiguousarray(a, np.float32).view(np.uint32) & 0xFFFF).any()
+    err = np.abs(l16 - l32).max() / np.abs(l32).max()
+    assert 0 < err < 2e-2, err
