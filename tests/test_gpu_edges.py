@@ -1,0 +1,119 @@
+"""Edge cases of the decode path through the C ABI: a pass before any prefill, passes over
+slots that are empty or finished, a batch with holes, generation that fills a slot's
+capacity exactly, and admission errors that must leave the context usable.
+
+Greedy decoding (T = 0, argmax proposals) makes a slot's tokens independent of its slot id
+and of the other slots (every kernel computes a row from that row alone), so a slot decoded
+in a batch with holes must produce exactly the tokens of the same prompt decoded alone.
+"""
+import pytest
+import torch
+
+import isd_inputs as I
+from strided_decoding_amd import Engine
+from strided_decoding_amd._abi import IsdError
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+SHAPE = I.SMALL_BF16
+N = 4
+
+
+def _engine(w, B, max_seq=96):
+    return Engine(SHAPE, w, stride=N, temperature=0.0, propose="argmax", seed=1, max_batch=B, max_seq_len=max_seq)
+
+
+def _run(eng, slots, max_steps=200):
+    """Step until every listed slot is DONE; returns each slot's committed tokens and the
+    per-pass commit counts of every slot."""
+    out = {b: [] for b in slots}
+    counts = []
+    for _ in range(max_steps):
+        tok, nc, _ = eng.step()
+        torch.cuda.synchronize()
+        tok, nc = tok.cpu().numpy(), nc.cpu().numpy()
+        counts.append(nc.copy())
+        for b in slots:
+            out[b] += [int(x) for x in tok[b, :nc[b]]]
+        st = eng.slots_host()
+        if all(st[b]["state"] == 3 for b in slots):
+            break
+    return out, counts
+
+
+def test_steps_before_prefill_and_after_every_slot_finished():
+    """A pass before any prefill is refused on the host (ISD_E_STATE, nothing enqueued); once
+    every slot has finished, passes commit nothing and the pool stays whole."""
+    w = I.weights_numpy(SHAPE, seed=0, scale=20.0)
+    eng = _engine(w, 3)
+    n_pages = eng.cfg.n_pages
+    with pytest.raises(IsdError, match="ISD_E_STATE"):
+        eng.step()
+    p = I.ragged_prompts([11], SHAPE.vocab, seed=20)
+    eng.prefill([1], p, [5])
+    out, _ = _run(eng, [1])
+    assert len(out[1]) == 4
+    for _ in range(3):
+        tok, nc, na = eng.step()
+        torch.cuda.synchronize()
+        assert nc.cpu().numpy().tolist() == [0, 0, 0]
+        assert na.cpu().numpy().tolist() == [0, 0, 0]
+    assert eng.status() == 0
+    assert int(eng.free_stack().numel()) == n_pages
+    assert [s["state"] for s in eng.slots_host()] == [0, 3, 0]
+
+
+def test_batch_with_holes_and_finished_slots_equals_alone():
+    """Slots 1 and 3 stay empty, slot 0 finishes early and keeps being stepped while slot 2
+    continues: empty and finished slots commit nothing and hold no pages, and slot 2's greedy
+    tokens equal the same prompt decoded in a context of its own."""
+    w = I.weights_numpy(SHAPE, seed=0, scale=20.0, sticky=(0.0, 20.0, 4.0, 7))
+    p0, p2 = I.ragged_prompts([13, 29], SHAPE.vocab, seed=21)
+    eng = _engine(w, 4)
+    eng.prefill([0, 2], [p0, p2], [3, 40])
+    out, counts = _run(eng, [0, 2])
+    for nc in counts:
+        assert nc[1] == 0 and nc[3] == 0
+    done0 = next(i for i, nc in enumerate(counts) if sum(c[0] for c in counts[:i + 1]) >= 2)
+    assert all(nc[0] == 0 for nc in counts[done0 + 1:])            # finished: nothing more
+    assert len(out[0]) == 2 and len(out[2]) == 39                    # max_new minus the first token
+    st = eng.slots_host()
+    assert st[0]["state"] == 3 and st[2]["state"] == 3
+    assert int(eng.free_stack().numel()) == eng.cfg.n_pages         # every page returned
+    alone = _engine(w, 1)
+    alone.prefill([0], [p2], [40])
+    ref, _ = _run(alone, [0])
+    assert out[2] == ref[0]
+
+
+def test_generation_fills_capacity_exactly():
+    """prompt + max_new + 2N == max_seq_len: the slot generates exactly max_new tokens and
+    returns all of its pages."""
+    w = I.weights_numpy(SHAPE, seed=0, scale=20.0)
+    max_seq = 80
+    p = I.ragged_prompts([20], SHAPE.vocab, seed=22)[0]
+    max_new = max_seq - len(p) - 2 * N
+    eng = _engine(w, 1, max_seq=max_seq)
+    eng.prefill([0], [p], [max_new])
+    out, _ = _run(eng, [0])
+    assert len(out[0]) == max_new - 1
+    assert eng.slots_host()[0]["n_gen"] == max_new
+    assert int(eng.free_stack().numel()) == eng.cfg.n_pages
+
+
+def test_admission_errors_leave_the_context_usable():
+    """A prompt beyond the capacity and a repeated slot are refused on the host (nothing is
+    enqueued); a valid prefill and decode then proceed normally."""
+    w = I.weights_numpy(SHAPE, seed=0, scale=20.0)
+    eng = _engine(w, 2, max_seq=64)
+    long_p = I.ragged_prompts([60], SHAPE.vocab, seed=23)[0]
+    with pytest.raises(IsdError):
+        eng.prefill([0], [long_p], [8])
+    p = I.ragged_prompts([10, 12], SHAPE.vocab, seed=24)
+    with pytest.raises(IsdError):
+        eng.prefill([1, 1], p, [5, 5])
+    assert int(eng.free_stack().numel()) == eng.cfg.n_pages
+    eng.prefill([0, 1], p, [6, 6])
+    out, _ = _run(eng, [0, 1])
+    assert len(out[0]) == 5 and len(out[1]) == 5
+    assert eng.status() == 0
