@@ -47,9 +47,9 @@ def _oracle(inp, b, q_len, group=4):
     return full
 
 
-def _check(inp, q_len, out):
+def _check(inp, q_len, out, group=4):
     for b in range(out.shape[0]):
-        ref = _oracle(inp, b, q_len)
+        ref = _oracle(inp, b, q_len, group)
         scale = max(np.abs(ref).max(), 1e-6)
         err = np.abs(out[b] - ref).max()
         assert err <= 2e-2 * scale, (b, err, scale)
@@ -85,3 +85,15 @@ def test_attention_row_invariance():
     inp1["ctx"] = inp["ctx"] - 6
     one = _run(inp1, np.ones(4, np.int32))
     np.testing.assert_array_equal(one[:, 0], full[:, 0])
+
+
+@pytest.mark.parametrize("batch,lo,hi", [(8, 300, 2500), (64, 512, 4096)])
+def test_attention_32b_head_grouping(batch, lo, hi):
+    """The 32B shape's heads: 64 query heads over 8 KV heads (8 per group, so a block's 7 rows
+    x 8 heads take the four-wave workgroup), small and full batches, ragged query lengths."""
+    import dataclasses
+    cfg = dataclasses.replace(I.ATTN_SAMPLER_MICRO, n_q_heads=64, n_kv_heads=8)
+    inp = I.attn_micro(cfg, batch=batch, ctx_lo=lo, ctx_hi=hi, seed=31 + batch)
+    q_len = np.random.default_rng(batch).integers(0, 8, size=batch).astype(np.int32)
+    q_len[0] = 7
+    _check(inp, q_len, _run(inp, q_len, n_kv=8), group=8)

@@ -185,6 +185,16 @@ def test_small_bf16_long_prompt():
                    on_gpu_logits=True)
 
 
+def test_bf16_eight_heads_per_group_end_to_end():
+    """The 32B shape's grouping (8 query heads per KV head: a block's 7 rows x 8 heads take the
+    four-wave attention workgroup in decode, and prefill tiles of 8 positions) on a small model."""
+    shape = I.ModelShape("small-g8-bf16", 2, 512, 16, 2, 128, 1024, 4096, "bf16")
+    w = I.weights_numpy(shape, seed=1, scale=20.0)
+    prompts = I.ragged_prompts([33, 9, 150], shape.vocab, seed=9)
+    teacher_forced(shape, w, 4, 1.0, "sample", prompts, [10, 14, 8], steps=10, logits_tol=2e-2, rel=True,
+                   on_gpu_logits=True)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_lora_mask_rows_end_to_end(dtype):
     """Gated LoRA (R-ISD adapter) on q, k, v, o, gate, up, down at the MASK rows: the GPU
