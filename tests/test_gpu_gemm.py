@@ -46,9 +46,12 @@ def _check(got, ref, bf16=True):
 
 SHAPES_8B = [("qkv", 448, 6144, 4096), ("o", 448, 4096, 4096), ("down", 448, 4096, 12288),
              ("lm_head", 448, 151936, 4096)]
+# the 32B shape: 64 x 128 query heads and 8 KV heads over d_model 5120, d_ffn 25600
+SHAPES_32B = [("qkv", 448, 10240, 5120), ("o", 448, 5120, 8192), ("down", 448, 5120, 25600),
+              ("qkv", 112, 10240, 5120), ("down", 112, 5120, 25600)]
 
 
-@pytest.mark.parametrize("name,M,N,K", SHAPES_8B)
+@pytest.mark.parametrize("name,M,N,K", SHAPES_8B + SHAPES_32B)
 def test_gemm_decode_shapes(name, M, N, K):
     from strided_decoding_amd import gemm
     print(f"gemm {name} {M}x{N}x{K}", flush=True)
@@ -61,9 +64,9 @@ def test_gemm_decode_shapes(name, M, N, K):
     _check(got, _ref(X, W, rows, cols), bf16=(name != "lm_head"))
 
 
-def test_gemm_swiglu_and_residual():
+@pytest.mark.parametrize("M,F,K", [(448, 12288, 4096), (448, 25600, 5120)])
+def test_gemm_swiglu_and_residual(M, F, K):
     from strided_decoding_amd import gemm
-    M, F, K = 448, 12288, 4096
     X = _rand((M, K), 4, 1.0)
     Wg = _rand((F, K), 5, 0.02)
     Wu = _rand((F, K), 6, 0.02)
