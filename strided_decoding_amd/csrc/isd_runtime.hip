@@ -315,10 +315,11 @@ GemmArgs gargs(const void* A, int lda, const void* B0, int ldb, int M, int N, in
 // LoRA of nt targets sharing one input on the MASK rows (targets t0 .. t0+nt-1, output widths
 // n[j]): S[:, j r .. (j+1) r] = X[mask_rows] A_j^T, then delta[:, o_j .. o_j + n_j] = S_j B_j^T with
 // o_j = n_0 + .. + n_{j-1}, added to the MASK rows of `base`, the group's projection.  When the
-// targets' A (and B) matrices are stacked in memory the shrinks run as one product; on the
-// bf16 path with stacked B the expand is fused into `base` itself (its MASK rows run r more k
-// values over S and B, the other rows add zeros), else it runs as separate products into an
-// fp32 delta that base's epilogue adds.
+// targets' A (and B) matrices are stacked in memory the shrinks run as one product (on the bf16
+// path one lora_shrink_kernel launch, k-split partials summed by the last workgroup to
+// arrive); on the bf16 path with stacked B the expand is fused into `base` itself (its MASK
+// rows run r more k values over S and B, the other rows add zeros), else it runs as separate
+// products into an fp32 delta that base's epilogue adds.
 isd_status lora_group(isd_ctx& x, int layer, int t0, int nt, const void* Xsrc, int ldx, int k_in, const int* n,
                       hipStream_t s, GemmArgs& base) {
   const int r = x.cfg.lora_rank, M = x.n_mask;
