@@ -48,6 +48,26 @@ static_assert(kBDepth <= kNsA - 2, "the B wait must cover the A wait");
 #ifndef ISD_SK_SD4
 #define ISD_SK_SD4 4
 #endif
+// waves per skinny workgroup for one / two / four row tiles, and the ring depth of the
+// two-wave form
+#ifndef ISD_SK_WV1
+#define ISD_SK_WV1 2
+#endif
+#ifndef ISD_SK_WV2
+#define ISD_SK_WV2 2
+#endif
+#ifndef ISD_SK_WV4
+#define ISD_SK_WV4 2
+#endif
+#ifndef ISD_SK_SD1W
+#define ISD_SK_SD1W 8
+#endif
+#ifndef ISD_SK_SD2W
+#define ISD_SK_SD2W 6
+#endif
+#ifndef ISD_SK_SD4W
+#define ISD_SK_SD4W 4
+#endif
 
 // Packed weight layout of the bf16 path: the B operand of one 32x32x16 MFMA is 1 KB contiguous.
 // Block (nb, kb) holds rows 32 nb .. 32 nb + 31 and k = 16 kb .. 16 kb + 15; its lane l part
@@ -395,33 +415,41 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
 }
 
 // Skinny path for at most 128 rows (decode at small batch, where a projection is bound by
-// streaming its weights from HBM).  One single-wave workgroup per (output-column group, K
-// split); no barriers.  The wave streams its packed weight operands (one contiguous 1 KB
-// direct load per block and k-step) and the (L2-resident) activation rows through a private
-// SD-stage LDS ring filled by direct global->LDS loads, with the loads of SD-1 stages in flight
-// under explicit vmcnt waits while one stage is multiplied.  The MFMA (32x32x16), the k-chunk
+// streaming its weights from HBM).  One workgroup of WV waves per (output-column group, K
+// split).  Each wave streams its packed weight operands (one contiguous 1 KB direct load per
+// block and k-step) and the (L2-resident) activation rows through an SD-stage LDS ring filled
+// by direct global->LDS loads, with the loads of the next stages in flight under explicit
+// vmcnt waits while one stage is multiplied.  WV = 1 needs no barrier at all.  The MFMA (32x32x16), the k-chunk
 // held by each lane, the k-step order, the split rule and the partial layout are those of the
 // tiled kernel, so every output element is accumulated in exactly the same order and the two
 // paths give bit-identical results.
-template <int EPI, bool PARTIAL, int MT, int SD>
-__global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_nt, int S, float* part) {
+//
+// WV = 2: two waves share the activation stages (each loads half of the row groups) and each
+// streams its own 64 output columns; a barrier per stage then orders the ring's refills.  The
+// activation traffic per output column halves; the accumulation order is unchanged.
+template <int EPI, bool PARTIAL, int MT, int SD, int WV>
+__global__ __launch_bounds__(64 * WV) void gemm_bf16_skinny_kernel(GemmArgs a, int n_nt, int S, float* part) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU);
   constexpr int NB = 2;                     // 32-column MFMA tiles per wave (gate + up for SwiGLU)
   constexpr int TNO = DUAL ? 32 : 64;       // output columns per wave
-  constexpr int STAGE = (MT + NB) * 2048;   // bytes per 32-k stage: activation tiles, then weight operands
-  constexpr int PER_STAGE = 2 * (MT + NB);  // direct loads per stage
+  constexpr int XG = 2 * MT / WV;           // activation row groups each wave loads per stage
+  constexpr int STAGE = (MT + NB * WV) * 2048;   // bytes per 32-k stage: activation tiles, then each wave's weight operands
+  constexpr int PER_STAGE = XG + 2 * NB;    // direct loads per stage and wave
+  static_assert(WV == 1 || WV == 2, "one or two waves");
   static_assert((SD - 1) * PER_STAGE < 64, "vmcnt counts at most 63 outstanding loads");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SD * STAGE];
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = WV > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
   const int unit = blockIdx.x;
   const int sp = unit / n_nt, nt = unit - sp * n_nt;
   const int kt_per = (a.K / BK) / S;
   const int kbase = sp * kt_per * BK;
-  const int n0 = nt * TNO;
+  const int nw0 = nt * TNO * WV;            // the workgroup's first column (segments never split a workgroup)
+  const int n0 = nw0 + wave * TNO;          // this wave's
   const int r32 = lane & 31, khi = lane >> 5;
   const uint16_t* zero = kZeroOperand + lane * 8;
   // stages kt_per .. kt_end-1: the fused LoRA expand (last split only)
-  const LoraPlan lp = lora_plan(a, n0, DUAL, sp == S - 1);
+  const LoraPlan lp = lora_plan(a, nw0, DUAL, sp == S - 1);
   const int kt_end = kt_per + lp.n;
 
   // Activation loader (the tiled kernel's 16-row group layout): one direct load per 16-row
@@ -429,30 +457,27 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_
   // k-chunk (l%4) ^ ((row/4)%4), so the operand reads below are free of bank conflicts.
   const int lrow = lane >> 2;
   const int chunk = (lane & 3) ^ ((lrow >> 2) & 3);
-  const int aoff = gemm_seg_aoff(a, n0);
-  const uint16_t* xsrc[MT][2];
-  const uint16_t* lsrc[MT][2];              // fused LoRA: the row's lora_a row (null: zeros)
+  const int aoff = gemm_seg_aoff(a, nw0);
+  // this wave's row groups: q * WV + wave, i.e. 16-row group g = gq % 2 of row tile gq / 2
+  const uint16_t* xsrc[XG];
+  const uint16_t* lsrc[XG];                 // fused LoRA: the row's lora_a row (null: zeros)
   {
     // every row-index load is issued before any is used (one wait, not one per row group)
-    int sr[MT][2], lr[MT][2];
+    int sr[XG], lr[XG];
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int q = 0; q < XG; ++q) {
+      const int mc = min(16 * (q * WV + wave) + lrow, a.M - 1);
+      sr[q] = a.a_rows ? a.a_rows[mc] : mc;
+      lr[q] = lp.n ? a.lora_rows[mc] : -1;
+    }
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int mc = min(32 * i + 16 * g + lrow, a.M - 1);
-        sr[i][g] = a.a_rows ? a.a_rows[mc] : mc;
-        lr[i][g] = lp.n ? a.lora_rows[mc] : -1;
-      }
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const bool valid = 32 * i + 16 * g + lrow < a.M;
-        const int srow = valid ? max(sr[i][g], 0) : 0;   // unused rows: their outputs are never consumed
-        const int l = valid ? lr[i][g] : -1;
-        xsrc[i][g] = (const uint16_t*)a.A + (size_t)srow * a.lda + aoff + kbase + chunk * 8;
-        lsrc[i][g] = l >= 0 ? (const uint16_t*)a.lora_a + (size_t)l * a.ld_la + lp.seg_off + chunk * 8 : nullptr;
-      }
+    for (int q = 0; q < XG; ++q) {
+      const bool valid = 16 * (q * WV + wave) + lrow < a.M;
+      const int srow = valid ? max(sr[q], 0) : 0;   // unused rows: their outputs are never consumed
+      const int l = valid ? lr[q] : -1;
+      xsrc[q] = (const uint16_t*)a.A + (size_t)srow * a.lda + aoff + kbase + chunk * 8;
+      lsrc[q] = l >= 0 ? (const uint16_t*)a.lora_a + (size_t)l * a.ld_la + lp.seg_off + chunk * 8 : nullptr;
+    }
   }
   // weight operand blocks: columns n0 + 32 j .. (SwiGLU: gate j = 0 and up j = 1 of n0 ..)
   const uint16_t* wsrc[NB];
@@ -478,13 +503,11 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_
     const int ls = kt - kt_per;                 // LoRA stage offsets as in the tiled kernel
     const bool lora = ls >= 0 && ls < lp.n;
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const uint16_t* l = (MODE == kLoraTail && lora && lsrc[t][g]) ? lsrc[t][g] + ls * BK : zero;
-        __builtin_amdgcn_global_load_lds((const void*)(live ? xsrc[t][g] + kt * BK : l),
-                                         (lds_void*)(st + (2 * t + g) * 1024), 16, 0, 0);
-      }
+    for (int q = 0; q < XG; ++q) {
+      const uint16_t* l = (MODE == kLoraTail && lora && lsrc[q]) ? lsrc[q] + ls * BK : zero;
+      __builtin_amdgcn_global_load_lds((const void*)(live ? xsrc[q] + kt * BK : l),
+                                       (lds_void*)(st + (q * WV + wave) * 1024), 16, 0, 0);
+    }
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -492,7 +515,7 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_
         const int lk = ls - (DUAL ? j * lp.per : 0);
         const uint16_t* l = (MODE == kLoraTail && lk >= 0 && lk < (DUAL ? lp.per : lp.n)) ? lwsrc[j] + (2 * lk + kk) * 512 : zero;
         __builtin_amdgcn_global_load_lds((const void*)(live ? wsrc[j] + (2 * kt + kk) * 512 : l),
-                                         (lds_void*)(st + (2 * MT + 2 * j + kk) * 1024), 16, 0, 0);
+                                         (lds_void*)(st + (2 * MT + 2 * NB * wave + 2 * j + kk) * 1024), 16, 0, 0);
       }
   };
   f32x16_t acc[MT][NB];
@@ -515,7 +538,8 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_
 #pragma unroll
       for (int t = 0; t < MT; ++t) x[t] = as_bf16x8(*(const u32x4_t*)(st + rd0 + 2 * t * 1024 + off));
 #pragma unroll
-      for (int j = 0; j < NB; ++j) w[j] = as_bf16x8(*(const u32x4_t*)(st + (2 * MT + 2 * j + kk) * 1024 + lane * 16));
+      for (int j = 0; j < NB; ++j)
+        w[j] = as_bf16x8(*(const u32x4_t*)(st + (2 * MT + 2 * NB * wave + 2 * j + kk) * 1024 + lane * 16));
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -523,24 +547,30 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(GemmArgs a, int n_
     }
   };
 
-  // Stage kt is issued SD-1 steps before it is multiplied; before multiplying it, at most the
-  // loads of the stages issued after it may be outstanding.
+  // Stage kt is issued SD-1 steps before it is multiplied.  One wave: issue, then wait until
+  // only the loads of the stages issued after stage kt are outstanding.  Two waves: wait for
+  // this wave's loads of stage kt, then a barrier (every wave's loads of stage kt have landed
+  // and every wave is done with stage kt-1, whose slot the next issue refills).
+  auto step = [&](auto mode, int kt) {
+    if constexpr (WV == 1) {
+      issue(mode, kt + SD - 1);
+      wait_vmcnt<(SD - 1) * PER_STAGE>();
+    } else {
+      wait_vmcnt<(SD - 2) * PER_STAGE>();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      issue(mode, kt + SD - 1);
+    }
+    mul(kt);
+    __builtin_amdgcn_sched_barrier(0);
+  };
   for (int kt = 0; kt < SD - 1; ++kt) issue(StageMode<kLoraTail>{}, kt);
   const int fast_end = max(0, kt_per - (SD - 1));   // steps whose issued stage is a product stage
   int kt = 0;
-  for (; kt < fast_end; ++kt) {
-    issue(StageMode<kPlainStages>{}, kt + SD - 1);
-    wait_vmcnt<(SD - 1) * PER_STAGE>();
-    mul(kt);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  for (; kt < fast_end; ++kt) step(StageMode<kPlainStages>{}, kt);
   auto tail = [&](auto mode) {
-    for (; kt < kt_end; ++kt) {
-      issue(mode, kt + SD - 1);
-      wait_vmcnt<(SD - 1) * PER_STAGE>();
-      mul(kt);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    for (; kt < kt_end; ++kt) step(mode, kt);
   };
   if (lp.n == 0)
     tail(StageMode<kZeroTail>{});
@@ -777,22 +807,39 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
 template <int EPI>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
   const int tno = EPI == EPI_SWIGLU ? 32 : 64;
-  const int n_nt = (a.N + tno - 1) / tno;
+  const int MT = a.M <= 32 ? 1 : (a.M <= 64 ? 2 : 4);
+  int WV = MT == 1 ? ISD_SK_WV1 : (MT == 2 ? ISD_SK_WV2 : ISD_SK_WV4);
+  // very wide products (the LM head) keep one wave per workgroup: their activation traffic is
+  // small next to the weights, and twice the workgroups spread better (measured)
+  if (a.N > 65536) WV = 1;
+  // a two-wave workgroup shares one activation stage: no (LoRA) segment boundary inside it
+  for (int j = 0; j + 1 < a.nseg; ++j)
+    if (a.seg_end[j] % (WV * tno)) WV = 1;
+  if (a.lora_r > 0)
+    for (int j = 0; j + 1 < a.lora_nseg; ++j)
+      if (a.lora_seg_end[j] % (WV * tno)) WV = 1;
+  const int n_nt = (a.N + WV * tno - 1) / (WV * tno);
   const int S = (a.splits > 1 && a.part) ? a.splits : 1;
   dim3 grid(n_nt * S);
   float* part = S > 1 ? a.part : nullptr;
-#define ISD_SKINNY(P, MT, SD) \
-  hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, P, MT, SD>), grid, dim3(64), 0, s, a, n_nt, S, part)
-  if (a.M <= 32) {
-    if (S > 1) ISD_SKINNY(true, 1, ISD_SK_SD1);
-    else ISD_SKINNY(false, 1, ISD_SK_SD1);
-  } else if (a.M <= 64) {
-    if (S > 1) ISD_SKINNY(true, 2, ISD_SK_SD2);
-    else ISD_SKINNY(false, 2, ISD_SK_SD2);
-  } else {
-    if (S > 1) ISD_SKINNY(true, 4, ISD_SK_SD4);
-    else ISD_SKINNY(false, 4, ISD_SK_SD4);
+#define ISD_SKINNY(P, MT, SD, W) \
+  hipLaunchKernelGGL((gemm_bf16_skinny_kernel<EPI, P, MT, SD, W>), grid, dim3(64 * W), 0, s, a, n_nt, S, part)
+#define ISD_SKINNY_WV(MT, SD, SDW)                         \
+  if (WV == 1) {                                           \
+    if (S > 1) ISD_SKINNY(true, MT, SD, 1);                \
+    else ISD_SKINNY(false, MT, SD, 1);                     \
+  } else {                                                 \
+    if (S > 1) ISD_SKINNY(true, MT, SDW, 2);               \
+    else ISD_SKINNY(false, MT, SDW, 2);                    \
   }
+  if (MT == 1) {
+    ISD_SKINNY_WV(1, ISD_SK_SD1, ISD_SK_SD1W)
+  } else if (MT == 2) {
+    ISD_SKINNY_WV(2, ISD_SK_SD2, ISD_SK_SD2W)
+  } else {
+    ISD_SKINNY_WV(4, ISD_SK_SD4, ISD_SK_SD4W)
+  }
+#undef ISD_SKINNY_WV
 #undef ISD_SKINNY
   return finish<EPI>(a, S, s);
 }
