@@ -103,8 +103,8 @@ def step_bytes(shape, M, ctx_rows):
 # Kernel (demangled-name pattern) behind each profiled operation whose traffic can be read from
 # rocprofv3 counters: the decode launches are the most frequent grid of that kernel in a run.
 OP_KERNELS = {
-    "gemm_gate_up": (r"gemm_bf16_big_kernel<3, false, false>", ("k_gemm.hip",)),
-    "lm_head": (r"gemm_bf16_big_kernel<1, false, false>", ("k_gemm.hip",)),
+    "gemm_gate_up": (r"gemm_bf16_big_kernel<3, false, false, 3>", ("k_gemm.hip",)),
+    "lm_head": (r"gemm_bf16_big_kernel<1, false, false, 4>", ("k_gemm.hip",)),
     "attention": (r"attn_bf16_kernel<", ("k_attn.hip",)),
     "row_stats": (r"row_stats_kernel", ("k_sampler.hip",)),
 }

@@ -313,9 +313,10 @@ isd_status isd_pack_weights(const void* src, void* dst, int32_t rows, int32_t co
  *            norm_out [M, N] act = RMSNorm(R row) * norm_g, eps norm_eps (as isd_step fuses
  *            the next block's input norm into the O and down projections)
  *   path     bf16 kernel: 0 = automatic (the skinny kernel up to 64 rows, and up to 128 rows
- *            unless N > 65536, else the tiled one), 1 = tiled, 2 = skinny (M <= 128 only).  Both
- *            kernels accumulate every output element in the same order, so the choice never
- *            changes the result.
+ *            unless N > 65536, else the tiled one), 1 = tiled, 2 = skinny (M <= 128 only),
+ *            3 / 4 / 5 = tiled with 4 / 3 / 2 waves per workgroup (0 and 1 choose the count
+ *            that fills the CUs best).  Every kernel accumulates each output element in the
+ *            same order, so the choice never changes the result.
  * K must be a multiple of 32 and N of 4 for bf16.  Errors: ISD_E_ARG, ISD_E_SHAPE. */
 enum { ISD_GEMM_STORE = 0, ISD_GEMM_STORE_F32 = 1, ISD_GEMM_RESID = 2, ISD_GEMM_SWIGLU = 3 };
 typedef struct {

@@ -163,7 +163,7 @@ struct GemmArgs {
   const void* norm_g;
   void* norm_out;
   float norm_eps;
-  int path;                  // bf16 kernel choice: GEMM_PATH_AUTO / _TILED / _SKINNY
+  int path;                  // bf16 kernel choice: GEMM_PATH_AUTO / _TILED / _SKINNY / _TILED4..2
   // Segmented A (0 = off): output columns [seg_end[j-1], seg_end[j]) read A columns starting at
   // seg_aoff[j], i.e. several products X_j W_j^T with stacked W_j in one launch.  Segment ends
   // must be multiples of 256 (no column tile straddles two segments).
@@ -188,7 +188,10 @@ struct GemmArgs {
   int lora_nseg;
   int lora_seg_end[3];
 };
-enum { GEMM_PATH_AUTO = 0, GEMM_PATH_TILED = 1, GEMM_PATH_SKINNY = 2 };
+// TILED4 / TILED3 / TILED2: the tiled kernel with that many waves per workgroup (TILED and
+// AUTO choose it by the grid's fill of the CUs)
+enum { GEMM_PATH_AUTO = 0, GEMM_PATH_TILED = 1, GEMM_PATH_SKINNY = 2, GEMM_PATH_TILED4 = 3, GEMM_PATH_TILED3 = 4,
+       GEMM_PATH_TILED2 = 5 };
 
 // Fused-LoRA stage plan of a workgroup: its number of extra k-stages (32 k each) and, for
 // extra stage ls, the lora_a column offset and the group (SwiGLU: 0 gate, 1 up; else 0).

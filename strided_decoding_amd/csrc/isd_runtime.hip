@@ -927,7 +927,7 @@ isd_status isd_gemm(const isd_gemm_args* a, void* stream) {
   if (a->M < 0 || a->N < 1 || a->K < 1 || a->splits < 0) return ISD_E_ARG;
   if (a->mode == ISD_GEMM_RESID ? !a->R : !a->Y) return ISD_E_ARG;
   if (a->mode == ISD_GEMM_SWIGLU && !a->W2) return ISD_E_ARG;
-  if (a->path < GEMM_PATH_AUTO || a->path > GEMM_PATH_SKINNY) return ISD_E_ARG;
+  if (a->path < GEMM_PATH_AUTO || a->path > GEMM_PATH_TILED2) return ISD_E_ARG;
   if (a->path == GEMM_PATH_SKINNY && a->M > kSkinnyMaxRows) return ISD_E_SHAPE;
   GemmArgs g = gargs(a->X, a->K, a->W, a->K, a->M, a->N, a->K, a->mode);
   g.B1 = a->W2;

@@ -4,11 +4,11 @@
 //
 // bf16 path: the weights are in a packed operand layout (the B operand of one 32x32x16 MFMA
 // is one contiguous kilobyte), so every weight load is a full-rate contiguous 1 KB access.
-// Tiled kernel (more than 128 rows): one 224 x 256 output tile per workgroup of 4 waves, one
-// wave per SIMD, each 224 x 64 = 7 x 2 MFMA tiles (224 accumulators in AGPRs).  224 = 448 / 2
+// Tiled kernel (more than 128 rows): one 224 x 64 WV output tile per workgroup of WV = 4, 3
+// or 2 waves, one wave per SIMD, each 224 x 64 = 7 x 2 MFMA tiles (224 accumulators in AGPRs).  224 = 448 / 2
 // makes the decode row count (64 slots x 7 rows) exactly two row tiles.  The activation tile
 // is streamed in 32-wide k stages through a 10-deep LDS ring filled by direct global->LDS
-// loads and shared by the four waves; each wave loads its own weight operands straight into a
+// loads and shared by the waves; each wave loads its own weight operands straight into a
 // 4-stage register ring.  Each 64-byte LDS row keeps its four 16-byte k-chunks XOR-swizzled by
 // (row/4)%4 so that the 16 rows an MFMA operand read touches fall in distinct banks.
 // Skinny kernel (at most 128 rows): single-wave workgroups streaming 64 weight columns.
@@ -30,7 +30,6 @@ constexpr int BK = 32;            // k per pipeline stage (one MFMA k-step)
 constexpr int TM2 = 224, TN2 = 256;
 constexpr int GROUP_BYTES = 16 * BK * 2;                 // 16 rows x 64 B
 constexpr int AG = TM2 / 16;              // A row groups of 16 rows per tile
-constexpr int kALoads = 4;                // A loads per wave and stage (4 waves x 4 >= 14 groups)
 constexpr int kNsA = 10;                  // A ring depth (10 x 14 KB)
 constexpr int kAStage = AG * GROUP_BYTES;
 constexpr int kBRing = 4;                 // B operands: a register ring of this many stages,
@@ -122,12 +121,18 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_
 }
 
 // LORA: the instance that can run fused LoRA stages (a separate instance, so that each one
-// holds only two versions of the pipeline loop: a third does not fit the registers)
-template <int EPI, bool PARTIAL, bool LORA>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// holds only two versions of the pipeline loop: a third does not fit the registers).
+// WV: waves per workgroup (4, 3 or 2), i.e. a 224 x 64 WV output tile.  The per-wave work and
+// the k order are the same for every WV; fewer waves per workgroup give more workgroups for a
+// product whose 4-wave grid leaves CUs idle, each CU then streaming less data per stage.
+template <int EPI, bool PARTIAL, bool LORA, int WV>
+__global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU);
-  constexpr int TNO = DUAL ? TN2 / 2 : TN2;
+  constexpr int TNO = DUAL ? 32 * WV : 64 * WV;   // output columns per workgroup
+  constexpr int kALoads = (AG + WV - 1) / WV;     // A loads per wave and stage (the 14 groups over WV waves)
+  constexpr int PER = kALoads + 4;                // loads per wave and pipeline step
+  static_assert(WV >= 2 && WV <= 4 && kALoads <= 13, "2 to 4 waves");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kBigLds];
 
   const int id = blockIdx.x;
@@ -146,8 +151,9 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
   const int kt_end = kt_per + lp.n;
   const int kt_loop = (kt_end + kBRing - 1) / kBRing * kBRing;
 
-  // A loader: wave w fills row groups min(w + 4 i, 13), i < 4, of the 14 (waves 1-3 all refill
-  // group 13 with the same bytes, so every wave issues 4 loads per stage).  Lane l writes LDS
+  // A loader: wave w fills row groups min(w + WV i, 13), i < kALoads, of the 14 (with 4 or 3
+  // waves some refill group 13 with the same bytes, so every wave issues kALoads loads per
+  // stage).  Lane l writes LDS
   // bytes [16 l, 16 l + 16) of its group: row l/4, slot l%4, which holds k-chunk
   // (l%4) ^ ((row/4)%4) of that row.
   const int lrow = lane >> 2;
@@ -160,13 +166,13 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
     int sr[kALoads], lr[kALoads];
 #pragma unroll
     for (int i = 0; i < kALoads; ++i) {
-      const int mc = min(m0 + min(wave + 4 * i, AG - 1) * 16 + lrow, a.M - 1);
+      const int mc = min(m0 + min(wave + WV * i, AG - 1) * 16 + lrow, a.M - 1);
       sr[i] = a.a_rows ? a.a_rows[mc] : mc;
       lr[i] = (LORA && lp.n) ? a.lora_rows[mc] : -1;
     }
 #pragma unroll
     for (int i = 0; i < kALoads; ++i) {
-      const bool valid = m0 + min(wave + 4 * i, AG - 1) * 16 + lrow < a.M;
+      const bool valid = m0 + min(wave + WV * i, AG - 1) * 16 + lrow < a.M;
       const int srow = valid ? max(sr[i], 0) : 0;   // unused rows: their outputs are never consumed
       const int l = valid ? lr[i] : -1;
       asrc[i] = (const uint16_t*)a.A + (size_t)srow * a.lda + aoff + kbase + chunk * 8;
@@ -201,7 +207,7 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
   };
   auto a_dma = [&](int i, uint8_t* st, int kt) {
     __builtin_amdgcn_global_load_lds((const void*)a_src(i, kt),
-                                     (lds_void*)(st + min(wave + 4 * i, AG - 1) * GROUP_BYTES), 16, 0, 0);
+                                     (lds_void*)(st + min(wave + WV * i, AG - 1) * GROUP_BYTES), 16, 0, 0);
   };
   // operand ring: stage kt's B fragments in slot kt % kBRing, loaded kBDepth stages ahead
   bf16x8_t bq[kBRing][2][2];
@@ -219,12 +225,12 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // The loads follow a fixed pattern: pipeline step i issues 4 A loads (stage i + kNsA - 1)
-  // and then 4 B loads (stage i + kBDepth), and the prologue is the same pattern for the steps
-  // i = 1 - kNsA .. -1 without the B loads of negative stages.  Stages past the last one load
-  // zeros, so the pattern never changes: before step kt reads B stage kt exactly
-  // 8 (kBDepth - 1) loads were issued after it, and at least as many after A stage kt+1
-  // because kBDepth <= kNsA - 2.
+  // The loads follow a fixed pattern: pipeline step i issues kALoads A loads (stage
+  // i + kNsA - 1) and 4 B loads (stage i + kBDepth), the last of them a B load, and the
+  // prologue is the same pattern for the steps i = 1 - kNsA .. -1 without the B loads of
+  // negative stages.  Stages past the last one load zeros, so the pattern never changes:
+  // before step kt reads B stage kt exactly PER (kBDepth - 1) loads were issued after it, and
+  // at least as many after A stage kt+1 because kBDepth <= kNsA - 2.
 #pragma unroll
   for (int i = 1 - kNsA; i < 0; ++i) {
     const int sa = i + kNsA - 1, sb = i + kBDepth;
@@ -243,7 +249,7 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
   };
 
   bf16x8_t x0[7], x1[7];
-  wait_vmcnt<8 * (kBDepth - 1)>();                 // A stage 0 and B stage 0 have landed
+  wait_vmcnt<PER * (kBDepth - 1)>();                 // A stage 0 and B stage 0 have landed
   __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int i = 0; i < 7; ++i) x0[i] = frag(0, 0, i);
@@ -261,7 +267,7 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
     for (int d = 0; d < kBRing; ++d) {
       const int kt = kt0 + d;
       __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<8 * (kBDepth - 1)>();   // B stage kt and A stage kt+1 have landed
+      wait_vmcnt<PER * (kBDepth - 1)>();   // B stage kt and A stage kt+1 have landed
       __builtin_amdgcn_s_barrier();      // no fence: the later stages' loads stay in flight
       __builtin_amdgcn_sched_barrier(0);
       {
@@ -279,7 +285,7 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
                                 : MODE == kZeroTail   ? (ka < kt_per ? asrc[q] + ka * BK : zero)
                                                       : a_src(q, ka);
             __builtin_amdgcn_global_load_lds((const void*)src,
-                                             (lds_void*)(dst + min(wave + 4 * q, AG - 1) * GROUP_BYTES), 16, 0, 0);
+                                             (lds_void*)(dst + min(wave + WV * q, AG - 1) * GROUP_BYTES), 16, 0, 0);
           }
           if (m >= 6 && m < 10) {
             const int j = (m - 6) >> 1, kk = (m - 6) & 1;
@@ -781,25 +787,61 @@ hipError_t finish(const GemmArgs& a, int S, hipStream_t s) {
   return hipSuccess;
 }
 
+// Waves per workgroup of the tiled kernel.  Every workgroup of a decode-size grid runs at
+// once (one per CU), and its stage time follows the data its CU streams per stage: the
+// activation tile (14 row-group loads, padded to a multiple of the wave count) plus 4 KB of
+// weight operands per wave.  Fewer waves per workgroup mean more workgroups over the same
+// columns; the choice minimises (grid rounds over the CUs) x (loads per stage and CU), among
+// the wave counts whose column tiles do not straddle a segment boundary.
+template <int EPI>
+int big_waves(const GemmArgs& a, int n_mt, int S) {
+  if (a.path >= GEMM_PATH_TILED4) return 4 - (a.path - GEMM_PATH_TILED4);
+  static int n_cu = 0;
+  if (!n_cu) {
+    int dev = 0, v = 0;
+    n_cu = (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) ? v : 256;
+  }
+  const int tnw = EPI == EPI_SWIGLU ? 32 : 64;   // output columns per wave
+  int best = 4;
+  long best_cost = -1;
+  for (int wv = 4; wv >= 2; --wv) {
+    bool ok = true;
+    for (int j = 0; j + 1 < a.nseg; ++j) ok = ok && a.seg_end[j] % (wv * tnw) == 0;
+    if (a.lora_r > 0)
+      for (int j = 0; j + 1 < a.lora_nseg; ++j) ok = ok && a.lora_seg_end[j] % (wv * tnw) == 0;
+    if (!ok) continue;
+    const long wgs = (long)n_mt * ((a.N + wv * tnw - 1) / (wv * tnw)) * S;
+    const long cost = (wgs + n_cu - 1) / n_cu * (wv * ((AG + wv - 1) / wv) + 4 * wv);
+    if (best_cost < 0 || cost < best_cost) best = wv, best_cost = cost;
+  }
+  return best;
+}
+
 template <int EPI>
 hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
-  const bool dual = EPI == EPI_SWIGLU;
-  const int tno = dual ? TN2 / 2 : TN2;
-  const int n_mt = (a.M + TM2 - 1) / TM2, n_nt = (a.N + tno - 1) / tno;
+  const int n_mt = (a.M + TM2 - 1) / TM2;
   const int S = (a.splits > 1 && a.part) ? a.splits : 1;
+  const int WV = big_waves<EPI>(a, n_mt, S);
+  const int tno = (EPI == EPI_SWIGLU ? 32 : 64) * WV;
+  const int n_nt = (a.N + tno - 1) / tno;
   const int units = n_nt * S;
   dim3 grid(((units + 7) / 8) * 8 * n_mt);
-  // the full B ring when the stage count of a split allows it, else a two-stage ring
-#define ISD_BIG(P, L) \
-  hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, P, L>), grid, dim3(256), 0, s, a, n_mt, units, S, P ? a.part : nullptr)
+#define ISD_BIG(P, L, W) \
+  hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, P, L, W>), grid, dim3(64 * W), 0, s, a, n_mt, units, S, P ? a.part : nullptr)
+#define ISD_BIG_W(P, L) \
+  if (WV == 4) ISD_BIG(P, L, 4); \
+  else if (WV == 3) ISD_BIG(P, L, 3); \
+  else ISD_BIG(P, L, 2);
   const bool lora = a.lora_r > 0;
   if (S > 1) {
-    if (lora) ISD_BIG(true, true);
-    else ISD_BIG(true, false);
+    if (lora) { ISD_BIG_W(true, true) }
+    else { ISD_BIG_W(true, false) }
   } else {
-    if (lora) ISD_BIG(false, true);
-    else ISD_BIG(false, false);
+    if (lora) { ISD_BIG_W(false, true) }
+    else { ISD_BIG_W(false, false) }
   }
+#undef ISD_BIG_W
 #undef ISD_BIG
   return finish<EPI>(a, S, s);
 }

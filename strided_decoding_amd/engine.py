@@ -273,7 +273,7 @@ def attn_paged(q, k_pool, v_pool, page_table, ctx_len, q_len, n_kv_heads, out=No
     return out, workspace, args
 
 
-GEMM_PATHS = {"auto": 0, "tiled": 1, "skinny": 2}
+GEMM_PATHS = {"auto": 0, "tiled": 1, "skinny": 2, "tiled4": 3, "tiled3": 4, "tiled2": 5}
 
 
 def gemm(X, W, mode="store", W2=None, out=None, R=None, splits=0, workspace=None, stream=None,
@@ -282,7 +282,8 @@ def gemm(X, W, mode="store", W2=None, out=None, R=None, splits=0, workspace=None
     (pack_weight) or a float32 device tensor.
 
     mode "resid" with norm_g / norm_out also writes RMSNorm(R) * norm_g into norm_out.
-    path: "auto", "tiled" or "skinny" (bf16 kernel choice; M <= 128 for skinny)."""
+    path: "auto", "tiled", "skinny" (bf16 kernel choice; M <= 128 for skinny) or "tiled4",
+    "tiled3", "tiled2" (the tiled kernel with that many waves per workgroup)."""
     lib = A.load()
     M, K = X.shape
     bf = X.dtype == torch.bfloat16

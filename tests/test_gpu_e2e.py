@@ -64,7 +64,7 @@ def _adopt(dec, model, b, g, committed, rec_logits, R, N, T, propose):
 
 
 def teacher_forced(shape, w, N, T, propose, prompts, max_new, steps, lora=None, on_gpu_logits=False,
-                   logits_tol=1e-4, rel=False):
+                   logits_tol=1e-4, rel=False, first_tau=CAT_TAU):
     B = len(prompts)
     max_seq = max(len(p) for p in prompts) + max(max_new) + 2 * N + 2
     eng = make_engine(shape, w, N, T, propose, B, max_seq, lora=lora)
@@ -81,7 +81,7 @@ def teacher_forced(shape, w, N, T, propose, prompts, max_new, steps, lora=None, 
         if first[b] != ofirst[b]:
             logits, _ = model.forward(prompts[b], np.arange(len(prompts[b])), M.empty_cache(model.spec))
             _, m = OI.draw(logits[-1], philox.uniform(1, b, 0, len(prompts[b]), 1), T)
-            assert T > 0 and m < CAT_TAU, ("first token differs", b, m)
+            assert T > 0 and m < first_tau, ("first token differs", b, m)
             near += 1
             lockstep = False
             dec.slots[b].committed[-1] = int(first[b])
@@ -235,6 +235,24 @@ def test_lora_8b_widths_end_to_end():
     prompts = I.ragged_prompts([17, 29], shape.vocab, seed=16)
     teacher_forced(shape, w, 4, 1.0, "sample", prompts, [8, 8], steps=4, lora=lora, logits_tol=2e-2, rel=True,
                    on_gpu_logits=True)
+
+
+@pytest.mark.parametrize("B", [20, 33])
+def test_lora_tiled_rows_end_to_end(B):
+    """The adapter on the tiled GEMM kernel: 20 and 33 slots of 7 rows (140 and 231 rows, past
+    the skinny kernel's 128) at the 8B shape's widths, so that the fused LoRA expands run in
+    the tiled kernel with 2 waves per workgroup (140 rows), and with 3 (gate/up) and 4 (q/k/v,
+    o, down) at 231 rows; the GPU logits of every row follow the oracle's.  With this many
+    slots some prefill draws sit within the bf16 logits error of a CDF boundary at d_model
+    4096 (a margin of a few percent): such a first token is adopted from the GPU, as a near
+    tie, and the passes that the test is about are then checked on the GPU's logits."""
+    shape = I.ModelShape("8b-widths-1-layer", 1, 4096, 32, 8, 128, 12288, 4096, "bf16")
+    w = I.weights_numpy(shape, seed=3, scale=20.0)
+    lora = I.lora_numpy(shape, 128, scale=2.0)
+    lens = [int(x) for x in np.random.default_rng(17).integers(5, 30, B)]
+    prompts = I.ragged_prompts(lens, shape.vocab, seed=17)
+    teacher_forced(shape, w, 4, 1.0, "sample", prompts, [8] * B, steps=2, lora=lora, logits_tol=2e-2, rel=True,
+                   on_gpu_logits=True, first_tau=0.1)
 
 
 @pytest.mark.parametrize("N,T,propose", [(3, 0.0, "argmax"), (4, 1.0, "argmax")])
