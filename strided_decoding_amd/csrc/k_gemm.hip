@@ -796,6 +796,9 @@ hipError_t finish(const GemmArgs& a, int S, hipStream_t s) {
 template <int EPI>
 int big_waves(const GemmArgs& a, int n_mt, int S) {
   if (a.path >= GEMM_PATH_TILED4) return 4 - (a.path - GEMM_PATH_TILED4);
+#ifdef ISD_BIG_WAVES
+  return ISD_BIG_WAVES;   // build-time override of the automatic choice (tuning)
+#endif
   static int n_cu = 0;
   if (!n_cu) {
     int dev = 0, v = 0;

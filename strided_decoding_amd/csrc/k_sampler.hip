@@ -283,25 +283,33 @@ struct Decider {
     return cat_in_row(l, a.V, nc, cw, rs.m, a.T, u * tot, excl, sm);
   }
 
-  // normalize(max(0, p - q)) with q the previous pass's row qrow
+  // normalize(max(0, p - q)) with q the previous pass's row qrow.  One sweep over the row
+  // gives every chunk's residual mass (each wave sums its share of a chunk, no block barrier
+  // per chunk; the four wave sums are added in a fixed order), then the chunk the draw lands
+  // in is re-read element by element.
   __device__ int resid_draw(int row, const RowStat& ps, int qrow, const RowStat& qs, double u) {
     const float* lp = a.logits + (size_t)row * a.V;
     const float* lq = a.q_logits + (size_t)qrow * a.V;
     __shared__ double rc[NT];
+    __shared__ double rcw[NT / 64][NT];
     const int tid = threadIdx.x;
+    const double ips = 1.0 / ps.S, iqs = 1.0 / qs.S;
+    auto resid = [&](int j) {
+      const double r = weight_of(lp[j], ps.m, a.T) * ips - weight_of(lq[j], qs.m, a.T) * iqs;
+      return r > 0.0 ? r : 0.0;
+    };
     for (int c = 0; c < nc; ++c) {
       double s = 0.0;
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
         const int j = c * kStatChunk + tid + NT * k;
-        if (j < a.V) {
-          const double r = weight_of(lp[j], ps.m, a.T) / ps.S - weight_of(lq[j], qs.m, a.T) / qs.S;
-          s += r > 0.0 ? r : 0.0;
-        }
+        if (j < a.V) s += resid(j);
       }
-      s = bsum(s, sm);
-      if (tid == 0) rc[c] = s;
+      s = wave_sum_d(s);
+      if ((tid & 63) == 0) rcw[tid >> 6][c] = s;
     }
+    __syncthreads();
+    if (tid < nc) rc[tid] = (rcw[0][tid] + rcw[1][tid]) + (rcw[2][tid] + rcw[3][tid]);
     __syncthreads();
     const double tot = bsum(tid < nc ? rc[tid] : 0.0, sm);
     if (!(tot > 0.0)) return draw(row, ps, u, -1);
@@ -321,9 +329,7 @@ struct Decider {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int j = j0 + k;
-      double r = 0.0;
-      if (j < a.V) r = weight_of(lp[j], ps.m, a.T) / ps.S - weight_of(lq[j], qs.m, a.T) / qs.S;
-      wv[k] = r > 0.0 ? r : 0.0;
+      wv[k] = j < a.V ? resid(j) : 0.0;
       tsum += wv[k];
     }
     const double excl_pref = bscan(tsum, sm) - tsum;
