@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--model", choices=("8b", "32b"), default="8b", help="model shape of the isd workload")
     p.add_argument("--batch", type=int, default=None, help="slots (default: the workload's)")
     p.add_argument("--stride", type=int, default=None, help="ISD stride N (default: the workload's, 4)")
+    p.add_argument("--active", type=int, default=None,
+                   help="isd workload: prefill only slots 0..K-1 of the batch and step them as the active "
+                        "prefix (isd_step_active)")
     p.add_argument("--prompt-len", type=int, default=None)
     p.add_argument("--gen", type=int, default=None)
     p.add_argument("--profile-steps", type=int, default=6)
@@ -304,8 +307,10 @@ def cpu_baseline(shape, weights, eng, B, N, T, min_seconds=10.0, max_slots=8):
                       f"numpy; committed {n_tok} token(s) in {dt:.1f}s"}
 
 
-def prefill_engine(I, Engine, torch, shape, weights, dev, B, N, T, propose, prompt_len, gen, lora=None, chunk=16):
-    """An engine with B slots prefilled with uniformly random prompts (16 slots per call)."""
+def prefill_engine(I, Engine, torch, shape, weights, dev, B, N, T, propose, prompt_len, gen, lora=None, chunk=16,
+                   live=None):
+    """An engine with B slots, the first `live` (default all) prefilled with uniformly random
+    prompts (16 slots per call)."""
     max_seq = prompt_len + gen + 2 * N + 8
     eng = Engine(shape, weights, stride=N, temperature=T, propose=propose, seed=I.SEED_PHILOX, max_batch=B,
                  max_seq_len=max_seq, max_prefill_tokens=chunk * prompt_len, lora=lora, device=dev)
@@ -314,25 +319,25 @@ def prefill_engine(I, Engine, torch, shape, weights, dev, B, N, T, propose, prom
     prompts = I.prompts(B, prompt_len, shape.vocab)
     t0 = time.perf_counter()
     first = []
-    for s0 in range(0, B, chunk):
-        sl = list(range(s0, min(B, s0 + chunk)))
+    for s0 in range(0, live or B, chunk):
+        sl = list(range(s0, min(live or B, s0 + chunk)))
         first += eng.prefill(sl, [prompts[b] for b in sl], [gen] * len(sl)).cpu().tolist()
         torch.cuda.synchronize()
     log(f"prefill {B}x{prompt_len} in {time.perf_counter() - t0:.1f}s")
     return eng, first
 
 
-def timed_steps(eng, torch, steps, warmup, graphs):
+def timed_steps(eng, torch, steps, warmup, graphs, n_active=None):
     """Warm-up steps, then `steps` steps between two synchronizations; slot records around them."""
     eng.set_graphs(graphs)
     for _ in range(warmup):
-        eng.step()
+        eng.step(n_active)
     torch.cuda.synchronize()
     st0 = eng.slots_host()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        eng.step()
+        eng.step(n_active)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     return elapsed, st0, eng.slots_host()
@@ -342,7 +347,7 @@ def delta(st0, st1, field):
     return sum(s1[field] - s0[field] for s0, s1 in zip(st0, st1))
 
 
-def kernel_profile(eng, shape, B, N, steps):
+def kernel_profile(eng, shape, B, N, steps, n_active=None):
     """Per-op launch counts and durations (HIP events on the launch stream) over `steps` passes,
     with the algorithmic bytes / flops of the same passes."""
     R = 2 * N - 1
@@ -354,11 +359,11 @@ def kernel_profile(eng, shape, B, N, steps):
             if q:
                 ctx_rows += s["L"] + q
                 attn_keys += sum(s["L"] + i + 1 for i in range(q))
-        eng.step()
+        eng.step(n_active)
     rep = eng.profile_report()
     eng.profile(False)
     P = max(1, steps)
-    model = kernel_model(shape, B * R, N, ctx_rows / P, attn_keys / P)
+    model = kernel_model(shape, (n_active or B) * R, N, ctx_rows / P, attn_keys / P)
     kernels = {}
     for name, (n, tot_ms) in rep.items():
         e = {"launches_per_step": n / P, "avg_us": 1e3 * tot_ms / n, "ms_per_step": tot_ms / P}
@@ -553,18 +558,27 @@ def main():
     weights, _ = I.weights_torch(shape, dev)
     torch.cuda.synchronize()
     log(f"weights generated in {time.perf_counter() - t0:.1f}s")
-    eng, _ = prefill_engine(I, Engine, torch, shape, weights, dev, B, N, T, propose, pl, gen)
-    elapsed, st0, st1 = timed_steps(eng, torch, args.steps, args.warmup, not args.no_graphs)
+    K = args.active
+    if K is not None and not 1 <= K <= B:
+        raise SystemExit(f"--active must be in 1..{B}")
+    eng, _ = prefill_engine(I, Engine, torch, shape, weights, dev, B, N, T, propose, pl, gen, live=K)
+    elapsed, st0, st1 = timed_steps(eng, torch, args.steps, args.warmup, not args.no_graphs, n_active=K)
     live = sum(1 for s in st1 if s["state"] in (1, 2))
     log(f"timed {args.steps} steps: {1e3 * elapsed / args.steps:.3f} ms/step, "
         f"{delta(st0, st1, 'committed')} tokens, live slots {live}")
-    kernels, roof, ctx = kernel_profile(eng, shape, B, N, args.profile_steps)
+    kernels, roof, ctx = kernel_profile(eng, shape, B, N, args.profile_steps, n_active=K)
     name = wl.name if B == wl.batch else wl.name.rsplit("-b", 1)[0] + f"-b{B}"
     if N != wl.stride:
         name += f"-n{N}"
-    metric = METRIC if wl is I.QWEN3_8B_DECODE and N == wl.stride else \
-        f"committed tokens/s on 1 MI355X ({'8B' if wl is I.QWEN3_8B_DECODE else '32B'}-shape, batch {B}, N={N})"
-    out = report(args, name, shape, B, N, T, propose, pl, gen, elapsed, st0, st1, kernels, roof, ctx, metric)
+    if K is not None:
+        name += f"-active{K}"
+    metric = METRIC if wl is I.QWEN3_8B_DECODE and N == wl.stride and K is None else \
+        f"committed tokens/s on 1 MI355X ({'8B' if wl is I.QWEN3_8B_DECODE else '32B'}-shape, batch {B}, N={N}" + \
+        (f", {K} live slots stepped as the active prefix)" if K is not None else ")")
+    out = report(args, name, shape, K or B, N, T, propose, pl, gen, elapsed, st0, st1, kernels, roof, ctx, metric)
+    if K is not None:
+        out["config"]["batch"] = B
+        out["config"]["active_slots"] = K
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, weights, eng, B, N, T)
     emit(args, out)

@@ -118,7 +118,8 @@ typedef struct {
   int32_t t;                             /* pass counter of the Philox stream (prefill = 0) */
   int32_t n_gen, max_new;                /* generated tokens so far / stop after max_new */
   int32_t n_pages;                       /* pages in this slot's page table */
-  int32_t status;                        /* 0 or ISD_E_NONFINITE */
+  int32_t status;                        /* 0, ISD_E_NONFINITE, ISD_E_CAPACITY (KV pool empty)
+                                            or ISD_E_STATE (live past isd_step_active's n_active) */
   int32_t pending[ISD_MAX_STRIDE - 1];   /* v_1 .. v_{N-1} awaiting verification (state A) */
   int32_t q_row[ISD_MAX_STRIDE - 1];     /* logits row (previous pass) that proposed pending[i];
                                             -1: delta q (argmax proposal) */
@@ -183,6 +184,19 @@ isd_status isd_prefill(isd_ctx* ctx, int32_t n, const int32_t* slots, const int3
 isd_status isd_step(isd_ctx* ctx, int32_t* tokens, int32_t* n_commit, int32_t* n_accept,
                     void* stream);
 
+/* isd_step over the slots 0 .. n_active-1 only (1 <= n_active <= max_batch): the block rows,
+ * attention items, LoRA MASK rows and decisions of the later slots are not computed, so a
+ * partly filled context (a serving loop that admits requests into the lowest free slots and
+ * passes the highest live slot + 1) pays for its live slots only - the pages' stationary
+ * batch with admission and retirement between passes.  Every kernel computes a slot's rows
+ * from those rows alone, so a slot's tokens are bit-identical to the ones isd_step gives it.
+ * Slots at or past n_active must be EMPTY or DONE: a live one there is not advanced and gets
+ * isd_slot.status = ISD_E_STATE (reported by isd_get_status).  The outputs of those slots
+ * are not written.  With graphs enabled, one graph is captured per (buffer parity, n_active).
+ * Errors: ISD_E_ARG (NULL outputs, n_active out of range), ISD_E_STATE (nothing prefilled). */
+isd_status isd_step_active(isd_ctx* ctx, int32_t n_active, int32_t* tokens, int32_t* n_commit,
+                           int32_t* n_accept, void* stream);
+
 /* Device addresses of internal buffers (see isd_buffers). */
 /* Replay isd_step from HIP graphs (enable != 0) instead of launching its kernels one by one,
  * the serving-loop measure the pages credit with the largest throughput gain (wiki note, Key
@@ -196,7 +210,8 @@ isd_status isd_set_graphs(isd_ctx* ctx, int32_t enable);
 
 isd_status isd_get_buffers(const isd_ctx* ctx, isd_buffers* out);
 
-/* Synchronize `stream` and return the sticky device status (ISD_OK or ISD_E_NONFINITE). */
+/* Synchronize `stream` and return the sticky device status: ISD_OK, or the first non-zero
+ * isd_slot.status seen (ISD_E_NONFINITE, ISD_E_CAPACITY, ISD_E_STATE). */
 isd_status isd_get_status(isd_ctx* ctx, void* stream);
 
 /* Free the host-side context. */

@@ -18,7 +18,7 @@ ISD_PROPOSE_SAMPLE, ISD_PROPOSE_ARGMAX = 0, 1
 ISD_SLOT_EMPTY, ISD_SLOT_A, ISD_SLOT_B, ISD_SLOT_DONE = 0, 1, 2, 3
 
 # symbols the header declares (checked by the CPU test-suite)
-EXPORTS = ("isd_init", "isd_prefill", "isd_step", "isd_get_buffers", "isd_get_status", "isd_release",
+EXPORTS = ("isd_init", "isd_prefill", "isd_step", "isd_step_active", "isd_get_buffers", "isd_get_status", "isd_release",
            "isd_attn_workspace_bytes", "isd_attn_paged", "isd_sample_workspace_bytes", "isd_sample",
            "isd_version", "isd_profile", "isd_profile_report", "isd_gemm", "isd_gemm_splits", "isd_set_graphs",
            "isd_packed_weight_bytes", "isd_pack_weights", "isd_set_meter")
@@ -112,6 +112,7 @@ def load(path=LIB_PATH):
     lib.isd_prefill.argtypes = [C.c_void_p, C.c_int32, C.POINTER(C.c_int32), C.c_void_p, C.POINTER(C.c_int32),
                                 C.POINTER(C.c_int32), C.c_void_p, C.c_void_p]
     lib.isd_step.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+    lib.isd_step_active.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
     lib.isd_get_buffers.argtypes = [C.c_void_p, C.POINTER(Buffers)]
     lib.isd_get_status.argtypes = [C.c_void_p, C.c_void_p]
     lib.isd_release.argtypes = [C.c_void_p]
@@ -133,7 +134,8 @@ def load(path=LIB_PATH):
     lib.isd_profile.argtypes = [C.c_void_p, C.c_int32]
     lib.isd_set_graphs.argtypes = [C.c_void_p, C.c_int32]
     lib.isd_profile_report.argtypes = [C.c_void_p, C.POINTER(ProfEntry), C.c_int32, C.POINTER(C.c_int32)]
-    for f in ("isd_init", "isd_prefill", "isd_step", "isd_get_buffers", "isd_get_status", "isd_release",
+    for f in ("isd_init", "isd_prefill", "isd_step", "isd_step_active", "isd_get_buffers", "isd_get_status",
+              "isd_release",
               "isd_attn_paged", "isd_sample", "isd_profile", "isd_profile_report", "isd_set_graphs"):
         getattr(lib, f).restype = C.c_int
     _lib = lib

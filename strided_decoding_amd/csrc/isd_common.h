@@ -332,6 +332,7 @@ struct StepMeta {            // device buffers of the block / page machinery
   AttnItem* items;
   int items_per_slot, q_max;   // decode: attention items per slot, query positions per item
   int max_batch, N, P, mask_id;
+  int n_active;               // decode: the pass covers slots 0 .. n_active-1 (isd_step_active)
   int32_t* last_rows;        // prefill: last row of each prompt
   int32_t* zero_words;       // cleared once at init (arrival counters)
   int n_zero_words;

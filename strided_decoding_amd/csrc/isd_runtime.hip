@@ -9,6 +9,7 @@
 // Everything is enqueued on the caller's stream; no host synchronization happens.
 #include <algorithm>
 #include <cstring>
+#include <map>
 #include <new>
 #include <vector>
 
@@ -46,6 +47,7 @@ struct isd_ctx {
   int max_pages, max_rows, max_dec_rows, n_chunks, max_splits, items_per_slot, q_max, ncb, q_tile;
   int attn_split;         // keys per context split of a decode pass
   int max_items, n_mask, delta_w;
+  int mask_active = 0;          // MASK-row entries of the pass being enqueued (slots 0 .. nb-1)
   size_t part_floats = 0;       // split-K partial buffer (bf16 decode GEMMs)
   float* gemm_part = nullptr;
   // weights
@@ -90,7 +92,9 @@ struct isd_ctx {
   struct StepGraph {
     hipGraphExec_t exec = nullptr;
     const void *tokens = nullptr, *n_commit = nullptr, *n_accept = nullptr;
-  } step_graph[2];
+  };
+  // one graph per (logits-buffer parity, active slot count)
+  std::map<std::pair<int, int>, StepGraph> step_graph;
 };
 
 namespace {
@@ -253,6 +257,7 @@ StepMeta meta(isd_ctx& x) {
   m.items_per_slot = x.items_per_slot;
   m.q_max = x.q_max;
   m.max_batch = x.cfg.max_batch;
+  m.n_active = x.cfg.max_batch;
   m.N = x.cfg.stride_n;
   m.P = x.cfg.page_size;
   m.mask_id = x.cfg.vocab;
@@ -322,7 +327,7 @@ GemmArgs gargs(const void* A, int lda, const void* B0, int ldb, int M, int N, in
 // products into an fp32 delta that base's epilogue adds.
 isd_status lora_group(isd_ctx& x, int layer, int t0, int nt, const void* Xsrc, int ldx, int k_in, const int* n,
                       hipStream_t s, GemmArgs& base) {
-  const int r = x.cfg.lora_rank, M = x.n_mask;
+  const int r = x.cfg.lora_rank, M = x.mask_active;
   const char* const* A = (const char* const*)&x.lora_a[(size_t)layer * 7 + t0];
   const char* const* Bm = (const char* const*)&x.lora_b[(size_t)layer * 7 + t0];
   bool stackA = true, stackB = x.bf;     // segmented products: bf16 kernels only
@@ -684,19 +689,24 @@ isd_status isd_prefill(isd_ctx* x, int32_t n, const int32_t* slots, const int32_
 
 namespace {
 
-// The launches of one decode pass on stream s, reading logits buffer parity cur.
-isd_status step_launches(isd_ctx* x, int32_t* tokens, int32_t* n_commit, int32_t* n_accept, int cur, hipStream_t s) {
+// The launches of one decode pass over slots 0 .. nb-1 on stream s, reading logits buffer
+// parity cur.  The rows of slot b are b R .. b R + R-1 whatever nb is, and every kernel
+// computes a row from that row alone, so a slot's results do not depend on nb.
+isd_status step_launches(isd_ctx* x, int nb, int32_t* tokens, int32_t* n_commit, int32_t* n_accept, int cur,
+                         hipStream_t s) {
   const isd_config& c = x->cfg;
   StepMeta m = meta(*x);
+  m.n_active = nb;
   TIMEDP("assemble", launch_assemble(m, s));
-  const int M = x->max_dec_rows;
-  isd_status st = forward(*x, M, c.max_batch * x->items_per_slot, /*decode=*/true, nullptr, M,
+  const int M = nb * x->R;
+  x->mask_active = nb * (c.stride_n - 1);
+  isd_status st = forward(*x, M, nb * x->items_per_slot, /*decode=*/true, nullptr, M,
                           /*lora=*/c.lora_rank > 0 && c.stride_n > 1, s);
   if (st != ISD_OK) return st;
   const int prev = cur ^ 1;
   TIMEDP("row_stats", launch_row_stats(x->logits[cur], M, c.vocab, c.temperature, x->stats[cur], s));
   SampleArgs a = sargs(*x);
-  a.n_slots = c.max_batch;
+  a.n_slots = nb;
   a.logits = x->logits[cur];
   a.rows_per_slot = x->R;
   a.stats = x->stats[cur];
@@ -712,21 +722,22 @@ isd_status step_launches(isd_ctx* x, int32_t* tokens, int32_t* n_commit, int32_t
 }
 
 void drop_graphs(isd_ctx* x) {
-  for (auto& g : x->step_graph) {
-    if (g.exec) hipGraphExecDestroy(g.exec);
-    g = isd_ctx::StepGraph{};
-  }
+  for (auto& kv : x->step_graph)
+    if (kv.second.exec) hipGraphExecDestroy(kv.second.exec);
+  x->step_graph.clear();
 }
 
 }  // namespace
 
-isd_status isd_step(isd_ctx* x, int32_t* tokens, int32_t* n_commit, int32_t* n_accept, void* stream) {
+isd_status isd_step_active(isd_ctx* x, int32_t n_active, int32_t* tokens, int32_t* n_commit, int32_t* n_accept,
+                           void* stream) {
   if (!x || !tokens || !n_commit || !n_accept) return ISD_E_ARG;
+  if (n_active < 1 || n_active > x->cfg.max_batch) return ISD_E_ARG;
   if (!x->prefilled) return ISD_E_STATE;
   hipStream_t s = (hipStream_t)stream;
   const int cur = x->cur;
   if (x->graphs && !x->prof_on) {
-    isd_ctx::StepGraph& g = x->step_graph[cur];
+    isd_ctx::StepGraph& g = x->step_graph[{cur, (int)n_active}];
     if (g.exec && (g.tokens != tokens || g.n_commit != n_commit || g.n_accept != n_accept)) {
       hipGraphExecDestroy(g.exec);
       g = isd_ctx::StepGraph{};
@@ -734,7 +745,7 @@ isd_status isd_step(isd_ctx* x, int32_t* tokens, int32_t* n_commit, int32_t* n_a
     if (!g.exec) {
       hipGraph_t graph = nullptr;
       HIP_OK(hipStreamBeginCapture(x->cap_stream, hipStreamCaptureModeRelaxed));
-      const isd_status st = step_launches(x, tokens, n_commit, n_accept, cur, x->cap_stream);
+      const isd_status st = step_launches(x, n_active, tokens, n_commit, n_accept, cur, x->cap_stream);
       const hipError_t e = hipStreamEndCapture(x->cap_stream, &graph);
       if (st != ISD_OK) {
         if (graph) hipGraphDestroy(graph);
@@ -753,11 +764,16 @@ isd_status isd_step(isd_ctx* x, int32_t* tokens, int32_t* n_commit, int32_t* n_a
     }
     HIP_OK(hipGraphLaunch(g.exec, s));
   } else {
-    const isd_status st = step_launches(x, tokens, n_commit, n_accept, cur, s);
+    const isd_status st = step_launches(x, n_active, tokens, n_commit, n_accept, cur, s);
     if (st != ISD_OK) return st;
   }
   x->cur = cur ^ 1;
   return ISD_OK;
+}
+
+isd_status isd_step(isd_ctx* x, int32_t* tokens, int32_t* n_commit, int32_t* n_accept, void* stream) {
+  if (!x) return ISD_E_ARG;
+  return isd_step_active(x, x->cfg.max_batch, tokens, n_commit, n_accept, stream);
 }
 
 isd_status isd_set_graphs(isd_ctx* x, int32_t enable) {
@@ -799,7 +815,7 @@ isd_status isd_get_status(isd_ctx* x, void* stream) {
   if (hipMemcpy(h.data(), x->slots, h.size() * sizeof(isd_slot), hipMemcpyDeviceToHost) != hipSuccess)
     return ISD_E_HIP;
   for (const auto& sl : h)
-    if (sl.status == ISD_E_NONFINITE) x->sticky = ISD_E_NONFINITE;
+    if (sl.status != ISD_OK && x->sticky == ISD_OK) x->sticky = (isd_status)sl.status;
   return x->sticky;
 }
 

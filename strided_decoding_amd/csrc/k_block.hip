@@ -43,7 +43,12 @@ __global__ __launch_bounds__(256) void assemble_kernel(StepMeta m) {
   int popped = 0;
   for (int g0 = 0; g0 < m.max_batch; g0 += 256) {
     const int b = g0 + tid;
-    const bool valid = b < m.max_batch;
+    // slots at or past n_active sit this pass out; a live one there is an error of the caller
+    if (b >= m.n_active && b < m.max_batch) {
+      isd_slot* so = &m.slots[b];
+      if (so->state == ISD_SLOT_A || so->state == ISD_SLOT_B) so->status = ISD_E_STATE;
+    }
+    const bool valid = b < m.n_active;
     isd_slot* st = valid ? &m.slots[b] : nullptr;
     const int state = valid ? st->state : ISD_SLOT_EMPTY;
     const int L = valid ? st->L : 0;

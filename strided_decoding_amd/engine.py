@@ -173,9 +173,15 @@ class Engine:
                                                     self._s()))
         return first
 
-    def step(self):
-        A.check("isd_step", self.lib.isd_step(self.ctx, self.tokens.data_ptr(), self.n_commit.data_ptr(),
-                                              self.n_accept.data_ptr(), self._s()))
+    def step(self, n_active=None):
+        """One ISD pass over every slot, or over slots 0 .. n_active-1 (isd_step_active)."""
+        if n_active is None:
+            A.check("isd_step", self.lib.isd_step(self.ctx, self.tokens.data_ptr(), self.n_commit.data_ptr(),
+                                                  self.n_accept.data_ptr(), self._s()))
+        else:
+            A.check("isd_step_active", self.lib.isd_step_active(self.ctx, int(n_active), self.tokens.data_ptr(),
+                                                                self.n_commit.data_ptr(), self.n_accept.data_ptr(),
+                                                                self._s()))
         return self.tokens, self.n_commit, self.n_accept
 
     def status(self):

@@ -117,3 +117,72 @@ def test_admission_errors_leave_the_context_usable():
     out, _ = _run(eng, [0, 1])
     assert len(out[0]) == 5 and len(out[1]) == 5
     assert eng.status() == 0
+
+
+def _lockstep(ref, eng, slots, n_active, log, max_steps=200):
+    """Step `ref` over every slot and `eng` over the first n_active slots until the listed
+    slots are DONE; each pass's tokens, commit and accept counts of the listed slots agree."""
+    for i in range(max_steps):
+        rt, rn, ra = [t.cpu().numpy().copy() for t in ref.step()]
+        gt, gn, ga = [t.cpu().numpy().copy() for t in eng.step(n_active)]
+        torch.cuda.synchronize()
+        for b in slots:
+            assert rn[b] == gn[b] and ra[b] == ga[b], (i, b, rn[b], gn[b])
+            assert list(rt[b, :rn[b]]) == list(gt[b, :gn[b]]), (i, b)
+        log.append(i)
+        if all(s["state"] == 3 for k, s in enumerate(eng.slots_host()) if k in slots):
+            return
+    raise AssertionError("slots did not finish")
+
+
+@pytest.mark.parametrize("graphs", [False, True])
+def test_active_prefix_equals_full_batch(graphs):
+    """isd_step_active over the live prefix of a partly filled context gives every live slot
+    exactly the tokens that isd_step over all slots gives it (sampled proposals, T = 1, so the
+    stored proposal rows of the previous pass are used), also when a slot is admitted in the
+    middle of the run and the prefix grows; the page pool ends the same."""
+    w = I.weights_numpy(SHAPE, seed=0, scale=20.0)
+    mk = lambda: Engine(SHAPE, w, stride=N, temperature=1.0, propose="sample", seed=5, max_batch=6, max_seq_len=96)
+    ref, eng = mk(), mk()
+    if graphs:
+        ref.set_graphs(True)
+        eng.set_graphs(True)
+    p = I.ragged_prompts([9, 17, 30, 12], SHAPE.vocab, seed=30)
+    for e in (ref, eng):
+        e.prefill([0, 1, 2], p[:3], [12, 20, 9])
+    done = []
+    for _ in range(3):
+        rt = ref.step()
+        gt = eng.step(3)
+        torch.cuda.synchronize()
+        r, g = [t.cpu().numpy() for t in rt], [t.cpu().numpy() for t in gt]
+        for b in range(3):
+            assert r[1][b] == g[1][b] and list(r[0][b, :r[1][b]]) == list(g[0][b, :g[1][b]])
+    for e in (ref, eng):
+        e.prefill([3], [p[3]], [15])
+    _lockstep(ref, eng, [0, 1, 2, 3], 4, done)
+    assert eng.status() == 0 and ref.status() == 0
+    assert int(eng.free_stack().numel()) == eng.cfg.n_pages == int(ref.free_stack().numel())
+    assert eng.slots_host()[:4] == ref.slots_host()[:4]
+
+
+def test_live_slot_past_active_prefix_is_flagged():
+    """A live slot at or past n_active is not advanced and reports ISD_E_STATE; the slots in
+    the prefix advance normally."""
+    w = I.weights_numpy(SHAPE, seed=0, scale=20.0)
+    eng = _engine(w, 6)
+    p = I.ragged_prompts([10, 14], SHAPE.vocab, seed=31)
+    eng.prefill([0, 4], p, [8, 8])
+    before = eng.slots_host()[4]
+    tok, nc, _ = eng.step(2)
+    torch.cuda.synchronize()
+    assert int(nc.cpu().numpy()[0]) >= 1
+    after = eng.slots_host()
+    assert after[0]["passes"] == 1
+    assert {k: v for k, v in after[4].items() if k != "status"} == {k: v for k, v in before.items() if k != "status"}
+    assert after[4]["status"] == -4
+    assert eng.status() == -4
+    with pytest.raises(IsdError, match="ISD_E_ARG"):
+        eng.step(7)
+    with pytest.raises(IsdError, match="ISD_E_ARG"):
+        eng.step(0)
