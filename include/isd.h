@@ -201,9 +201,9 @@ isd_status isd_step_active(isd_ctx* ctx, int32_t n_active, int32_t* tokens, int3
 /* Replay isd_step from HIP graphs (enable != 0) instead of launching its kernels one by one,
  * the serving-loop measure the pages credit with the largest throughput gain (wiki note, Key
  * claims; GeekNews, Serving).  A pass's launch sequence depends only on the configuration and
- * on which of the two logits buffers it writes, so the library captures it once per buffer
- * parity (on an internal stream, at the first isd_step after enabling) and then launches the
- * graph on the caller's stream.  Results are identical to eager launches.  A graph is
+ * on which of the two logits buffers it writes (and, for isd_step_active, on n_active), so the
+ * library captures it once per buffer parity and slot count (on an internal stream, at the
+ * first such pass after enabling) and then launches the graph on the caller's stream.  Results are identical to eager launches.  A graph is
  * re-captured when isd_step receives different output pointers; profiling (isd_profile)
  * launches eagerly.  enable = 0 frees the graphs.  Errors: ISD_E_ARG, ISD_E_HIP. */
 isd_status isd_set_graphs(isd_ctx* ctx, int32_t enable);
