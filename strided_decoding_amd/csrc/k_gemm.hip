@@ -787,6 +787,16 @@ hipError_t finish(const GemmArgs& a, int S, hipStream_t s) {
   return hipSuccess;
 }
 
+// CUs of the current device (queried once).
+int num_cus() {
+  static const int n = [] {
+    int dev = 0, v = 0;
+    return (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) ? v : 256;
+  }();
+  return n;
+}
+
 // Waves per workgroup of the tiled kernel.  Every workgroup of a decode-size grid runs at
 // once (one per CU), and its stage time follows the data its CU streams per stage: the
 // activation tile (14 row-group loads, padded to a multiple of the wave count) plus 4 KB of
@@ -795,25 +805,26 @@ hipError_t finish(const GemmArgs& a, int S, hipStream_t s) {
 // the wave counts whose column tiles do not straddle a segment boundary.
 template <int EPI>
 int big_waves(const GemmArgs& a, int n_mt, int S) {
-  if (a.path >= GEMM_PATH_TILED4) return 4 - (a.path - GEMM_PATH_TILED4);
-#ifdef ISD_BIG_WAVES
-  return ISD_BIG_WAVES;   // build-time override of the automatic choice (tuning)
-#endif
-  static int n_cu = 0;
-  if (!n_cu) {
-    int dev = 0, v = 0;
-    n_cu = (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) ? v : 256;
-  }
   const int tnw = EPI == EPI_SWIGLU ? 32 : 64;   // output columns per wave
-  int best = 4;
-  long best_cost = -1;
-  for (int wv = 4; wv >= 2; --wv) {
+  auto fits = [&](int wv) {                       // no column tile straddles a segment boundary
     bool ok = true;
     for (int j = 0; j + 1 < a.nseg; ++j) ok = ok && a.seg_end[j] % (wv * tnw) == 0;
     if (a.lora_r > 0)
       for (int j = 0; j + 1 < a.lora_nseg; ++j) ok = ok && a.lora_seg_end[j] % (wv * tnw) == 0;
-    if (!ok) continue;
+    return ok;
+  };
+  if (a.path >= GEMM_PATH_TILED4) {
+    const int wv = 4 - (a.path - GEMM_PATH_TILED4);
+    return fits(wv) ? wv : 4;
+  }
+#ifdef ISD_BIG_WAVES
+  return ISD_BIG_WAVES;   // build-time override of the automatic choice (tuning)
+#endif
+  const int n_cu = num_cus();
+  int best = 4;
+  long best_cost = -1;
+  for (int wv = 4; wv >= 2; --wv) {
+    if (!fits(wv)) continue;
     const long wgs = (long)n_mt * ((a.N + wv * tnw - 1) / (wv * tnw)) * S;
     const long cost = (wgs + n_cu - 1) / n_cu * (wv * ((AG + wv - 1) / wv) + 4 * wv);
     if (best_cost < 0 || cost < best_cost) best = wv, best_cost = cost;
