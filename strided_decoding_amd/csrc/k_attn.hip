@@ -290,10 +290,11 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
       const int ns = pos / a.split + 1;
       const size_t e0 = (size_t)row * a.Hq + head;
       float M = kNegInf;
-#pragma unroll 4
+      // unrolled by 8 (the loads of eight splits issued together); the sums stay in split order
+#pragma unroll 8
       for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, a.part_ml[(e0 + sp * stride) * 2]);
       float L = 0.f;
-#pragma unroll 4
+#pragma unroll 8
       for (int sp = 0; sp < ns; ++sp) {
         const size_t e = e0 + sp * stride;
         const float2 ml = *(const float2*)(a.part_ml + e * 2);

@@ -11,7 +11,8 @@
 // loads and shared by the waves; each wave loads its own weight operands straight into a
 // 4-stage register ring.  Each 64-byte LDS row keeps its four 16-byte k-chunks XOR-swizzled by
 // (row/4)%4 so that the 16 rows an MFMA operand read touches fall in distinct banks.
-// Skinny kernel (at most 128 rows): single-wave workgroups streaming 64 weight columns.
+// Skinny kernel (at most 128 rows): workgroups of two waves (one for very wide products), each
+// wave streaming 64 weight columns while the pair shares the activation stages.
 // Split-K: split s covers k-stages [s kt, (s+1) kt) and writes fp32 partials that
 // splitk_reduce_kernel sums in split order - no atomics - so every output element has a fixed
 // accumulation order that depends only on K and the split count, never on the number of rows.
