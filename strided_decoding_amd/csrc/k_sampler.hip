@@ -227,7 +227,8 @@ __device__ int cat_in_row(const float* l, int V, int nc, const double* cw_in, fl
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int j = j0 + k;
-    const double w = (j < V && j != excl) ? weight_of(l[j], m, T) : 0.0;
+    const float lj = l[min(j, V - 1)];   // unconditional load (past the row: counted as zero)
+    const double w = (j < V && j != excl) ? weight_of(lj, m, T) : 0.0;
     wv[k] = w;
     tsum += w;
   }
@@ -294,16 +295,18 @@ struct Decider {
     __shared__ double rcw[NT / 64][NT];
     const int tid = threadIdx.x;
     const double ips = 1.0 / ps.S, iqs = 1.0 / qs.S;
+    // j past the row reads its last element and counts zero: the loads carry no condition, so
+    // all of a thread's loads of a chunk are in flight together
     auto resid = [&](int j) {
-      const double r = weight_of(lp[j], ps.m, a.T) * ips - weight_of(lq[j], qs.m, a.T) * iqs;
-      return r > 0.0 ? r : 0.0;
+      const int jj = min(j, a.V - 1);
+      const double r = weight_of(lp[jj], ps.m, a.T) * ips - weight_of(lq[jj], qs.m, a.T) * iqs;
+      return (j < a.V && r > 0.0) ? r : 0.0;
     };
     for (int c = 0; c < nc; ++c) {
       double s = 0.0;
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
-        const int j = c * kStatChunk + tid + NT * k;
-        if (j < a.V) s += resid(j);
+        s += resid(c * kStatChunk + tid + NT * k);
       }
       s = wave_sum_d(s);
       if ((tid & 63) == 0) rcw[tid >> 6][c] = s;
@@ -329,7 +332,7 @@ struct Decider {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int j = j0 + k;
-      wv[k] = j < a.V ? resid(j) : 0.0;
+      wv[k] = resid(j);
       tsum += wv[k];
     }
     const double excl_pref = bscan(tsum, sm) - tsum;
