@@ -4,10 +4,12 @@
 Workload: Qwen3-8B-shaped random-init bf16 model (36 layers, d 4096, 32/8 heads x 128,
 SwiGLU 12288, vocab 151936), batch 64, stride N = 4, argmax proposals, temperature 1,
 1024-token uniformly random prompts (synthetic stand-ins for the pages' prompts and
-trained weights, which are not available).  A step is one isd_step: one ISD pass over
-all 64 slots (block assembly, page reservation, 36 layers, LM head, acceptance /
-resample / proposals, KV truncation).  `value` is committed tokens per second over the
-timed steps, with everything resident in HBM before the timed region starts.
+trained weights, which are not available).  A step is one ISD pass over all 64 slots
+(block assembly, page reservation, 36 layers, LM head, acceptance / resample / proposals,
+KV truncation), launched as isd_step_n runs of passes (one HIP graph launch each).  `value`
+is committed tokens per second over the timed steps, with everything resident in HBM
+before the timed region starts.  The default 10 + 1000 passes walk the slots' contexts from
+1034 to 2034 tokens, so the timed window averages the 1024 + 1024 workload's mean context.
 
 Prints one JSON line; progress goes to stderr.
 """
@@ -32,11 +34,17 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--steps", type=int, default=None,
+                   help="timed passes (default: 1000 for the 8B isd workload, the whole generation window; "
+                        "200 for the 32B shape, R-ISD and the microbench; 100 for the meter)")
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", choices=("isd", "risd", "meter"), default="isd",
+    p.add_argument("--workload", choices=("isd", "risd", "meter", "micro"), default="isd",
                    help="isd: decode throughput (default); risd: R-ISD == AR check and overhead factor; "
-                        "meter: introspective acceptance rate of the model's own proposals (teacher-forced)")
+                        "meter: introspective acceptance rate of the model's own proposals (teacher-forced); "
+                        "micro: the attention + acceptance kernel microbench (64 slots, contexts U[512, 4096], "
+                        "7 query rows, vocab 151936) with the oracle timed beside it")
+    p.add_argument("--passes-per-launch", type=int, default=8,
+                   help="passes per isd_step_n call (one graph launch each; 1 = isd_step)")
     p.add_argument("--model", choices=("8b", "32b"), default="8b", help="model shape of the isd workload")
     p.add_argument("--batch", type=int, default=None, help="slots (default: the workload's)")
     p.add_argument("--stride", type=int, default=None, help="ISD stride N (default: the workload's, 4)")
@@ -301,21 +309,23 @@ def cpu_baseline(shape, weights, eng, B, N, T, min_seconds=10.0, max_slots=8):
         rows += len(ids)
         ctx += L
         b += 1
-    return {"value": n_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle", "host": host_info(),
             "sample": f"one ISD pass of each of slots 0..{b - 1} ({b} of {B}): {rows} rows over synthetic KV caches "
                       f"of {ctx // b} tokens on average, {shape.n_layers} layers + LM head + decisions each, fp32 "
                       f"numpy; committed {n_tok} token(s) in {dt:.1f}s"}
 
 
 def prefill_engine(I, Engine, torch, shape, weights, dev, B, N, T, propose, prompt_len, gen, lora=None, chunk=16,
-                   live=None):
+                   live=None, max_seq=None, engine=None):
     """An engine with B slots, the first `live` (default all) prefilled with uniformly random
-    prompts (16 slots per call)."""
-    max_seq = prompt_len + gen + 2 * N + 8
-    eng = Engine(shape, weights, stride=N, temperature=T, propose=propose, seed=I.SEED_PHILOX, max_batch=B,
-                 max_seq_len=max_seq, max_prefill_tokens=chunk * prompt_len, lora=lora, device=dev)
-    log(f"engine N={N} lora={'yes' if lora else 'no'}: kv pool {eng.sizes[0] / 2**30:.1f} GiB, "
-        f"workspace {eng.sizes[1] / 2**30:.2f} GiB")
+    prompts (16 slots per call); `engine`: prefill that one's slots again instead."""
+    max_seq = max_seq or prompt_len + gen + 2 * N + 8
+    eng = engine
+    if eng is None:
+        eng = Engine(shape, weights, stride=N, temperature=T, propose=propose, seed=I.SEED_PHILOX, max_batch=B,
+                     max_seq_len=max_seq, max_prefill_tokens=chunk * prompt_len, lora=lora, device=dev)
+        log(f"engine N={N} lora={'yes' if lora else 'no'}: kv pool {eng.sizes[0] / 2**30:.1f} GiB, "
+            f"workspace {eng.sizes[1] / 2**30:.2f} GiB")
     prompts = I.prompts(B, prompt_len, shape.vocab)
     t0 = time.perf_counter()
     first = []
@@ -327,19 +337,36 @@ def prefill_engine(I, Engine, torch, shape, weights, dev, B, N, T, propose, prom
     return eng, first
 
 
-def timed_steps(eng, torch, steps, warmup, graphs, n_active=None):
-    """Warm-up steps, then `steps` steps between two synchronizations; slot records around them."""
+def run_passes(eng, n, n_active, per_launch):
+    """n passes: isd_step_n runs of per_launch passes (then single passes for the rest), or
+    isd_step / isd_step_active one at a time; returns the host seconds spent in the calls."""
+    h = 0.0
+    done = 0
+    while done < n:
+        t = time.perf_counter()
+        if n_active is None and per_launch > 1 and n - done >= per_launch:
+            eng.step_n(per_launch)
+            done += per_launch
+        else:
+            eng.step(n_active)
+            done += 1
+        h += time.perf_counter() - t
+    return h
+
+
+def timed_steps(eng, torch, steps, warmup, graphs, n_active=None, per_launch=1):
+    """Warm-up steps, then `steps` steps between two synchronizations; slot records around them.
+    Also returns the host time spent enqueuing the timed passes."""
     eng.set_graphs(graphs)
-    for _ in range(warmup):
-        eng.step(n_active)
+    run_passes(eng, warmup, n_active, per_launch)
     torch.cuda.synchronize()
     st0 = eng.slots_host()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        eng.step(n_active)
+    host = run_passes(eng, steps, n_active, per_launch)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    timed_steps.host_seconds = host
     return elapsed, st0, eng.slots_host()
 
 
@@ -388,11 +415,26 @@ def kernel_profile(eng, shape, B, N, steps, n_active=None):
     return kernels, roof, ctx_rows / P
 
 
+def window_ctx_rows(st0, st1, N):
+    """Mean keys in the pages per pass (sum over live slots of L + q_len) over a timed window,
+    from the slot records at its two ends (L grows steadily; q_len alternates between the
+    B-state N rows and the A-state 2N-1 rows with random weights)."""
+    rows = 0.0
+    for s0, s1 in zip(st0, st1):
+        if s0["state"] in (1, 2):
+            rows += 0.5 * (s0["L"] + s1["L"]) + 0.5 * (N + 2 * N - 1)
+    return rows
+
+
 def report(args, wl_name, shape, B, N, T, propose, prompt_len, gen, elapsed, st0, st1, kernels, roof, ctx_rows,
            metric=METRIC):
     committed = delta(st0, st1, "committed")
     ms = 1e3 * elapsed / args.steps
+    ctx_rows = window_ctx_rows(st0, st1, N) or ctx_rows
     sb = step_bytes(shape, B * (2 * N - 1), ctx_rows)
+    live0 = [s["L"] for s in st0 if s["state"] in (1, 2)] or [0]
+    live1 = [s["L"] for s in st1 if s["state"] in (1, 2)] or [0]
+    per_launch = 1 if args.no_graphs else args.passes_per_launch
     return {
         "metric": metric, "value": committed / elapsed, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
@@ -400,7 +442,9 @@ def report(args, wl_name, shape, B, N, T, propose, prompt_len, gen, elapsed, st0
         "data": "synthetic (random-init weights N(0,0.02), uniformly random prompt ids)",
         "config": {"workload": wl_name, "batch": B, "stride": N, "prompt_len": prompt_len, "max_new": gen,
                    "propose": propose, "temperature": T, "parallelism": "single GPU",
-                   "hip_graphs": not args.no_graphs},
+                   "hip_graphs": not args.no_graphs, "passes_per_graph_launch": per_launch,
+                   "timed_context": [min(live0), max(live1)]},
+        "host_enqueue_ms_per_step": 1e3 * getattr(timed_steps, "host_seconds", 0.0) / args.steps,
         "isd_steps_per_s": args.steps / elapsed,
         "tokens_per_forward": committed / max(1, delta(st0, st1, "passes")),
         "acceptance": delta(st0, st1, "accepted") / max(1, delta(st0, st1, "verified")),
@@ -528,6 +572,155 @@ def run_meter(args, I, Engine, torch, dev):
     emit(args, out)
 
 
+def host_info():
+    """CPU model (lscpu) and the BLAS library numpy uses (threadpoolctl)."""
+    import subprocess
+    model = None
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [x for x in threadpool_info() if x.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+    except Exception:
+        pass
+    return {"cpu_model": model, "blas": blas, "nproc": os.cpu_count()}
+
+
+def run_micro(args, I, torch, dev):
+    """The attention + acceptance kernel microbench: one paged-attention launch over 64 slots
+    (32 query / 8 KV heads x 128, bf16 KV in 16-token pages under a shuffled page table, contexts
+    uniform in [512, 4096], 7 query rows) and one acceptance step over 64 x 7 rows of 151936
+    logits, with fresh logits every pass (p ~ N(0, 3^2); a pending token's verify row is its
+    proposing row + N(0, 0.3^2)).  A step is one attention launch plus one acceptance step.
+    The oracle computes the same attention and decisions on the host beside it."""
+    import numpy as np
+
+    from strided_decoding_amd import attn_paged, sample
+    cfg = I.ATTN_SAMPLER_MICRO
+    B, N, V = cfg.batch, cfg.stride, cfg.vocab
+    R = 2 * N - 1
+    steps, warm = args.steps, args.warmup
+    a = I.attn_micro(cfg)
+    ctx = a["ctx"]
+
+    def bf(x):
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    q = bf(a["q"])
+    kp = bf(a["k_pages"])
+    vp = bf(a["v_pages"]).permute(0, 1, 3, 2).contiguous()          # pages hold V transposed
+    pt = torch.from_numpy(a["page_table"]).to(dev)
+    ctx_t = torch.from_numpy(ctx).to(dev)
+    qlen = torch.full((B,), R, dtype=torch.int32, device=dev)
+    out, ws, _ = attn_paged(q, kp, vp, pt, ctx_t, qlen, cfg.n_kv_heads)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for _ in range(warm):
+        attn_paged(q, kp, vp, pt, ctx_t, qlen, cfg.n_kv_heads, out=out, workspace=ws)
+    ev[0].record()
+    for _ in range(steps):
+        attn_paged(q, kp, vp, pt, ctx_t, qlen, cfg.n_kv_heads, out=out, workspace=ws)
+    ev[1].record()
+    torch.cuda.synchronize()
+    attn_us = 1e3 * ev[0].elapsed_time(ev[1]) / steps
+    kd = cfg.n_kv_heads * cfg.head_dim
+    attn_bytes = int(ctx.sum()) * 2 * kd * 2 + 2 * B * R * cfg.n_q_heads * cfg.head_dim * 2
+    attn_flops = 4.0 * sum(sum(int(c) - R + i + 1 for i in range(R)) for c in ctx) * cfg.n_q_heads * cfg.head_dim
+    log(f"micro: attention {attn_us:.1f} us per launch, {attn_bytes / attn_us / 1e3:.0f} GB/s")
+
+    # acceptance steps with fresh logits (the state machine runs on; q rows from the previous pass)
+    g = torch.Generator(device=dev).manual_seed(7)
+    slots = torch.zeros((B, 32), dtype=torch.int32, device=dev)
+    slots[:, 0], slots[:, 1], slots[:, 3], slots[:, 5] = 2, 100, 1, 1 << 30
+    slots[:, 8:22] = -1
+    bufs = [torch.empty((B, R, V), dtype=torch.float32, device=dev) for _ in range(2)]
+    bufs[1].normal_(0.0, cfg.p_std, generator=g)
+    tok = torch.empty((B, N), dtype=torch.int32, device=dev)
+    nc = torch.empty(B, dtype=torch.int32, device=dev)
+    na = torch.empty(B, dtype=torch.int32, device=dev)
+    sws = None
+    samp_ms = 0.0
+    evs = []
+    for it in range(warm + steps):
+        cur, prev = bufs[it & 1], bufs[(it & 1) ^ 1]
+        cur.normal_(0.0, cfg.p_std, generator=g)
+        q_row = slots[:, 15:15 + N - 1].long().clamp(min=0)
+        src = prev.view(B * R, V)[q_row.reshape(-1)].view(B, N - 1, V)
+        noisy = src + cfg.q_noise_std * torch.randn(src.shape, generator=g, device=dev)
+        cur[:, :N - 1] = torch.where((slots[:, 0] == 1)[:, None, None], noisy, cur[:, :N - 1])
+        if it == warm:
+            st0 = slots.cpu().numpy().copy()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        sws = sample(slots, cur, prev.view(B * R, V), N, 1.0, "sample", I.SEED_PHILOX, tok, nc, na, workspace=sws)
+        e[1].record()
+        if it >= warm:
+            evs.append(e)
+    torch.cuda.synchronize()
+    samp_ms = sum(e[0].elapsed_time(e[1]) for e in evs)
+    samp_us = 1e3 * samp_ms / steps
+    st1 = slots.cpu().numpy()
+    d = st1 - st0
+    acc = d[:, 23].sum() / max(1, d[:, 24].sum())
+    tpf = d[:, 25].sum() / max(1, d[:, 22].sum())
+    samp_bytes = B * R * V * 4 * 2          # the pass's rows once for the statistics, the previous rows once
+    log(f"micro: acceptance step {samp_us:.1f} us, acceptance {acc:.4f}, tokens per forward {tpf:.4f} "
+        f"(closed form at that acceptance {tpf_projection(acc, N):.4f})")
+
+    # the oracle on the same inputs: attention of every slot, decisions of every slot
+    cpu = None
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        from oracle import isd as OI
+        from oracle import model as M
+        threads = sum(x.get("num_threads", 0) for x in threadpool_info() if x.get("user_api") == "blas") or 1
+        k_np = M.f32(a["k_pages"])
+        v_np = M.f32(a["v_pages"])
+        q_np = M.f32(a["q"])
+        t0 = time.perf_counter()
+        for b in range(B):
+            c = int(ctx[b])
+            M.paged_attention(q_np[b], k_np, v_np, a["page_table"][b], c, c - R + np.arange(R),
+                              cfg.n_q_heads // cfg.n_kv_heads, cfg.page_size)
+        t_attn = time.perf_counter() - t0
+        lg = I.sampler_micro(cfg)
+        t0 = time.perf_counter()
+        for b in range(B):
+            OI.decide("B", 100, 1, b, [], [], lg["p_logits"][b], N, 1.0, "sample", I.SEED_PHILOX)
+        t_samp = time.perf_counter() - t0
+        cpu = {"value": 1e6 * (t_attn + t_samp), "unit": "us per step", "cores": threads, "kind": "oracle",
+               "sample": f"the whole step: attention of all {B} slots (contexts {int(ctx.min())}..{int(ctx.max())}) "
+                         f"{t_attn:.2f}s and the B-state decisions of all {B} slots on the recipe's logits "
+                         f"{t_samp:.2f}s, fp32/fp64 numpy",
+               "host": host_info()}
+    us = attn_us + samp_us
+    out = {
+        "metric": "attention + acceptance microbench time per step (64 slots, N=4, contexts U[512,4096], "
+                  "vocab 151936)",
+        "value": us, "unit": "us", "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": us / 1e3,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16 attention, fp32 logits",
+        "data": "synthetic (N(0,1) bf16 Q/K/V, shuffled page table; N(0,3^2) logits with N(0,0.3^2) proposal noise)",
+        "config": {"workload": "attn-accept-micro-b64", "batch": B, "stride": N, "ctx": [cfg.ctx_lo, cfg.ctx_hi],
+                   "vocab": V},
+        "attention_us": attn_us, "attention_GBps": attn_bytes / attn_us / 1e3,
+        "acceptance_step_us": samp_us, "acceptance_step_GBps": samp_bytes / samp_us / 1e3,
+        "acceptance": acc, "tokens_per_forward": tpf, "tpf_formula_at_measured_acceptance": tpf_projection(acc, N),
+        "roofline": {"bound": "hbm", "achieved": attn_bytes / attn_us / 1e3, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": attn_bytes / attn_us / 1e3 / HBM_PEAK_GBS, "traffic": None, "kernel": "attention",
+                     "per_launch": {"bytes": attn_bytes, "flops": attn_flops, "avg_us": attn_us}},
+    }
+    if cpu:
+        out["cpu_baseline"] = cpu
+    emit(args, out)
+
+
 def main():
     args = parse()
     if args.trace_summary:
@@ -537,7 +730,7 @@ def main():
     if args.copy_probe_mib:
         return copy_probe(args.copy_probe_mib)
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on exactly one GPU; --gpus must be 1"}))
         sys.exit(2)
     import torch
 
@@ -545,6 +738,11 @@ def main():
     from strided_decoding_amd import Engine
 
     dev = torch.device("cuda:0")
+    if args.steps is None:
+        args.steps = {"risd": 200, "meter": 100, "micro": 200}.get(args.workload,
+                                                                   200 if args.model == "32b" else 1000)
+    if args.workload == "micro":
+        return run_micro(args, I, torch, dev)
     if args.workload == "risd":
         return run_risd(args, I, Engine, torch, dev)
     if args.workload == "meter":
@@ -562,10 +760,33 @@ def main():
     if K is not None and not 1 <= K <= B:
         raise SystemExit(f"--active must be in 1..{B}")
     eng, _ = prefill_engine(I, Engine, torch, shape, weights, dev, B, N, T, propose, pl, gen, live=K)
-    elapsed, st0, st1 = timed_steps(eng, torch, args.steps, args.warmup, not args.no_graphs, n_active=K)
+    elapsed, st0, st1 = timed_steps(eng, torch, args.steps, args.warmup, not args.no_graphs, n_active=K,
+                                    per_launch=1 if args.no_graphs else args.passes_per_launch)
     live = sum(1 for s in st1 if s["state"] in (1, 2))
     log(f"timed {args.steps} steps: {1e3 * elapsed / args.steps:.3f} ms/step, "
         f"{delta(st0, st1, 'committed')} tokens, live slots {live}")
+    # per-kernel figures at the timed window's mean context: the live slots are prefilled again
+    # with prompts of that length (the timed passes moved every context through the window)
+    prof_ctx = int(round(window_ctx_rows(st0, st1, N) / max(1, live) - 0.5 * (3 * N - 1)))
+    prof_ctx = max(1, min(prof_ctx, pl + gen - 64))
+
+    def reprefill():
+        prefill_engine(I, Engine, torch, shape, weights, dev, B, N, T, propose, prof_ctx, pl + gen - prof_ctx,
+                       live=K, chunk=8, engine=eng)
+
+    reprefill()
+    graph_ab = None
+    if K is None and not args.no_graphs:
+        graph_ab = {}
+        for per in (1, args.passes_per_launch):
+            run_passes(eng, 2 * per, None, per)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            run_passes(eng, 4 * per, None, per)
+            torch.cuda.synchronize()
+            graph_ab[f"passes_per_launch_{per}_ms_per_step"] = 1e3 * (time.perf_counter() - t0) / (4 * per)
+            reprefill()
+        log(f"graph launches: {graph_ab}")
     kernels, roof, ctx = kernel_profile(eng, shape, B, N, args.profile_steps, n_active=K)
     name = wl.name if B == wl.batch else wl.name.rsplit("-b", 1)[0] + f"-b{B}"
     if N != wl.stride:
@@ -576,6 +797,9 @@ def main():
         f"committed tokens/s on 1 MI355X ({'8B' if wl is I.QWEN3_8B_DECODE else '32B'}-shape, batch {B}, N={N}" + \
         (f", {K} live slots stepped as the active prefix)" if K is not None else ")")
     out = report(args, name, shape, K or B, N, T, propose, pl, gen, elapsed, st0, st1, kernels, roof, ctx, metric)
+    out["kernel_profile_context"] = prof_ctx
+    if graph_ab:
+        out["graph_launch_ab"] = graph_ab
     if K is not None:
         out["config"]["batch"] = B
         out["config"]["active_slots"] = K

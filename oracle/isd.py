@@ -5,11 +5,12 @@ and *Method*; Agentic Commons post, *How Introspective Strided Decoding Works*):
 one causal forward pass both proposes new tokens at MASK positions (distribution q)
 and re-scores the previously generated, still pending tokens under the anchor
 distribution p of the current pass; a pending token x is kept when u < p(x)/q(x);
-on the first rejection the block restarts from that position; position 1 is always
-accepted because of the logit shift; position k is accepted with probability
-p^(k-1); tokens per forward is (2 + p + ... + p^(N-2)) / (2 - p^(N-1)).
+the first rejected pending token ends the pass's accepted prefix and the next block
+resumes from its position; the logit shift makes the first new token always accepted;
+acceptance compounds geometrically along the block (the k-th position survives with
+probability p^(k-1)); the tokens per forward are (2 + p + ... + p^(N-2)) / (2 - p^(N-1)).
 
-Block layout (this build's reading; the only one consistent with the 2N-1 query rows
+Block layout (the reading taken here; the only one consistent with the 2N-1 query rows
 of the pages' configurations, the TPF denominator 2 - p^(N-1) and the printed
 efficiency TPF^2 / queries-per-forward = 1.22 at N = 4, p = 0.9).  Per slot, with
 L = cached tokens and c = newest committed token (not yet cached):

@@ -9,7 +9,7 @@ is active only at MASK positions while verify positions use the base weights
 (wiki note, *Key claims* and *Method*; GeekNews, *Lossless R-ISD*).
 
 The pages give no architecture; the configurations name a Qwen3-shaped pre-norm
-decoder, which this build reads as (no biases, untied LM head, no QK-norm):
+decoder, read here as (no biases, untied LM head, no QK-norm):
 
     h  = x + Wo * Attn(RoPE(Wq n(x)), RoPE(Wk n(x)), Wv n(x)),   n = RMSNorm
     x' = h + Wd (silu(Wg n(h)) * Wu n(h))
@@ -162,6 +162,48 @@ def _lin(x, w, lora_a=None, lora_b=None, row_mask=None):
     return y.astype(np.float32)
 
 
+def layer_forward(spec, L, x, positions, ck, cv, lo=None, is_mask=None, rd=None):
+    """One pre-norm decoder layer over a block of rows of one sequence.
+
+    L: the layer's weights (attn_norm, wqkv, wo, ffn_norm, wg, wu, wd); x [R, d] float32 the
+    residual stream entering the layer; positions [R]; ck, cv [Lc, Hkv, hd] the cached keys and
+    values of positions 0 .. Lc-1; lo: None or the layer's LoRA {m: (a, b)}, applied on the
+    rows of is_mask; rd: the activation rounding of the bf16 precision model (None = none).
+    Returns (x_out [R, d], (k, v) of the block [R, Hkv, hd], attention output [R, Hq, hd]).
+    """
+    s = spec
+    rd = rd if rd is not None else (lambda a: a)
+    R = x.shape[0]
+    if is_mask is None:
+        is_mask = np.zeros(R, dtype=bool)
+    qd, kd = s.n_q_heads * s.head_dim, s.n_kv_heads * s.head_dim
+
+    def lin(inp, w, tgt):
+        if lo is None:
+            return _lin(inp, w)
+        a, b = lo[tgt]
+        return _lin(inp, w, a, b, is_mask)
+
+    h = rd(rmsnorm(x, L["attn_norm"], s.rms_eps))
+    wqkv = f32(L["wqkv"])
+    q = lin(h, wqkv[:qd], "q").reshape(R, s.n_q_heads, s.head_dim)
+    k = lin(h, wqkv[qd:qd + kd], "k").reshape(R, s.n_kv_heads, s.head_dim)
+    v = lin(h, wqkv[qd + kd:], "v").reshape(R, s.n_kv_heads, s.head_dim)
+    q = rd(apply_rope(q, positions, s.rope_base))
+    k = rd(apply_rope(k, positions, s.rope_base))
+    v = rd(v)
+    k_all = np.concatenate([ck, k], axis=0)
+    v_all = np.concatenate([cv, v], axis=0)
+    k_pos = np.concatenate([np.arange(len(ck)), positions])
+    o = rd(causal_attention(q, k_all, v_all, positions, k_pos, s.group))
+    x = x + lin(o.reshape(R, qd), L["wo"], "o")
+    h2 = rd(rmsnorm(x, L["ffn_norm"], s.rms_eps))
+    g = lin(h2, L["wg"], "g")
+    u = lin(h2, L["wu"], "u")
+    x = x + lin(rd((silu(g) * u).astype(np.float32)), L["wd"], "d")
+    return x, (k, v), o
+
+
 class Model:
     """fp32 forward of a block of rows of ONE sequence on top of its KV cache.
 
@@ -197,37 +239,15 @@ class Model:
         x = self.embed(ids)
         block_kv = []
         attn_out = []
-        qd, kd = s.n_q_heads * s.head_dim, s.n_kv_heads * s.head_dim
         for li, L in enumerate(self.w["layers"]):
             lo = self.lora[li] if self.lora is not None else None
-
-            def lin(inp, w, tgt):
-                if lo is None:
-                    return _lin(inp, w)
-                a, b = lo[tgt]
-                return _lin(inp, w, a, b, is_mask)
-
-            rd = self.rd
-            h = rd(rmsnorm(x, L["attn_norm"], s.rms_eps))
-            wqkv = f32(L["wqkv"])
-            q = lin(h, wqkv[:qd], "q").reshape(R, s.n_q_heads, s.head_dim)
-            k = lin(h, wqkv[qd:qd + kd], "k").reshape(R, s.n_kv_heads, s.head_dim)
-            v = lin(h, wqkv[qd + kd:], "v").reshape(R, s.n_kv_heads, s.head_dim)
-            q = rd(apply_rope(q, positions, s.rope_base))
-            k = rd(apply_rope(k, positions, s.rope_base))
-            v = rd(v)
-            block_kv.append((k, v))
-            ck, cv = cache[li] if cache is not None else (np.zeros((0,) + k.shape[1:], np.float32),) * 2
-            k_all = np.concatenate([ck, k], axis=0)
-            v_all = np.concatenate([cv, v], axis=0)
-            k_pos = np.concatenate([np.arange(len(ck)), positions])
-            o = rd(causal_attention(q, k_all, v_all, positions, k_pos, s.group))
+            if cache is not None:
+                ck, cv = cache[li]
+            else:
+                ck = cv = np.zeros((0, s.n_kv_heads, s.head_dim), np.float32)
+            x, kv, o = layer_forward(s, L, x, positions, ck, cv, lo, is_mask, self.rd)
+            block_kv.append(kv)
             attn_out.append(o)
-            x = x + lin(o.reshape(R, qd), L["wo"], "o")
-            h2 = rd(rmsnorm(x, L["ffn_norm"], s.rms_eps))
-            g = lin(h2, L["wg"], "g")
-            u = lin(h2, L["wu"], "u")
-            x = x + lin(rd((silu(g) * u).astype(np.float32)), L["wd"], "d")
         logits = self.rd(rmsnorm(x, self.w["final_norm"], s.rms_eps)) @ f32(self.w["lm_head"]).T
         logits = logits.astype(np.float32)
         if return_hidden:

@@ -1,10 +1,10 @@
 """Page allocator and page tables of the paged KV cache (oracle; test infrastructure only).
 
 The pages name a paged KV cache (wiki note, *TL;DR* and *Key claims*; GeekNews,
-*Serving (SGLang)*) and say that on the first rejection the block restarts from
-that position, i.e. the cache is rolled back (wiki note, *Method*).  They give no
-allocator; page tables must nevertheless be bit-identical between the oracle and
-the GPU, so this build fixes a deterministic one:
+*Serving (SGLang)*), and a rejection makes the next block resume from the rejected
+position, so the cache is rolled back to the committed length (wiki note, *Method*).
+They give no allocator; page tables must nevertheless be bit-identical between the oracle and
+the GPU, so a deterministic one is fixed here:
 
 * a LIFO free stack, stack[0 .. n_free), top at n_free - 1, initialised so that the
   first pops return pages 0, 1, 2, ...;

@@ -11,8 +11,8 @@ Weyl constants (0x9E3779B9, 0xBB67AE85).  Ten rounds are applied.  Pinned by
 the generator's published known-answer vectors (tests/golden/philox4x32_10_kat.txt).
 
 The method needs a uniform u ~ U(0,1) for every acceptance test and every
-categorical draw (wiki note, section *Method*: "u ~ U(0,1), u < p(x)/q(x)").
-The pages do not say how it is drawn; this build's reading is a counter-based
+categorical draw (wiki note, section *Method*: a uniform draw compared with p(x)/q(x)).
+The pages do not say how it is drawn; the reading taken here is a counter-based
 stream so that two implementations draw identical numbers:
 
     key     = (seed mod 2^32, seed >> 32)

@@ -16,12 +16,19 @@ STATUS_NAMES = {0: "ISD_OK", -1: "ISD_E_ARG", -2: "ISD_E_SHAPE", -3: "ISD_E_CAPA
 ISD_F32, ISD_BF16 = 0, 1
 ISD_PROPOSE_SAMPLE, ISD_PROPOSE_ARGMAX = 0, 1
 ISD_SLOT_EMPTY, ISD_SLOT_A, ISD_SLOT_B, ISD_SLOT_DONE = 0, 1, 2, 3
+ISD_DEC_ACCEPT, ISD_DEC_RESID, ISD_DEC_Z1, ISD_DEC_PROPOSE = 0, 1, 2, 3
+DEC_NAMES = {ISD_DEC_ACCEPT: "accept", ISD_DEC_RESID: "resid", ISD_DEC_Z1: "z1", ISD_DEC_PROPOSE: "propose"}
+ISD_DEBUG_MAX_ROWS = 64
+# a status only the device reports (an enqueuing call returns it as the context's sticky
+# status); ISD_E_CAPACITY and ISD_E_STATE are also host refusals (isd_get_status tells them apart)
+DEVICE_STATUSES = (-6,)
 
 # symbols the header declares (checked by the CPU test-suite)
-EXPORTS = ("isd_init", "isd_prefill", "isd_step", "isd_step_active", "isd_get_buffers", "isd_get_status", "isd_release",
-           "isd_attn_workspace_bytes", "isd_attn_paged", "isd_sample_workspace_bytes", "isd_sample",
-           "isd_version", "isd_profile", "isd_profile_report", "isd_gemm", "isd_gemm_splits", "isd_set_graphs",
-           "isd_packed_weight_bytes", "isd_pack_weights", "isd_set_meter")
+EXPORTS = ("isd_init", "isd_prefill", "isd_step", "isd_step_active", "isd_step_n", "isd_get_buffers",
+           "isd_get_status", "isd_release", "attn_paged_decode_workspace_bytes", "attn_paged_decode",
+           "isd_sample_step_workspace_bytes", "isd_sample_step", "isd_version", "isd_profile",
+           "isd_profile_report", "isd_gemm", "isd_gemm_splits", "isd_set_graphs", "isd_packed_weight_bytes",
+           "isd_pack_weights", "isd_set_meter")
 
 ISD_GEMM_STORE, ISD_GEMM_STORE_F32, ISD_GEMM_RESID, ISD_GEMM_SWIGLU = 0, 1, 2, 3
 
@@ -77,7 +84,13 @@ class Buffers(C.Structure):
     _fields_ = [("slots", C.c_void_p), ("page_table", C.c_void_p), ("max_pages_per_slot", C.c_int32),
                 ("free_stack", C.c_void_p), ("n_free", C.c_void_p), ("logits", C.c_void_p),
                 ("rows_per_slot", C.c_int32), ("row_token", C.c_void_p), ("row_pos", C.c_void_p),
-                ("k_pool", C.c_void_p), ("v_pool", C.c_void_p), ("attn_out", C.c_void_p)]
+                ("k_pool", C.c_void_p), ("v_pool", C.c_void_p), ("attn_out", C.c_void_p),
+                ("prefill_logits", C.c_void_p)]
+
+
+class Debug(C.Structure):
+    _fields_ = [("n_rows", C.c_int32), ("rows", C.c_void_p), ("layer_in", C.c_void_p), ("layer_attn", C.c_void_p),
+                ("final_normed", C.c_void_p), ("margins", C.c_void_p), ("kinds", C.c_void_p)]
 
 
 class AttnArgs(C.Structure):
@@ -92,7 +105,8 @@ class SampleArgs(C.Structure):
     _fields_ = [("batch", C.c_int32), ("stride_n", C.c_int32), ("vocab", C.c_int32), ("propose", C.c_int32),
                 ("q_rows", C.c_int32), ("temperature", C.c_float), ("seed", C.c_uint64), ("slots", C.c_void_p),
                 ("logits", C.c_void_p), ("q_logits", C.c_void_p), ("tokens", C.c_void_p),
-                ("n_commit", C.c_void_p), ("n_accept", C.c_void_p), ("workspace", C.c_void_p), ("meter", C.c_int32)]
+                ("n_commit", C.c_void_p), ("n_accept", C.c_void_p), ("workspace", C.c_void_p), ("meter", C.c_int32),
+                ("margins", C.c_void_p), ("kinds", C.c_void_p)]
 
 
 _lib = None
@@ -111,17 +125,18 @@ def load(path=LIB_PATH):
                              C.POINTER(C.c_void_p), C.c_void_p]
     lib.isd_prefill.argtypes = [C.c_void_p, C.c_int32, C.POINTER(C.c_int32), C.c_void_p, C.POINTER(C.c_int32),
                                 C.POINTER(C.c_int32), C.c_void_p, C.c_void_p]
-    lib.isd_step.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+    lib.isd_step.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(Debug), C.c_void_p]
+    lib.isd_step_n.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
     lib.isd_step_active.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
     lib.isd_get_buffers.argtypes = [C.c_void_p, C.POINTER(Buffers)]
     lib.isd_get_status.argtypes = [C.c_void_p, C.c_void_p]
     lib.isd_release.argtypes = [C.c_void_p]
-    lib.isd_attn_workspace_bytes.argtypes = [C.POINTER(AttnArgs)]
-    lib.isd_attn_workspace_bytes.restype = C.c_size_t
-    lib.isd_attn_paged.argtypes = [C.POINTER(AttnArgs), C.c_void_p]
-    lib.isd_sample_workspace_bytes.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_int32]
-    lib.isd_sample_workspace_bytes.restype = C.c_size_t
-    lib.isd_sample.argtypes = [C.POINTER(SampleArgs), C.c_void_p]
+    lib.attn_paged_decode_workspace_bytes.argtypes = [C.POINTER(AttnArgs)]
+    lib.attn_paged_decode_workspace_bytes.restype = C.c_size_t
+    lib.attn_paged_decode.argtypes = [C.POINTER(AttnArgs), C.c_void_p]
+    lib.isd_sample_step_workspace_bytes.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_int32]
+    lib.isd_sample_step_workspace_bytes.restype = C.c_size_t
+    lib.isd_sample_step.argtypes = [C.POINTER(SampleArgs), C.c_void_p]
     lib.isd_version.restype = C.c_char_p
     lib.isd_gemm.argtypes = [C.POINTER(GemmArgs), C.c_void_p]
     lib.isd_gemm.restype = C.c_int
@@ -134,9 +149,9 @@ def load(path=LIB_PATH):
     lib.isd_profile.argtypes = [C.c_void_p, C.c_int32]
     lib.isd_set_graphs.argtypes = [C.c_void_p, C.c_int32]
     lib.isd_profile_report.argtypes = [C.c_void_p, C.POINTER(ProfEntry), C.c_int32, C.POINTER(C.c_int32)]
-    for f in ("isd_init", "isd_prefill", "isd_step", "isd_step_active", "isd_get_buffers", "isd_get_status",
-              "isd_release",
-              "isd_attn_paged", "isd_sample", "isd_profile", "isd_profile_report", "isd_set_graphs"):
+    for f in ("isd_init", "isd_prefill", "isd_step", "isd_step_active", "isd_step_n", "isd_get_buffers",
+              "isd_get_status", "isd_release", "attn_paged_decode", "isd_sample_step", "isd_profile",
+              "isd_profile_report", "isd_set_graphs", "isd_set_meter", "isd_pack_weights"):
         getattr(lib, f).restype = C.c_int
     _lib = lib
     return lib

@@ -127,11 +127,14 @@ struct AttnItem {              // query rows row0 .. row0+nq-1 of one slot at po
   int32_t slot, row0, nq, pos0;
 };
 
-// Per-row, per-chunk statistics of a logits row: max m_c, lowest argmax, and
-// s_c = sum_j exp((l_j - m_c)/T) over the chunk (double).
+// Per-row, per-chunk statistics of a logits row: max m_c, lowest argmax, the second largest
+// logit m2_c (equal to m_c when the maximum occurs twice), and s_c = sum_j exp((l_j - m_c)/T)
+// over the chunk (double).
 struct ChunkStat {
   float m;
+  float m2;
   int32_t arg;
+  int32_t pad;
   double s;
 };
 
@@ -293,7 +296,7 @@ template <typename T>
 hipError_t launch_rmsnorm(const float* X, const T* g, T* Y, int rows, int d, float eps, hipStream_t s);
 
 struct RopeAppendArgs {
-  const void* qkv;           // [rows, (Hq+2Hkv)*hd] act
+  const float* qkv;          // [rows, (Hq+2Hkv)*hd] fp32 (the projection, unrounded)
   void* q_out;               // [rows, Hq*hd] act
   void* k_pool;              // layer base
   void* v_pool;
@@ -305,8 +308,8 @@ struct RopeAppendArgs {
   const float* sin_t;
   int rows, Hq, Hkv, hd, P;
   // Optional: read the projection from its split-K partials (part != null: fp32
-  // [splits, rows, (Hq+2Hkv)*hd], summed in split order, plus the LoRA delta of MASK rows,
-  // rounded to act) instead of qkv - the same values the split-K reduce would store.
+  // [splits, rows, (Hq+2Hkv)*hd], summed in split order, plus the LoRA delta of MASK rows)
+  // instead of qkv.  Either way q, k and v are rounded to act once, after RoPE.
   const float* part;
   int splits;
   const int32_t* delta_row;  // -1 / null: no delta
@@ -336,6 +339,7 @@ struct StepMeta {            // device buffers of the block / page machinery
   int32_t* last_rows;        // prefill: last row of each prompt
   int32_t* zero_words;       // cleared once at init (arrival counters)
   int n_zero_words;
+  int32_t* sticky_host;      // pinned host word: the first non-zero slot status (0 = none), or null
 };
 hipError_t launch_init_state(const StepMeta& m, int n_pages, hipStream_t s);
 hipError_t launch_assemble(const StepMeta& m, hipStream_t s);
@@ -376,8 +380,14 @@ struct SampleArgs {
   int prefill;               // 1: draw the first token only (t = 0, position L)
   int32_t* first_tok;        // prefill output [n_slots]
   int meter;                 // 1: commit pending tokens untested, accumulate their acceptance
+  double* margins;           // optional [n_slots, 2N]: margin of each decision (-1 past the last)
+  int32_t* kinds;            // optional [n_slots, 2N]: ISD_DEC_* of each decision (-1 past the last)
 };
 hipError_t launch_row_stats(const float* logits, int rows, int V, float T, ChunkStat* stats, hipStream_t s);
+// Debug record: dst[r, 0:width] = src[rows[r], 0:width] for r < n, zeros when rows[r] is outside
+// [0, n_src) (ld and width in elements of elem_bytes; both multiples of 16 bytes).
+hipError_t launch_debug_gather(const void* src, size_t ld, const int32_t* rows, int n, int n_src, int width,
+                               int elem_bytes, void* dst, hipStream_t s);
 hipError_t launch_decide(const SampleArgs& a, hipStream_t s);
 
 }  // namespace isd

@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cstring>
 #include <map>
+#include <tuple>
 #include <new>
 #include <vector>
 
@@ -64,7 +65,8 @@ struct isd_ctx {
   int32_t *mask_rows = nullptr, *ctx_len = nullptr, *last_rows = nullptr, *order = nullptr;
   AttnItem* items = nullptr;
   float* X = nullptr;
-  void *Xn = nullptr, *QKV = nullptr, *Qr = nullptr, *O = nullptr, *H = nullptr;
+  float* QKV = nullptr;   // the unsplit QKV projection in fp32 (q, k, v are rounded once, after RoPE)
+  void *Xn = nullptr, *Qr = nullptr, *O = nullptr, *H = nullptr;
   float *part_o = nullptr, *part_ml = nullptr;
   float* logits[2] = {nullptr, nullptr};
   ChunkStat* stats[2] = {nullptr, nullptr};
@@ -78,6 +80,8 @@ struct isd_ctx {
   std::vector<long long> reserved;   // admission reservation per slot (pages)
   long long reserved_total = 0;
   isd_status sticky = ISD_OK;
+  int32_t* sticky_host = nullptr;   // pinned host word the truncate kernel reports into (device address)
+  int32_t* sticky_host_h = nullptr; // the same word's host address
   // kernel timing (isd_profile)
   bool prof_on = false;
   bool prof_overflow = false;
@@ -86,15 +90,15 @@ struct isd_ctx {
   int ev_used = 0;
   // graph replay of isd_step (isd_set_graphs): one executable graph per logits-buffer parity,
   // valid for the output pointers it was captured with
-  bool graphs = false;
+  bool graphs = true;
   bool meter = false;           // introspective acceptance meter (isd_set_meter)
   hipStream_t cap_stream = nullptr;
   struct StepGraph {
     hipGraphExec_t exec = nullptr;
     const void *tokens = nullptr, *n_commit = nullptr, *n_accept = nullptr;
   };
-  // one graph per (logits-buffer parity, active slot count)
-  std::map<std::pair<int, int>, StepGraph> step_graph;
+  // one graph per (logits-buffer parity, active slot count, passes per launch)
+  std::map<std::tuple<int, int, int>, StepGraph> step_graph;
 };
 
 namespace {
@@ -172,7 +176,7 @@ size_t carve(isd_ctx& x, char* base) {
   x.items = cv.take<AttnItem>(x.max_items);
   x.X = cv.take<float>((size_t)x.max_rows * d);
   x.Xn = cv.take<char>((size_t)x.max_rows * d * x.act);
-  x.QKV = cv.take<char>((size_t)x.max_rows * x.qkvw * x.act);
+  x.QKV = cv.take<float>((size_t)x.max_rows * x.qkvw);
   x.Qr = cv.take<char>((size_t)x.max_rows * x.qd * x.act);
   x.O = cv.take<char>((size_t)x.max_rows * x.qd * x.act);
   x.H = cv.take<char>((size_t)x.max_rows * F * x.act);
@@ -264,6 +268,7 @@ StepMeta meta(isd_ctx& x) {
   m.last_rows = x.last_rows;
   m.zero_words = x.tile_cnt;
   m.n_zero_words = x.n_cnt;
+  m.sticky_host = x.sticky_host;
   return m;
 }
 
@@ -407,16 +412,25 @@ isd_status lora_group(isd_ctx& x, int layer, int t0, int nt, const void* Xsrc, i
 
 
 // The transformer body over M rows.  decode: split-context attention over the decode items;
-// prefill: one pass per item.  lm_rows: rows fed to the LM head (gather list or null = all).
+// prefill: one pass per item.  lm_rows: rows fed to the LM head (gather list or null = all),
+// whose fp32 logits go to logits_out.
 isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* lm_rows, int lm_M, bool lora,
-                   hipStream_t s) {
+                   float* logits_out, const isd_debug* dbg, hipStream_t s) {
   const isd_config& c = x.cfg;
   const int d = c.d_model, F = c.d_ffn, Hq = c.n_q_heads, Hkv = c.n_kv_heads, hd = c.head_dim;
+  const int nd = dbg ? dbg->n_rows : 0;
+  // debug record of the followed rows: dst slice `idx` of `width` elements per row
+  auto record = [&](const void* src, int width, int esize, void* dst, int idx) -> hipError_t {
+    if (!nd || !dst) return hipSuccess;
+    return launch_debug_gather(src, width, dbg->rows, nd, M, width, esize,
+                               (char*)dst + (size_t)idx * nd * width * esize, s);
+  };
   if (x.bf) TIMED("embed", launch_embed<bf16>(x.row_tok, (const bf16*)x.embed, x.X, M, d, c.vocab, s));
   else TIMED("embed", launch_embed<float>(x.row_tok, (const float*)x.embed, x.X, M, d, c.vocab, s));
   for (int l = 0; l < c.n_layers; ++l) {
     char* kl = x.k_pool + (size_t)l * x.kv_layer_bytes;
     char* vl = x.v_pool + (size_t)l * x.kv_layer_bytes;
+    HIP_OK(record(x.X, d, 4, dbg ? dbg->layer_in : nullptr, l));
     // attention block (layers after the first get their input norm from the previous
     // layer's down projection)
     if (l == 0) {
@@ -424,7 +438,7 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
       else TIMED("rmsnorm", launch_rmsnorm<float>(x.X, (const float*)x.attn_norm[0], (float*)x.Xn, M, d, c.rms_eps, s));
     }
     // QKV projection; with split-K its partials are reduced by rope_append itself
-    GemmArgs gq = plan_gemm(x, gargs(x.Xn, d, x.wqkv[l], d, M, x.qkvw, d, EPI_STORE));
+    GemmArgs gq = plan_gemm(x, gargs(x.Xn, d, x.wqkv[l], d, M, x.qkvw, d, EPI_STORE_F32));
     gq.C = x.QKV;
     gq.ldc = x.qkvw;
     if (lora) {
@@ -496,6 +510,7 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
         TIMED("attention", launch_attn_bf16(aa, s));
       }
     }
+    HIP_OK(record(x.O, x.qd, (int)x.act, dbg ? dbg->layer_attn : nullptr, l));
     {
       // O projection + residual, then the FFN input norm of the updated rows
       GemmArgs g = gargs(x.O, x.qd, x.wo[l], x.qd, M, d, x.qd, EPI_RESID);
@@ -540,9 +555,11 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
       TIMED("gemm_down", gemm(x, g, s));
     }
   }
+  HIP_OK(record(x.X, d, 4, dbg ? dbg->layer_in : nullptr, c.n_layers));
+  HIP_OK(record(x.Xn, d, (int)x.act, dbg ? dbg->final_normed : nullptr, 0));
   GemmArgs g = gargs(x.Xn, d, x.lm_head, d, lm_M, c.vocab, d, EPI_STORE_F32);
   g.a_rows = lm_rows;
-  g.C = x.logits[x.cur];
+  g.C = logits_out;
   g.ldc = c.vocab;
   TIMED("lm_head", gemm(x, g, s));
   return ISD_OK;
@@ -559,6 +576,15 @@ SampleArgs sargs(isd_ctx& x) {
   a.n_chunks = x.n_chunks;
   a.meter = x.meter ? 1 : 0;
   return a;
+}
+
+// The sticky device status as far as the host has seen it (no synchronization).
+isd_status sticky_now(isd_ctx* x) {
+  if (x->sticky == ISD_OK && x->sticky_host_h) {
+    const int32_t v = *(volatile int32_t*)x->sticky_host_h;
+    if (v != 0) x->sticky = (isd_status)v;
+  }
+  return x->sticky;
 }
 
 }  // namespace
@@ -618,11 +644,28 @@ isd_status isd_init(const isd_config* cfg, const isd_weights* w, void* kv_pool, 
   x->k_pool = (char*)kv_pool;
   x->v_pool = (char*)kv_pool + (size_t)L * x->kv_layer_bytes;
   x->reserved.assign(cfg->max_batch, 0);
+  // the sticky device status: one pinned host word the truncate kernel writes (host memory:
+  // the library still allocates no device memory)
+  void* hw = nullptr;
+  if (hipHostMalloc(&hw, 64, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess) {
+    delete x;
+    return ISD_E_HIP;
+  }
+  *(volatile int32_t*)hw = 0;
+  void* dw = nullptr;
+  if (hipHostGetDevicePointer(&dw, hw, 0) != hipSuccess) {
+    hipHostFree(hw);
+    delete x;
+    return ISD_E_HIP;
+  }
+  x->sticky_host_h = (int32_t*)hw;
+  x->sticky_host = (int32_t*)dw;
   hipStream_t s = (hipStream_t)stream;
   StepMeta m = meta(*x);
   if (launch_init_state(m, cfg->n_pages, s) != hipSuccess ||
       launch_rope_tables(x->cos_t, x->sin_t, cfg->max_seq_len + 2 * cfg->stride_n, cfg->head_dim, cfg->rope_base, s) !=
           hipSuccess) {
+    hipHostFree(hw);
     delete x;
     return ISD_E_HIP;
   }
@@ -670,7 +713,8 @@ isd_status isd_prefill(isd_ctx* x, int32_t n, const int32_t* slots, const int32_
   hipStream_t s = (hipStream_t)stream;
   StepMeta m = meta(*x);
   TIMEDP("prefill_setup", launch_prefill_setup(m, call, prompt_ids, x->q_tile, x->order, s));
-  isd_status st = forward(*x, M, call.item_off[n], /*decode=*/false, x->last_rows, n, /*lora=*/false, s);
+  isd_status st = forward(*x, M, call.item_off[n], /*decode=*/false, x->last_rows, n, /*lora=*/false,
+                          x->logits[x->cur], nullptr, s);
   if (st != ISD_OK) return st;
   TIMEDP("row_stats", launch_row_stats(x->logits[x->cur], n, c.vocab, c.temperature, x->stats[x->cur], s));
   SampleArgs a = sargs(*x);
@@ -684,7 +728,7 @@ isd_status isd_prefill(isd_ctx* x, int32_t n, const int32_t* slots, const int32_
   TIMEDP("decide", launch_decide(a, s));
   TIMEDP("truncate", launch_truncate(m, x->order, n, s));
   x->prefilled = true;
-  return ISD_OK;
+  return sticky_now(x);
 }
 
 namespace {
@@ -693,7 +737,7 @@ namespace {
 // parity cur.  The rows of slot b are b R .. b R + R-1 whatever nb is, and every kernel
 // computes a row from that row alone, so a slot's results do not depend on nb.
 isd_status step_launches(isd_ctx* x, int nb, int32_t* tokens, int32_t* n_commit, int32_t* n_accept, int cur,
-                         hipStream_t s) {
+                         const isd_debug* dbg, hipStream_t s) {
   const isd_config& c = x->cfg;
   StepMeta m = meta(*x);
   m.n_active = nb;
@@ -701,7 +745,7 @@ isd_status step_launches(isd_ctx* x, int nb, int32_t* tokens, int32_t* n_commit,
   const int M = nb * x->R;
   x->mask_active = nb * (c.stride_n - 1);
   isd_status st = forward(*x, M, nb * x->items_per_slot, /*decode=*/true, nullptr, M,
-                          /*lora=*/c.lora_rank > 0 && c.stride_n > 1, s);
+                          /*lora=*/c.lora_rank > 0 && c.stride_n > 1, x->logits[cur], dbg, s);
   if (st != ISD_OK) return st;
   const int prev = cur ^ 1;
   TIMEDP("row_stats", launch_row_stats(x->logits[cur], M, c.vocab, c.temperature, x->stats[cur], s));
@@ -716,6 +760,10 @@ isd_status step_launches(isd_ctx* x, int nb, int32_t* tokens, int32_t* n_commit,
   a.tokens = tokens;
   a.n_commit = n_commit;
   a.n_accept = n_accept;
+  if (dbg) {
+    a.margins = dbg->margins;
+    a.kinds = dbg->kinds;
+  }
   TIMEDP("decide", launch_decide(a, s));
   TIMEDP("truncate", launch_truncate(m, nullptr, c.max_batch, s));
   return ISD_OK;
@@ -727,17 +775,24 @@ void drop_graphs(isd_ctx* x) {
   x->step_graph.clear();
 }
 
-}  // namespace
-
-isd_status isd_step_active(isd_ctx* x, int32_t n_active, int32_t* tokens, int32_t* n_commit, int32_t* n_accept,
-                           void* stream) {
-  if (!x || !tokens || !n_commit || !n_accept) return ISD_E_ARG;
-  if (n_active < 1 || n_active > x->cfg.max_batch) return ISD_E_ARG;
-  if (!x->prefilled) return ISD_E_STATE;
-  hipStream_t s = (hipStream_t)stream;
+// n_passes passes over slots 0 .. nb-1: pass i writes tokens + i B N, n_commit + i B,
+// n_accept + i B.  From a captured graph (one per parity, nb and n_passes) when graphs are on
+// and the passes are neither profiled nor debugged; kernel by kernel otherwise.
+isd_status run_passes(isd_ctx* x, int nb, int n_passes, int32_t* tokens, int32_t* n_commit, int32_t* n_accept,
+                      const isd_debug* dbg, hipStream_t s) {
+  const int B = x->cfg.max_batch, N = x->cfg.stride_n;
   const int cur = x->cur;
-  if (x->graphs && !x->prof_on) {
-    isd_ctx::StepGraph& g = x->step_graph[{cur, (int)n_active}];
+  auto launches = [&](hipStream_t st) -> isd_status {
+    for (int i = 0; i < n_passes; ++i) {
+      const isd_status r = step_launches(x, nb, tokens + (size_t)i * B * N, n_commit + (size_t)i * B,
+                                         n_accept + (size_t)i * B, cur ^ (i & 1), dbg, st);
+      if (r != ISD_OK) return r;
+    }
+    return ISD_OK;
+  };
+  if (x->graphs && !x->prof_on && !dbg) {
+    if (!x->cap_stream) HIP_OK(hipStreamCreateWithFlags(&x->cap_stream, hipStreamNonBlocking));
+    isd_ctx::StepGraph& g = x->step_graph[std::make_tuple(cur, nb, n_passes)];
     if (g.exec && (g.tokens != tokens || g.n_commit != n_commit || g.n_accept != n_accept)) {
       hipGraphExecDestroy(g.exec);
       g = isd_ctx::StepGraph{};
@@ -745,7 +800,7 @@ isd_status isd_step_active(isd_ctx* x, int32_t n_active, int32_t* tokens, int32_
     if (!g.exec) {
       hipGraph_t graph = nullptr;
       HIP_OK(hipStreamBeginCapture(x->cap_stream, hipStreamCaptureModeRelaxed));
-      const isd_status st = step_launches(x, n_active, tokens, n_commit, n_accept, cur, x->cap_stream);
+      const isd_status st = launches(x->cap_stream);
       const hipError_t e = hipStreamEndCapture(x->cap_stream, &graph);
       if (st != ISD_OK) {
         if (graph) hipGraphDestroy(graph);
@@ -764,21 +819,55 @@ isd_status isd_step_active(isd_ctx* x, int32_t n_active, int32_t* tokens, int32_
     }
     HIP_OK(hipGraphLaunch(g.exec, s));
   } else {
-    const isd_status st = step_launches(x, n_active, tokens, n_commit, n_accept, cur, s);
+    const isd_status st = launches(s);
     if (st != ISD_OK) return st;
   }
-  x->cur = cur ^ 1;
-  return ISD_OK;
+  x->cur = cur ^ (n_passes & 1);
+  return sticky_now(x);
 }
 
-isd_status isd_step(isd_ctx* x, int32_t* tokens, int32_t* n_commit, int32_t* n_accept, void* stream) {
-  if (!x) return ISD_E_ARG;
-  return isd_step_active(x, x->cfg.max_batch, tokens, n_commit, n_accept, stream);
+// A debug record the context can fill: row count in range, and every recorded row width a
+// whole number of 16-byte units.
+bool debug_ok(const isd_ctx* x, const isd_debug* d) {
+  if (!d) return true;
+  if (d->n_rows < 0 || d->n_rows > ISD_DEBUG_MAX_ROWS) return false;
+  if (d->n_rows > 0 && !d->rows) return false;
+  const isd_config& c = x->cfg;
+  if ((d->layer_in || d->layer_attn || d->final_normed) && d->n_rows > 0) {
+    if (((size_t)c.d_model * 4) % 16 || ((size_t)c.d_model * x->act) % 16 || ((size_t)x->qd * x->act) % 16)
+      return false;
+  }
+  return true;
+}
+
+}  // namespace
+
+isd_status isd_step_active(isd_ctx* x, int32_t n_active, int32_t* tokens, int32_t* n_commit, int32_t* n_accept,
+                           void* stream) {
+  if (!x || !tokens || !n_commit || !n_accept) return ISD_E_ARG;
+  if (n_active < 1 || n_active > x->cfg.max_batch) return ISD_E_ARG;
+  if (!x->prefilled) return ISD_E_STATE;
+  return run_passes(x, n_active, 1, tokens, n_commit, n_accept, nullptr, (hipStream_t)stream);
+}
+
+isd_status isd_step(isd_ctx* x, int32_t* tokens, int32_t* n_commit, int32_t* n_accept, const isd_debug* debug,
+                    void* stream) {
+  if (!x || !tokens || !n_commit || !n_accept) return ISD_E_ARG;
+  if (!debug_ok(x, debug)) return ISD_E_ARG;
+  if (!x->prefilled) return ISD_E_STATE;
+  return run_passes(x, x->cfg.max_batch, 1, tokens, n_commit, n_accept, debug, (hipStream_t)stream);
+}
+
+isd_status isd_step_n(isd_ctx* x, int32_t n_passes, int32_t* tokens, int32_t* n_commit, int32_t* n_accept,
+                      void* stream) {
+  if (!x || !tokens || !n_commit || !n_accept) return ISD_E_ARG;
+  if (n_passes < 1 || n_passes > 64) return ISD_E_ARG;
+  if (!x->prefilled) return ISD_E_STATE;
+  return run_passes(x, x->cfg.max_batch, n_passes, tokens, n_commit, n_accept, nullptr, (hipStream_t)stream);
 }
 
 isd_status isd_set_graphs(isd_ctx* x, int32_t enable) {
   if (!x) return ISD_E_ARG;
-  if (enable && !x->cap_stream) HIP_OK(hipStreamCreateWithFlags(&x->cap_stream, hipStreamNonBlocking));
   if (!enable) drop_graphs(x);
   x->graphs = enable != 0;
   return ISD_OK;
@@ -805,6 +894,7 @@ isd_status isd_get_buffers(const isd_ctx* x, isd_buffers* out) {
   out->k_pool = x->k_pool;
   out->v_pool = x->v_pool;
   out->attn_out = x->O;
+  out->prefill_logits = x->logits[x->cur];
   return ISD_OK;
 }
 
@@ -814,6 +904,7 @@ isd_status isd_get_status(isd_ctx* x, void* stream) {
   std::vector<isd_slot> h(x->cfg.max_batch);
   if (hipMemcpy(h.data(), x->slots, h.size() * sizeof(isd_slot), hipMemcpyDeviceToHost) != hipSuccess)
     return ISD_E_HIP;
+  sticky_now(x);
   for (const auto& sl : h)
     if (sl.status != ISD_OK && x->sticky == ISD_OK) x->sticky = (isd_status)sl.status;
   return x->sticky;
@@ -824,6 +915,7 @@ isd_status isd_release(isd_ctx* x) {
   for (hipEvent_t e : x->ev_pool) hipEventDestroy(e);
   drop_graphs(x);
   if (x->cap_stream) hipStreamDestroy(x->cap_stream);
+  if (x->sticky_host_h) hipHostFree(x->sticky_host_h);
   delete x;
   return ISD_OK;
 }
@@ -869,7 +961,7 @@ isd_status isd_profile_report(isd_ctx* x, isd_prof_entry* out, int32_t cap, int3
   return overflow ? ISD_E_CAPACITY : ISD_OK;
 }
 
-size_t isd_attn_workspace_bytes(const isd_attn_args* a) {
+size_t attn_paged_decode_workspace_bytes(const isd_attn_args* a) {
   if (!a) return 0;
   const int splits = cdiv(std::max(1, a->max_ctx), attn_split_len(a->batch, a->n_kv_heads, a->max_ctx));
   const size_t rows = (size_t)a->batch * a->rows;
@@ -882,7 +974,7 @@ size_t isd_attn_workspace_bytes(const isd_attn_args* a) {
   return off;
 }
 
-isd_status isd_attn_paged(const isd_attn_args* a, void* stream) {
+isd_status attn_paged_decode(const isd_attn_args* a, void* stream) {
   if (!a || !a->q || !a->k_pool || !a->v_pool || !a->page_table || !a->ctx_len || !a->q_len || !a->out ||
       !a->workspace)
     return ISD_E_ARG;
@@ -988,13 +1080,13 @@ isd_status isd_pack_weights(const void* src, void* dst, int32_t rows, int32_t co
   return ISD_OK;
 }
 
-size_t isd_sample_workspace_bytes(int32_t batch, int32_t rows, int32_t vocab, int32_t q_rows) {
+size_t isd_sample_step_workspace_bytes(int32_t batch, int32_t rows, int32_t vocab, int32_t q_rows) {
   const int nc = cdiv(vocab, kStatChunk);
   return align_up((size_t)batch * rows * nc * sizeof(ChunkStat)) +
          align_up((size_t)std::max(1, q_rows) * nc * sizeof(ChunkStat));
 }
 
-isd_status isd_sample(const isd_sample_args* a, void* stream) {
+isd_status isd_sample_step(const isd_sample_args* a, void* stream) {
   if (!a || !a->slots || !a->logits || !a->tokens || !a->n_commit || !a->n_accept || !a->workspace)
     return ISD_E_ARG;
   if (a->batch < 1 || a->stride_n < 1 || a->stride_n > ISD_MAX_STRIDE || a->vocab < 2 ||
@@ -1029,6 +1121,8 @@ isd_status isd_sample(const isd_sample_args* a, void* stream) {
   sa.n_commit = a->n_commit;
   sa.n_accept = a->n_accept;
   sa.meter = a->meter != 0;
+  sa.margins = a->margins;
+  sa.kinds = a->kinds;
   HIP_OK(launch_decide(sa, s));
   return ISD_OK;
 }

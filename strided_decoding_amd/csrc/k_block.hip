@@ -50,22 +50,32 @@ __global__ __launch_bounds__(256) void assemble_kernel(StepMeta m) {
     }
     const bool valid = b < m.n_active;
     isd_slot* st = valid ? &m.slots[b] : nullptr;
-    const int state = valid ? st->state : ISD_SLOT_EMPTY;
+    int state = valid ? st->state : ISD_SLOT_EMPTY;
     const int L = valid ? st->L : 0;
-    const int q_len = state == ISD_SLOT_A ? R : (state == ISD_SLOT_B ? N : 0);
+    int q_len = state == ISD_SLOT_A ? R : (state == ISD_SLOT_B ? N : 0);
     const int have = valid ? st->n_pages : 0;
     int need = 0;
     if (q_len > 0) need = max(0, (L + q_len + P - 1) / P - have);
     int total;
     const int off = block_excl_scan(need, sh, &total);
+    // A slot whose pages do not all fit on the stack after the slots before it (host admission
+    // makes this unreachable; this is the device's own guard) takes none, is flagged
+    // ISD_E_CAPACITY and finishes: no rows, no cache writes, its pages freed by truncate.
+    // Slots are served in order, so the pages taken are one contiguous run from the top.
+    const bool fits = popped + off + need <= s_nfree;
+    const int grant = fits ? need : 0;
+    int granted;
+    block_excl_scan(grant, sh, &granted);
+    if (valid && !fits) {
+      st->status = ISD_E_CAPACITY;
+      st->state = ISD_SLOT_DONE;
+      state = ISD_SLOT_DONE;
+      q_len = 0;
+    }
     if (valid) {
       int32_t* pt = m.page_table + (size_t)b * m.max_pages;
-      for (int k = 0; k < need; ++k) {
-        const int idx = s_nfree - 1 - (popped + off + k);
-        pt[have + k] = idx >= 0 ? m.free_stack[idx] : -1;
-        if (idx < 0) st->status = ISD_E_CAPACITY;
-      }
-      st->n_pages = have + need;
+      for (int k = 0; k < grant; ++k) pt[have + k] = m.free_stack[s_nfree - 1 - (popped + off + k)];
+      st->n_pages = have + grant;
       // rows
       for (int i = 0; i < R; ++i) {
         const int r = b * R + i;
@@ -97,7 +107,7 @@ __global__ __launch_bounds__(256) void assemble_kernel(StepMeta m) {
       }
       m.ctx_len[b] = L + q_len;
     }
-    popped += total;
+    popped += granted;
   }
   __syncthreads();
   if (tid == 0) *m.n_free = s_nfree - popped;
@@ -108,8 +118,12 @@ __global__ __launch_bounds__(256) void assemble_kernel(StepMeta m) {
 __global__ __launch_bounds__(256) void truncate_kernel(StepMeta m, const int32_t* order, int n) {
   __shared__ int sh[256];
   __shared__ int s_nfree;
+  __shared__ int s_bad;           // first slot (in processing order) with a non-zero status
   const int tid = threadIdx.x;
-  if (tid == 0) s_nfree = *m.n_free;
+  if (tid == 0) {
+    s_nfree = *m.n_free;
+    s_bad = INT_MAX;
+  }
   __syncthreads();
   int pushed = 0;
   for (int g0 = 0; g0 < n; g0 += 256) {
@@ -122,6 +136,7 @@ __global__ __launch_bounds__(256) void truncate_kernel(StepMeta m, const int32_t
       have = st.n_pages;
       keep = (st.state == ISD_SLOT_A || st.state == ISD_SLOT_B) ? (st.L + m.P - 1) / m.P : 0;
       frees = max(0, have - keep);
+      if (st.status != 0) atomicMin(&s_bad, i);
     }
     int total;
     const int off = block_excl_scan(frees, sh, &total);
@@ -136,7 +151,15 @@ __global__ __launch_bounds__(256) void truncate_kernel(StepMeta m, const int32_t
     pushed += total;
   }
   __syncthreads();
-  if (tid == 0) *m.n_free = s_nfree + pushed;
+  if (tid == 0) {
+    *m.n_free = s_nfree + pushed;
+    // the context's sticky status: the first slot status ever reported, kept in a pinned
+    // host word so that the host reads it without a synchronization
+    if (m.sticky_host && s_bad != INT_MAX) {
+      volatile int32_t* h = m.sticky_host;
+      if (*h == 0) *h = m.slots[order ? order[s_bad] : s_bad].status;
+    }
+  }
 }
 
 // Prefill set-up: slot by slot in call order, free the slot's old pages and take the
@@ -157,24 +180,24 @@ __global__ __launch_bounds__(256) void prefill_setup_kernel(StepMeta m, PrefillC
     __syncthreads();
     if (tid == 0) s_nfree += old;
     __syncthreads();
-    const int np = (len + m.P - 1) / m.P;
-    for (int k = tid; k < np; k += 256) {
-      const int idx = s_nfree - 1 - k;
-      pt[k] = idx >= 0 ? m.free_stack[idx] : -1;
-    }
+    // a prompt whose pages are not all on the stack (host admission makes this unreachable)
+    // takes none and finishes at once with ISD_E_CAPACITY: dead rows, empty attention items
+    const int need = (len + m.P - 1) / m.P;
+    const bool ok = need <= s_nfree;
+    const int np = ok ? need : 0;
+    for (int k = tid; k < np; k += 256) pt[k] = m.free_stack[s_nfree - 1 - k];
     for (int k = np + tid; k < m.max_pages; k += 256) pt[k] = -1;
     __syncthreads();
     if (tid == 0) {
-      const int stat = s_nfree < np ? ISD_E_CAPACITY : 0;
       s_nfree -= np;
-      st->state = ISD_SLOT_B;
+      st->state = ok ? ISD_SLOT_B : ISD_SLOT_DONE;
       st->L = len;
       st->c = 0;
       st->t = 0;
       st->n_gen = 0;
       st->max_new = c.max_new[i];
       st->n_pages = np;
-      st->status = stat;
+      st->status = ok ? 0 : ISD_E_CAPACITY;
       for (int j = 0; j < ISD_MAX_STRIDE - 1; ++j) {
         st->pending[j] = -1;
         st->q_row[j] = -1;
@@ -188,7 +211,7 @@ __global__ __launch_bounds__(256) void prefill_setup_kernel(StepMeta m, PrefillC
     }
     for (int r = c.off[i] + tid; r < c.off[i + 1]; r += 256) {
       m.row_tok[r] = prompt_ids[r];
-      m.row_pos[r] = r - c.off[i];
+      m.row_pos[r] = ok ? r - c.off[i] : -1;
       m.row_slot[r] = b;
       m.delta_row[r] = -1;
     }
@@ -197,7 +220,7 @@ __global__ __launch_bounds__(256) void prefill_setup_kernel(StepMeta m, PrefillC
       AttnItem it;
       it.slot = b;
       it.row0 = c.off[i] + k * q_tile;
-      it.nq = min(q_tile, len - k * q_tile);
+      it.nq = ok ? min(q_tile, len - k * q_tile) : 0;
       it.pos0 = k * q_tile;
       m.items[c.item_off[i] + k] = it;
     }
@@ -258,20 +281,20 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
     const int r = (int)(it / per_row), w = (int)(it % per_row);
     const int pos = a.row_pos[r];
     const int dr = (a.part && a.delta_row) ? a.delta_row[r] : -1;
-    // columns c .. c+3 of row r's projection as stored in act (or as the split-K reduce stores them)
+    // columns c .. c+3 of row r's projection in fp32 (summed from the split-K partials, or as
+    // the unsplit projection stored them): q, k and v are rounded to act once, after RoPE
     auto load4 = [&](int c, float* v) {
+      f32x4_t acc;
       if (a.part) {
         const float* pr = a.part + (size_t)r * width + c;
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        acc = (f32x4_t){0.f, 0.f, 0.f, 0.f};
         for (int sp = 0; sp < a.splits; ++sp) acc += *(const f32x4_t*)(pr + sp * split_stride);
         if (dr >= 0) acc += *(const f32x4_t*)(a.delta + (size_t)dr * a.ldd + c);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) v[jj] = to_f(from_f<T>(acc[jj]));
       } else {
-        const T* x = (const T*)a.qkv + (size_t)r * width + c;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) v[jj] = to_f(x[jj]);
+        acc = *(const f32x4_t*)(a.qkv + (size_t)r * width + c);
       }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) v[jj] = acc[jj];
     };
     if (w < qi + ki) {
       // RoPE group: head h, elements e0 .. e0+3 and their partners e0+half ..
@@ -294,6 +317,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
       T* dst = qo;
       if (!isq) {
         const int page = a.page_table[(size_t)a.row_slot[r] * a.max_pages + pos / P];
+        if (page < 0) continue;                // no page (never after a successful reserve)
         dst = (T*)a.k_pool + (((size_t)page * a.Hkv + h) * P + pos % P) * hd + e0;
       }
 #pragma unroll
@@ -310,6 +334,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
       float v[4];
       load4(qd + kd + h * hd + d0, v);
       const int page = a.page_table[(size_t)a.row_slot[r] * a.max_pages + pos / P];
+      if (page < 0) continue;
       T* vp = (T*)a.v_pool + (((size_t)page * a.Hkv + h) * hd + d0) * P + pos % P;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) vp[(size_t)jj * P] = from_f<T>(v[jj]);
@@ -328,6 +353,18 @@ __global__ void rope_tables_kernel(float* cos_t, float* sin_t, int max_pos, int 
     cos_t[idx] = (float)cos(ang);
     sin_t[idx] = (float)sin(ang);
   }
+}
+
+// Debug record: row r of dst = row rows[r] of src (zeros for an index outside [0, n_src)),
+// copied in 16-byte units.
+__global__ __launch_bounds__(256) void debug_gather_kernel(const char* src, size_t ld_bytes, const int32_t* rows,
+                                                           int n_src, int width_bytes, char* dst) {
+  const int r = blockIdx.x;
+  const int row = rows[r];
+  const bool ok = row >= 0 && row < n_src;
+  u32x4_t* d = (u32x4_t*)(dst + (size_t)r * width_bytes);
+  for (int c = threadIdx.x; c < width_bytes / 16; c += 256)
+    d[c] = ok ? *(const u32x4_t*)(src + (size_t)row * ld_bytes + 16 * (size_t)c) : (u32x4_t){0u, 0u, 0u, 0u};
 }
 
 // Context set-up: every slot EMPTY, page tables -1, free stack popping 0, 1, 2, ... first.
@@ -386,6 +423,15 @@ hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s) {
   const size_t items = (size_t)a.rows * ((a.Hq + a.Hkv) * (a.hd / 8) + a.Hkv * (a.hd / 4));
   const unsigned blocks = (unsigned)std::min<size_t>((items + 255) / 256, 4096);
   hipLaunchKernelGGL(rope_append_kernel<T>, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_gather(const void* src, size_t ld, const int32_t* rows, int n, int n_src, int width,
+                               int elem_bytes, void* dst, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if ((width * elem_bytes) % 16 || (ld * elem_bytes) % 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(debug_gather_kernel, dim3(n), dim3(256), 0, s, (const char*)src, ld * elem_bytes, rows, n_src,
+                     width * elem_bytes, (char*)dst);
   return hipGetLastError();
 }
 

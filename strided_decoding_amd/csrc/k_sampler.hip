@@ -28,7 +28,7 @@ constexpr int PER = kStatChunk / NT;   // logits per thread in a chunk
 
 __global__ __launch_bounds__(NT) void row_stats_kernel(const float* logits, int V, float T, ChunkStat* stats,
                                                        int n_chunks) {
-  __shared__ float shm[4];
+  __shared__ float shm[4], shm2[4];
   __shared__ int sha[4];
   __shared__ double shs[4];
   __shared__ int shbad[4];
@@ -36,7 +36,7 @@ __global__ __launch_bounds__(NT) void row_stats_kernel(const float* logits, int 
   const int c0 = c * kStatChunk, c1 = min(V, c0 + kStatChunk);
   const float* l = logits + (size_t)row * V;
   float v[PER];
-  float mx = kNegInf;
+  float mx = kNegInf, mx2 = kNegInf;   // largest and second largest (a repeated maximum counts twice)
   int am = INT_MAX;
   int bad = 0;
 #pragma unroll
@@ -45,16 +45,20 @@ __global__ __launch_bounds__(NT) void row_stats_kernel(const float* logits, int 
     const float x = j < c1 ? l[j] : kNegInf;
     v[k] = x;
     if (j < c1 && !isfinite(x)) bad = 1;
+    mx2 = fmaxf(mx2, fminf(mx, x));
     if (x > mx) {
       mx = x;
       am = j;
     }
   }
-  // (max, lowest index) reduction
+  // (max, lowest index) reduction; the second largest of two (max, second) pairs is the larger
+  // of the smaller maximum and the two seconds
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float m2 = __shfl_xor(mx, o, 64);
+    const float s2 = __shfl_xor(mx2, o, 64);
     const int a2 = __shfl_xor(am, o, 64);
+    mx2 = fmaxf(fminf(mx, m2), fmaxf(mx2, s2));
     if (m2 > mx || (m2 == mx && a2 < am)) {
       mx = m2;
       am = a2;
@@ -64,17 +68,21 @@ __global__ __launch_bounds__(NT) void row_stats_kernel(const float* logits, int 
   const int w = tid >> 6;
   if ((tid & 63) == 0) {
     shm[w] = mx;
+    shm2[w] = mx2;
     sha[w] = am;
     shbad[w] = bad;
   }
   __syncthreads();
   mx = shm[0];
+  mx2 = shm2[0];
   am = sha[0];
-  for (int i = 1; i < 4; ++i)
+  for (int i = 1; i < 4; ++i) {
+    mx2 = fmaxf(fminf(mx, shm[i]), fmaxf(mx2, shm2[i]));
     if (shm[i] > mx || (shm[i] == mx && sha[i] < am)) {
       mx = shm[i];
       am = sha[i];
     }
+  }
   bad = shbad[0] | shbad[1] | shbad[2] | shbad[3];
   double s = 0.0;
   if (T > 0.f && !bad) {
@@ -91,7 +99,9 @@ __global__ __launch_bounds__(NT) void row_stats_kernel(const float* logits, int 
   if (tid == 0) {
     ChunkStat cs;
     cs.m = bad ? __builtin_nanf("") : mx;
+    cs.m2 = mx2;
     cs.arg = am;
+    cs.pad = 0;
     cs.s = s;
     stats[(size_t)row * n_chunks + c] = cs;
   }
@@ -101,9 +111,10 @@ __global__ __launch_bounds__(NT) void row_stats_kernel(const float* logits, int 
 struct Smem {
   double d[NT];
   int i[NT];
-  float f[4];
+  float f[4], f2[4];
   double dw[4];
   int iw[4];
+  double margin;      // margin of the last categorical draw
 };
 
 __device__ double bsum(double v, Smem& sm) {
@@ -148,7 +159,7 @@ __device__ double bscan(double v, Smem& sm) {
 }
 
 struct RowStat {
-  float m;
+  float m, m2;        // largest and second largest logit
   int arg;
   double S;
   bool ok;
@@ -156,12 +167,13 @@ struct RowStat {
 
 // Combine the chunk statistics of one row: m = max m_c (lowest argmax), S = sum s_c e^{(m_c-m)/T}.
 __device__ RowStat row_stat(const ChunkStat* cs, int nc, float T, Smem& sm) {
-  float m = kNegInf;
+  float m = kNegInf, sec = kNegInf;
   int a = INT_MAX;
   bool bad = false;
   for (int c = threadIdx.x; c < nc; c += NT) {
     const ChunkStat x = cs[c];
     if (!isfinite(x.m)) bad = true;
+    sec = fmaxf(fminf(m, x.m), fmaxf(sec, x.m2));
     if (x.m > m || (x.m == m && x.arg < a)) {
       m = x.m;
       a = x.arg;
@@ -170,7 +182,9 @@ __device__ RowStat row_stat(const ChunkStat* cs, int nc, float T, Smem& sm) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float m2 = __shfl_xor(m, o, 64);
+    const float s2 = __shfl_xor(sec, o, 64);
     const int a2 = __shfl_xor(a, o, 64);
+    sec = fmaxf(fminf(m, m2), fmaxf(sec, s2));
     if (m2 > m || (m2 == m && a2 < a)) {
       m = m2;
       a = a2;
@@ -180,18 +194,23 @@ __device__ RowStat row_stat(const ChunkStat* cs, int nc, float T, Smem& sm) {
   __syncthreads();
   if ((threadIdx.x & 63) == 0) {
     sm.f[threadIdx.x >> 6] = m;
+    sm.f2[threadIdx.x >> 6] = sec;
     sm.iw[threadIdx.x >> 6] = a;
   }
   __syncthreads();
   m = sm.f[0];
+  sec = sm.f2[0];
   a = sm.iw[0];
-  for (int i = 1; i < 4; ++i)
+  for (int i = 1; i < 4; ++i) {
+    sec = fmaxf(fminf(m, sm.f[i]), fmaxf(sec, sm.f2[i]));
     if (sm.f[i] > m || (sm.f[i] == m && sm.iw[i] < a)) {
       m = sm.f[i];
       a = sm.iw[i];
     }
+  }
   RowStat r;
   r.m = m;
+  r.m2 = sec;
   r.arg = a;
   r.S = 0.0;
   if (T > 0.f) {
@@ -205,10 +224,21 @@ __device__ RowStat row_stat(const ChunkStat* cs, int nc, float T, Smem& sm) {
 
 ISD_DEV double weight_of(float l, float m, float T) { return (double)expf((l - m) / T); }
 
+// Margin of a draw (left in sm.margin for every thread): the distance of the target u*S to the
+// nearest edge [lo, lo + w) of the chosen token's interval, divided by S; 0 for a fallback.
+__device__ void publish_margin(int j, int cand, double lo, double w, double target, double total, Smem& sm) {
+  __syncthreads();
+  if (threadIdx.x == 0) sm.margin = 0.0;
+  __syncthreads();
+  if (cand == j && cand != INT_MAX) sm.margin = fmin(target - lo, lo + w - target) / total;
+  __syncthreads();
+}
+
 // Smallest j with (prefix of w up to j) > target, w_j = exp((l_j - m)/T) with w_excl = 0;
-// chunk weights cw (one per chunk, excl removed) locate the chunk first.
+// chunk weights cw (one per chunk, excl removed) locate the chunk first.  total: the sum of
+// the weights (target = u * total).
 __device__ int cat_in_row(const float* l, int V, int nc, const double* cw_in, float m, float T, double target,
-                          int excl, Smem& sm) {
+                          double total, int excl, Smem& sm) {
   const int tid = threadIdx.x;
   // chunk level (nc <= NT)
   const double cw = tid < nc ? cw_in[tid] : 0.0;
@@ -235,14 +265,21 @@ __device__ int cat_in_row(const float* l, int V, int nc, const double* cw_in, fl
   const double excl_pref = bscan(tsum, sm) - tsum;
   double run = base + excl_pref;
   int cand = INT_MAX, lastpos = -1;
+  double cand_lo = 0.0, cand_w = 0.0;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
+    const double lo = run;
     run += wv[k];
     if (wv[k] > 0.0) lastpos = j0 + k;
-    if (cand == INT_MAX && wv[k] > 0.0 && run > target) cand = j0 + k;
+    if (cand == INT_MAX && wv[k] > 0.0 && run > target) {
+      cand = j0 + k;
+      cand_lo = lo;
+      cand_w = wv[k];
+    }
   }
   int j = bmin_i(cand, sm);
   if (j == INT_MAX) j = bmax_i(lastpos, sm);
+  publish_margin(j, cand, cand_lo, cand_w, target, total, sm);
   return j;
 }
 
@@ -281,7 +318,7 @@ struct Decider {
       tot = bsum(threadIdx.x < nc ? cw[threadIdx.x] : 0.0, sm);
       excl = -1;
     }
-    return cat_in_row(l, a.V, nc, cw, rs.m, a.T, u * tot, excl, sm);
+    return cat_in_row(l, a.V, nc, cw, rs.m, a.T, u * tot, tot, excl, sm);
   }
 
   // normalize(max(0, p - q)) with q the previous pass's row qrow.  One sweep over the row
@@ -338,14 +375,21 @@ struct Decider {
     const double excl_pref = bscan(tsum, sm) - tsum;
     double run = base + excl_pref;
     int cand = INT_MAX, lastpos = -1;
+    double cand_lo = 0.0, cand_w = 0.0;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
+      const double lo = run;
       run += wv[k];
       if (wv[k] > 0.0) lastpos = j0 + k;
-      if (cand == INT_MAX && wv[k] > 0.0 && run > target) cand = j0 + k;
+      if (cand == INT_MAX && wv[k] > 0.0 && run > target) {
+        cand = j0 + k;
+        cand_lo = lo;
+        cand_w = wv[k];
+      }
     }
     int j = bmin_i(cand, sm);
     if (j == INT_MAX) j = bmax_i(lastpos, sm);
+    publish_margin(j, cand, cand_lo, cand_w, target, tot, sm);
     return j;
   }
 };
@@ -361,7 +405,10 @@ __global__ __launch_bounds__(NT) void decide_kernel(SampleArgs a) {
   const bool greedy = !(a.T > 0.f);
 
   if (a.prefill) {
-    if (st->state != ISD_SLOT_B) return;
+    if (st->state != ISD_SLOT_B) {     // finished at admission (no KV pages on the device)
+      if (tid == 0) a.first_tok[i] = -1;
+      return;
+    }
     const RowStat rs = D.stat_cur(i);
     int z = 0;
     if (rs.ok) {
@@ -389,6 +436,10 @@ __global__ __launch_bounds__(NT) void decide_kernel(SampleArgs a) {
   const int state = st->state;
   if (state != ISD_SLOT_A && state != ISD_SLOT_B) {
     if (tid < N) a.tokens[(size_t)b * N + tid] = -1;
+    if (tid < 2 * N) {
+      if (a.margins) a.margins[(size_t)b * 2 * N + tid] = -1.0;
+      if (a.kinds) a.kinds[(size_t)b * 2 * N + tid] = -1;
+    }
     if (tid == 0) {
       a.n_commit[b] = 0;
       a.n_accept[b] = 0;
@@ -398,6 +449,17 @@ __global__ __launch_bounds__(NT) void decide_kernel(SampleArgs a) {
   const int R = a.rows_per_slot, base_row = b * R;
   const int L = st->L, t = st->t;
   int ncommit = 0, nacc = 0, nver = 0;
+  // debug record: kind and margin of each decision in order (an argmax decision's margin is
+  // the top-2 logit gap of its row)
+  int nd = 0;
+  auto note = [&](int kind, double margin) {
+    if (tid == 0) {
+      if (a.margins) a.margins[(size_t)b * 2 * N + nd] = margin;
+      if (a.kinds) a.kinds[(size_t)b * 2 * N + nd] = kind;
+    }
+    ++nd;
+  };
+  auto gap = [](const RowStat& r) { return (double)r.m - (double)r.m2; };
   double msum = 0.0;                   // meter: acceptance probabilities of the pending tokens
   bool failed = false;
   int newL = L, newc = st->c, newstate = ISD_SLOT_A;
@@ -418,8 +480,10 @@ __global__ __launch_bounds__(NT) void decide_kernel(SampleArgs a) {
     int qr = -1;
     if (greedy || a.propose == ISD_PROPOSE_ARGMAX) {
       z = rs.arg;
+      note(ISD_DEC_PROPOSE, gap(rs));
     } else {
       z = D.draw(row, rs, philox_uniform(a.seed, b, t, pos, 1), -1);
+      note(ISD_DEC_PROPOSE, sm.margin);
       qr = row;
     }
     pend[npend] = z;
@@ -450,6 +514,7 @@ __global__ __launch_bounds__(NT) void decide_kernel(SampleArgs a) {
           msum += ok ? 1.0 : 0.0;
           ok = true;
         }
+        note(ISD_DEC_ACCEPT, a.meter ? __builtin_huge_val() : gap(ps));
       } else {
         const double px = weight_of(a.logits[(size_t)row * a.V + v], ps.m, a.T) / ps.S;
         double qx = 1.0;
@@ -464,9 +529,11 @@ __global__ __launch_bounds__(NT) void decide_kernel(SampleArgs a) {
         if (a.meter) {
           msum += fmin(1.0, px / qx);
           ok = true;
+          note(ISD_DEC_ACCEPT, __builtin_huge_val());
         } else {
           const double u = philox_uniform(a.seed, b, t, L + k, 0);
           ok = u < px / qx;
+          note(ISD_DEC_ACCEPT, fabs(u - fmin(1.0, px / qx)));
         }
       }
       if (ok) {
@@ -477,10 +544,12 @@ __global__ __launch_bounds__(NT) void decide_kernel(SampleArgs a) {
       int r;
       if (greedy) {
         r = ps.arg;
+        note(ISD_DEC_RESID, gap(ps));
       } else {
         const double u2 = philox_uniform(a.seed, b, t, L + k, 1);
         if (sampled_q) r = D.resid_draw(row, ps, qr, qs, u2);
         else r = D.draw(row, ps, u2, v);
+        note(ISD_DEC_RESID, sm.margin);
       }
       commit(r);
       rejected = true;
@@ -496,6 +565,7 @@ __global__ __launch_bounds__(NT) void decide_kernel(SampleArgs a) {
         failed = true;
       } else {
         const int z1 = greedy ? rs.arg : D.draw(row, rs, philox_uniform(a.seed, b, t, L + N, 1), -1);
+        note(ISD_DEC_Z1, greedy ? gap(rs) : sm.margin);
         commit(z1);
         for (int j = 1; j < N && !failed; ++j) propose_from(base_row + N - 1 + j, L + N + j);
         newL = L + N;
@@ -509,6 +579,7 @@ __global__ __launch_bounds__(NT) void decide_kernel(SampleArgs a) {
       failed = true;
     } else {
       const int z1 = greedy ? rs.arg : D.draw(base_row, rs, philox_uniform(a.seed, b, t, L + 1, 1), -1);
+      note(ISD_DEC_Z1, greedy ? gap(rs) : sm.margin);
       commit(z1);
       for (int j = 1; j < N && !failed; ++j) propose_from(base_row + j, L + 1 + j);
       newL = L + 1;
@@ -547,6 +618,11 @@ __global__ __launch_bounds__(NT) void decide_kernel(SampleArgs a) {
     for (int k = 0; k < N; ++k) a.tokens[(size_t)b * N + k] = k < ncommit ? s_tok[k] : -1;
     a.n_commit[b] = ncommit;
     a.n_accept[b] = nacc;
+    if (failed) nd = 0;                        // a failed pass took no decision
+    for (int k = nd; k < 2 * N; ++k) {
+      if (a.margins) a.margins[(size_t)b * 2 * N + k] = -1.0;
+      if (a.kinds) a.kinds[(size_t)b * 2 * N + k] = -1;
+    }
   }
 }
 

@@ -67,7 +67,7 @@ class Engine:
 
     def __init__(self, shape, weights, *, stride, temperature, propose="sample", seed=1, max_batch=1,
                  max_seq_len=256, n_pages=None, max_prefill_tokens=None, lora=None, page_size=16,
-                 device="cuda:0", stream=None):
+                 device="cuda:0", stream=None, graphs=None):
         self.lib = A.load()
         self.shape = shape
         self.device = torch.device(device)
@@ -146,6 +146,11 @@ class Engine:
         b = A.Buffers()
         A.check("isd_get_buffers", self.lib.isd_get_buffers(self.ctx, C.byref(b)))
         self._buf = b
+        self._prefilled = False
+        self.device_status = A.ISD_OK     # the sticky device status the last call returned
+        self._multi = {}
+        if graphs is not None:
+            self.set_graphs(graphs)
 
     def _s(self):
         return C.c_void_p(self.stream.cuda_stream)
@@ -159,6 +164,16 @@ class Engine:
             pass
 
     # ------------------------------------------------------------------ calls
+    def _enqueued(self, where, rc):
+        """A call's return: host-side errors raise; after the work was enqueued the call returns
+        the context's sticky device status, kept in self.device_status."""
+        if rc in A.DEVICE_STATUSES:
+            self.device_status = rc
+            return rc
+        A.check(where, rc)
+        self.device_status = rc
+        return rc
+
     def prefill(self, slots, prompts, max_new):
         n = len(slots)
         lens = [len(p) for p in prompts]
@@ -169,22 +184,46 @@ class Engine:
         cs = (C.c_int32 * n)(*slots)
         co = (C.c_int32 * (n + 1))(*offs.tolist())
         cm = (C.c_int32 * n)(*max_new)
-        A.check("isd_prefill", self.lib.isd_prefill(self.ctx, n, cs, ids.data_ptr(), co, cm, first.data_ptr(),
-                                                    self._s()))
+        self._enqueued("isd_prefill", self.lib.isd_prefill(self.ctx, n, cs, ids.data_ptr(), co, cm,
+                                                           first.data_ptr(), self._s()))
+        self._prefilled = True
         return first
 
-    def step(self, n_active=None):
-        """One ISD pass over every slot, or over slots 0 .. n_active-1 (isd_step_active)."""
+    def step(self, n_active=None, debug=None):
+        """One ISD pass over every slot, or over slots 0 .. n_active-1 (isd_step_active).
+        debug: an isd_debug record (make_debug) filled by the pass."""
         if n_active is None:
-            A.check("isd_step", self.lib.isd_step(self.ctx, self.tokens.data_ptr(), self.n_commit.data_ptr(),
-                                                  self.n_accept.data_ptr(), self._s()))
+            self._enqueued("isd_step", self.lib.isd_step(self.ctx, self.tokens.data_ptr(), self.n_commit.data_ptr(),
+                                                         self.n_accept.data_ptr(),
+                                                         C.byref(debug.c) if debug is not None else None, self._s()))
         else:
-            A.check("isd_step_active", self.lib.isd_step_active(self.ctx, int(n_active), self.tokens.data_ptr(),
-                                                                self.n_commit.data_ptr(), self.n_accept.data_ptr(),
-                                                                self._s()))
+            assert debug is None, "isd_step_active takes no debug record"
+            self._enqueued("isd_step_active", self.lib.isd_step_active(self.ctx, int(n_active), self.tokens.data_ptr(),
+                                                                       self.n_commit.data_ptr(),
+                                                                       self.n_accept.data_ptr(), self._s()))
         return self.tokens, self.n_commit, self.n_accept
 
+    def step_n(self, n_passes):
+        """n_passes consecutive passes (isd_step_n: one graph launch with graphs on).  Returns
+        (tokens [n, B, N], n_commit [n, B], n_accept [n, B]) device tensors."""
+        if n_passes not in self._multi:
+            B, N, dev = self.max_batch, self.N, self.device
+            self._multi[n_passes] = (torch.full((n_passes, B, N), -1, dtype=torch.int32, device=dev),
+                                     torch.zeros((n_passes, B), dtype=torch.int32, device=dev),
+                                     torch.zeros((n_passes, B), dtype=torch.int32, device=dev))
+        t, c, a = self._multi[n_passes]
+        self._enqueued("isd_step_n", self.lib.isd_step_n(self.ctx, int(n_passes), t.data_ptr(), c.data_ptr(),
+                                                         a.data_ptr(), self._s()))
+        return t, c, a
+
+    def make_debug(self, rows, layers=True, decisions=True):
+        """An isd_debug record following the pass rows `rows` (slot b's block row i is
+        b*(2N-1)+i): per-layer inputs and attention outputs and the LM head input when
+        `layers`, every slot's decision kinds and margins when `decisions`."""
+        return DebugRecord(self, rows, layers, decisions)
+
     def status(self):
+        """isd_get_status: synchronizes and returns the sticky device status."""
         return self.lib.isd_get_status(self.ctx, self._s())
 
     def profile(self, enable):
@@ -242,6 +281,14 @@ class Engine:
         rows = self.max_batch * self.R
         return self._view(b.logits, rows * V * 4, torch.float32, (self.max_batch, self.R, V))
 
+    def prefill_logits(self, n):
+        """Logits of the last prompt row of each slot of the last isd_prefill call [n, V]
+        (valid until the next pass)."""
+        b = A.Buffers()
+        A.check("isd_get_buffers", self.lib.isd_get_buffers(self.ctx, C.byref(b)))
+        V = self.shape.vocab
+        return self._view(b.prefill_logits, n * V * 4, torch.float32, (n, V))
+
     def rows(self):
         n = self.max_batch * self.R
         tok = self._view(self._buf.row_token, n * 4, torch.int32, (self.max_batch, self.R))
@@ -260,8 +307,33 @@ class Engine:
         return kp, vp
 
 
+class DebugRecord:
+    """Device buffers of one isd_debug record (see isd.h) and their torch views."""
+
+    def __init__(self, eng, rows, layers, decisions):
+        s, dev = eng.shape, eng.device
+        rows = [int(r) for r in rows]
+        if len(rows) > A.ISD_DEBUG_MAX_ROWS:
+            raise ValueError(f"at most {A.ISD_DEBUG_MAX_ROWS} rows")
+        n = len(rows)
+        act = _dt(s.dtype)
+        qd = s.n_q_heads * s.head_dim
+        self.rows = torch.tensor(rows, dtype=torch.int32, device=dev)
+        self.layer_in = self.layer_attn = self.final_normed = self.margins = self.kinds = None
+        if layers:
+            self.layer_in = torch.zeros((s.n_layers + 1, n, s.d_model), dtype=torch.float32, device=dev)
+            self.layer_attn = torch.zeros((s.n_layers, n, qd), dtype=act, device=dev)
+            self.final_normed = torch.zeros((n, s.d_model), dtype=act, device=dev)
+        if decisions:
+            self.margins = torch.zeros((eng.max_batch, 2 * eng.N), dtype=torch.float64, device=dev)
+            self.kinds = torch.zeros((eng.max_batch, 2 * eng.N), dtype=torch.int32, device=dev)
+        ptr = lambda t: 0 if t is None else t.data_ptr()
+        self.c = A.Debug(n, self.rows.data_ptr(), ptr(self.layer_in), ptr(self.layer_attn), ptr(self.final_normed),
+                         ptr(self.margins), ptr(self.kinds))
+
+
 def attn_paged(q, k_pool, v_pool, page_table, ctx_len, q_len, n_kv_heads, out=None, workspace=None, stream=None):
-    """Kernel-level paged attention (see isd_attn_paged).  q [B, R, Hq, hd] bf16 on device."""
+    """Kernel-level paged attention (see attn_paged_decode).  q [B, R, Hq, hd] bf16 on device."""
     lib = A.load()
     B, R, Hq, hd = q.shape
     P = k_pool.shape[2]
@@ -271,11 +343,12 @@ def attn_paged(q, k_pool, v_pool, page_table, ctx_len, q_len, n_kv_heads, out=No
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
-        workspace = torch.empty(lib.isd_attn_workspace_bytes(C.byref(args)), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(lib.attn_paged_decode_workspace_bytes(C.byref(args)), dtype=torch.uint8,
+                                device=q.device)
     args.out = out.data_ptr()
     args.workspace = workspace.data_ptr()
     stream = stream if stream is not None else torch.cuda.current_stream(q.device)
-    A.check("isd_attn_paged", lib.isd_attn_paged(C.byref(args), C.c_void_p(stream.cuda_stream)))
+    A.check("attn_paged_decode", lib.attn_paged_decode(C.byref(args), C.c_void_p(stream.cuda_stream)))
     return out, workspace, args
 
 
@@ -316,19 +389,21 @@ def gemm(X, W, mode="store", W2=None, out=None, R=None, splits=0, workspace=None
 
 
 def sample(slots, logits, q_logits, stride, temperature, propose, seed, tokens, n_commit, n_accept,
-           workspace=None, stream=None, meter=False):
-    """Kernel-level acceptance step (see isd_sample).  slots: int32 [B, 32] device tensor (in/out);
-    meter: the introspective acceptance meter mode (see isd_set_meter)."""
+           workspace=None, stream=None, meter=False, margins=None, kinds=None):
+    """Kernel-level acceptance step (see isd_sample_step).  slots: int32 [B, 32] device tensor
+    (in/out); meter: the introspective acceptance meter mode (see isd_set_meter); margins
+    (float64) / kinds (int32) [B, 2N]: optional decision record."""
     lib = A.load()
     B, R, V = logits.shape
     q_rows = 0 if q_logits is None else q_logits.shape[0]
     if workspace is None:
-        workspace = torch.empty(lib.isd_sample_workspace_bytes(B, R, V, q_rows), dtype=torch.uint8,
+        workspace = torch.empty(lib.isd_sample_step_workspace_bytes(B, R, V, q_rows), dtype=torch.uint8,
                                 device=logits.device)
     args = A.SampleArgs(B, stride, V, A.ISD_PROPOSE_ARGMAX if propose == "argmax" else A.ISD_PROPOSE_SAMPLE,
                         q_rows, float(temperature), int(seed), slots.data_ptr(), logits.data_ptr(),
                         0 if q_logits is None else q_logits.data_ptr(), tokens.data_ptr(), n_commit.data_ptr(),
-                        n_accept.data_ptr(), workspace.data_ptr(), 1 if meter else 0)
+                        n_accept.data_ptr(), workspace.data_ptr(), 1 if meter else 0,
+                        0 if margins is None else margins.data_ptr(), 0 if kinds is None else kinds.data_ptr())
     stream = stream if stream is not None else torch.cuda.current_stream(logits.device)
-    A.check("isd_sample", lib.isd_sample(C.byref(args), C.c_void_p(stream.cuda_stream)))
+    A.check("isd_sample_step", lib.isd_sample_step(C.byref(args), C.c_void_p(stream.cuda_stream)))
     return workspace

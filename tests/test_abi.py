@@ -22,7 +22,7 @@ def _lib():
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(isd_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b((?:isd|attn)_[a-z_0-9]+)\s*\(", src)))
 
 
 def test_header_declarations_match_binding():
@@ -94,5 +94,6 @@ def test_null_arguments_rejected():
     sizes = A.Sizes()
     ctx = C.c_void_p()
     assert lib.isd_init(None, None, None, None, C.byref(sizes), C.byref(ctx), None) == A.ISD_E_ARG
-    assert lib.isd_step(None, None, None, None, None) == A.ISD_E_ARG
+    assert lib.isd_step(None, None, None, None, None, None) == A.ISD_E_ARG
+    assert lib.isd_step_n(None, 2, None, None, None, None) == A.ISD_E_ARG
     assert lib.isd_release(None) == A.ISD_E_ARG

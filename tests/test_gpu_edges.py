@@ -6,6 +6,7 @@ Greedy decoding (T = 0, argmax proposals) makes a slot's tokens independent of i
 and of the other slots (every kernel computes a row from that row alone), so a slot decoded
 in a batch with holes must produce exactly the tokens of the same prompt decoded alone.
 """
+import numpy as np
 import pytest
 import torch
 
@@ -186,3 +187,98 @@ def test_live_slot_past_active_prefix_is_flagged():
         eng.step(7)
     with pytest.raises(IsdError, match="ISD_E_ARG"):
         eng.step(0)
+
+
+def test_nonfinite_logits_end_only_that_slot():
+    """isd_sample_step with a NaN in one slot's logits: that slot ends DONE with
+    ISD_E_NONFINITE and commits nothing; every other slot's outputs and record equal those of
+    the same call without the NaN."""
+    from strided_decoding_amd import sample
+    B, N, V = 8, 4, 3000
+    R = 2 * N - 1
+    g = torch.Generator(device=DEV).manual_seed(77)
+    logits = torch.randn((B, R, V), generator=g, device=DEV) * 3.0
+    q = torch.randn((B * R, V), generator=g, device=DEV) * 3.0
+    base = torch.zeros((B, 32), dtype=torch.int32, device=DEV)
+    base[:, 0] = torch.tensor([1, 2] * (B // 2), dtype=torch.int32)   # A and B slots
+    base[:, 1] = 50
+    base[:, 3] = 3
+    base[:, 4] = 1
+    base[:, 5] = 100
+    base[:, 8:22] = -1
+    base[:, 8:8 + N - 1] = torch.randint(0, V, (B, N - 1), generator=g, device=DEV).int()
+    base[:, 15:15 + N - 1] = (torch.arange(B, device=DEV)[:, None] * R + N +
+                              torch.arange(N - 1, device=DEV)[None, :]).int()
+    outs = []
+    for poison in (None, 3, 6):
+        slots = base.clone()
+        lg = logits.clone()
+        if poison is not None:
+            lg[poison, 0, 17] = float("nan")
+        tok = torch.full((B, N), -7, dtype=torch.int32, device=DEV)
+        nc = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+        na = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+        print(f"nonfinite logits: poisoned slot {poison}", flush=True)
+        sample(slots, lg, q, N, 1.0, "sample", 1, tok, nc, na)
+        torch.cuda.synchronize()
+        outs.append((slots.cpu().numpy(), tok.cpu().numpy(), nc.cpu().numpy(), na.cpu().numpy()))
+    ref = outs[0]
+    assert np.all(ref[0][:, 7] == 0)
+    for poison, out in zip((3, 6), outs[1:]):
+        for b in range(B):
+            if b == poison:
+                assert out[0][b, 0] == 3 and out[0][b, 7] == -6      # DONE, ISD_E_NONFINITE
+                assert out[2][b] == 0 and np.all(out[1][b] == -1)
+            else:
+                assert np.array_equal(out[0][b], ref[0][b]) and np.array_equal(out[1][b], ref[1][b])
+                assert out[2][b] == ref[2][b] and out[3][b] == ref[3][b]
+
+
+def test_nonfinite_weight_row_is_confined_to_its_slot():
+    """A NaN in the embedding row of one token: the slot whose prompt holds that token sees
+    non-finite logits at its prefill and ends DONE with ISD_E_NONFINITE; the context's sticky
+    status reports it (isd_get_status, and the return of the next pass once the prefill has
+    run); the other slots decode exactly as they do without that slot (greedy)."""
+    w = I.weights_numpy(SHAPE, seed=0, scale=20.0)
+    p = I.ragged_prompts([12, 15, 9], SHAPE.vocab, seed=41)
+    bad = int(p[1][4])
+    assert bad not in set(p[0].tolist()) | set(p[2].tolist())
+    w_bad = dict(w)
+    emb = w["embed"].copy()
+    emb[bad] = np.uint16(0x7FC0)                  # bf16 NaN
+    w_bad["embed"] = emb
+    eng = _engine(w_bad, 3)
+    ref = _engine(w, 3)
+    eng.prefill([0, 1, 2], p, [12, 12, 12])
+    ref.prefill([0, 2], [p[0], p[2]], [12, 12])
+    assert eng.status() == -6                       # synchronizes: the prefill has run
+    st = eng.slots_host()
+    assert st[1]["state"] == 3 and st[1]["status"] == -6 and st[0]["status"] == 0 and st[2]["status"] == 0
+    tok, nc, _ = eng.step()
+    assert eng.device_status == -6                  # returned by isd_step itself
+    torch.cuda.synchronize()
+    first = {b: [int(x) for x in tok[b, :int(nc[b])].cpu()] for b in (0, 2)}
+    assert int(nc[1]) == 0
+    out, _ = _run(eng, [0, 2])
+    out_ref, _ = _run(ref, [0, 2])
+    assert first[0] + out[0] == out_ref[0] and first[2] + out[2] == out_ref[2]
+    assert int(eng.free_stack().numel()) == eng.cfg.n_pages
+
+
+def test_prefill_page_order_matches_golden():
+    """The hand-worked multi-slot prefill example (tests/golden/prefill_pages_example.txt, page
+    size 4) at page size 16 with every prompt 4 times as long (the same page counts): the
+    GPU's page tables and free stack after each isd_prefill call equal the example's."""
+    from _golden import prefill_golden
+    shape = I.TINY
+    w = I.weights_numpy(shape)
+    eng = Engine(shape, w, stride=2, temperature=1.0, propose="sample", seed=1, max_batch=3, max_seq_len=64,
+                 n_pages=8, graphs=False)
+    for slots, lens, mx, tables, stack in prefill_golden():
+        prompts = I.ragged_prompts([4 * n for n in lens], shape.vocab, seed=sum(lens))
+        eng.prefill(slots, prompts, mx)
+        torch.cuda.synchronize()
+        pt = eng.page_table().cpu().numpy()
+        for s, t in tables.items():
+            assert pt[s, :len(t)].tolist() == t and np.all(pt[s, len(t):] == -1), (slots, s, pt[s])
+        assert eng.free_stack().cpu().numpy().tolist() == stack, slots

@@ -1,5 +1,5 @@
-"""isd_set_graphs: replaying a decode pass from a captured HIP graph gives exactly the eager
-results.  Two contexts with the same weights and prompts, one launching eagerly and one
+"""isd_set_graphs / isd_step_n: replaying decode passes from captured HIP graphs gives exactly
+the eager results.  Two contexts with the same weights and prompts, one launching eagerly and one
 replaying graphs, are stepped side by side (with eager torch work and synchronizations
 between the replays), and every pass's tokens, counts, logits, slot records and page tables
 are compared bit for bit; a prefill that recycles a slot between replays, profiling (which
@@ -15,11 +15,11 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def _engine(shape, w, prompts, max_new, N=4, T=1.0, propose="sample", lora=None):
+def _engine(shape, w, prompts, max_new, N=4, T=1.0, propose="sample", lora=None, graphs=False):
     from strided_decoding_amd import Engine
     max_seq = max(len(p) for p in prompts) + 64
     eng = Engine(shape, w, stride=N, temperature=T, propose=propose, seed=1, max_batch=len(prompts),
-                 max_seq_len=max_seq, lora=lora)
+                 max_seq_len=max_seq, lora=lora, graphs=graphs)
     eng.prefill(list(range(len(prompts))), prompts, max_new)
     return eng
 
@@ -49,8 +49,7 @@ def test_graph_replay_equals_eager(propose, T):
     max_new = [40, 25, 33, 40]
     print(f"graphs {propose} T={T}", flush=True)
     eager = _engine(shape, w, prompts, max_new, T=T, propose=propose)
-    graph = _engine(shape, w, prompts, max_new, T=T, propose=propose)
-    graph.set_graphs(True)
+    graph = _engine(shape, w, prompts, max_new, T=T, propose=propose, graphs=True)
     scratch = torch.randn(1 << 20, device=DEV)
     for step in range(14):
         a = _snap(eager, eager.step())
@@ -81,8 +80,7 @@ def test_graph_replay_equals_eager_with_adapter():
     prompts = I.ragged_prompts([19, 33, 8], shape.vocab, seed=15)
     max_new = [30, 30, 30]
     eager = _engine(shape, w, prompts, max_new, lora=lora)
-    graph = _engine(shape, w, prompts, max_new, lora=lora)
-    graph.set_graphs(True)
+    graph = _engine(shape, w, prompts, max_new, lora=lora, graphs=True)
     scratch = torch.randn(1 << 20, device=DEV)
     for step in range(8):
         a = _snap(eager, eager.step())
@@ -90,3 +88,29 @@ def test_graph_replay_equals_eager_with_adapter():
         _same(a, b, step)
         scratch.mul_(0.5).add_(1.0)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("n_passes", [2, 3, 8])
+def test_multi_pass_graph_equals_single_passes(n_passes):
+    """isd_step_n: n passes in one graph launch commit exactly what n eager isd_step calls
+    commit, pass by pass (odd counts leave the logits-buffer parity flipped for the next call)."""
+    shape = I.SMALL_BF16
+    w = I.weights_numpy(shape, seed=0, scale=20.0, sticky=(0.0, 20.0, 4.0, 7))
+    prompts = I.ragged_prompts([37, 5, 90, 16], shape.vocab, seed=12)
+    max_new = [60, 45, 53, 60]
+    print(f"multi-pass graph n={n_passes}", flush=True)
+    eager = _engine(shape, w, prompts, max_new)
+    multi = _engine(shape, w, prompts, max_new, graphs=True)
+    for call in range(3):
+        t, c, a = [x.clone() for x in multi.step_n(n_passes)]
+        torch.cuda.synchronize()
+        for i in range(n_passes):
+            et, ec, ea = eager.step()
+            torch.cuda.synchronize()
+            assert torch.equal(ec, c[i]) and torch.equal(ea, a[i]), (call, i)
+            for b in range(len(prompts)):
+                n = int(ec[b])
+                assert torch.equal(et[b, :n], t[i, b, :n]), (call, i, b)
+        assert torch.equal(eager.logits(), multi.logits()), call
+        assert eager.slots_host() == multi.slots_host(), call
+        assert torch.equal(eager.page_table(), multi.page_table()), call

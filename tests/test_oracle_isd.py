@@ -18,6 +18,7 @@ import numpy as np
 import pytest
 
 import isd_inputs as I
+from _golden import prefill_golden
 from oracle import isd, philox, sampler
 from oracle import model as M
 from oracle.paged_kv import PagePool
@@ -313,3 +314,16 @@ def test_meter_commits_the_models_own_proposals():
             break
         assert r.tokens[:N - 1] == pend and len(r.tokens) == N
     assert dec.slots[0].meter_n > 0 and 0.0 <= dec.slots[0].meter_sum <= dec.slots[0].meter_n
+
+
+def test_prefill_page_order_golden_example():
+    """Several slots per prefill call, recycled slots and slots finished at admission: the
+    decoder's page tables and free stack follow the hand-worked example."""
+    m = _model()
+    dec = isd.Decoder(m, 2, 1.0, seed=1, page_size=4, n_pages=8)
+    for slots, lens, mx, tables, stack in prefill_golden():
+        prompts = I.ragged_prompts(lens, m.spec.vocab, seed=sum(lens))
+        dec.prefill(slots, prompts, mx)
+        for s, t in tables.items():
+            assert dec.pool.table(s) == t, (slots, s)
+        assert dec.pool.stack == stack, slots

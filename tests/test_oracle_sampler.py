@@ -134,3 +134,36 @@ def test_temperature_scaling():
     p = S.probs_T(l, 0.5)
     e = np.exp(np.array([0.0, 2.0, 4.0]))
     np.testing.assert_allclose(p, e / e.sum(), rtol=1e-6)
+
+
+def test_top2_gap_hand_values():
+    """top2_gap: the largest logit minus the second largest; a repeated maximum gives 0."""
+    assert S.top2_gap([1.0, 5.0, 3.0]) == 2.0
+    assert S.top2_gap([5.0, 1.0, 5.0]) == 0.0
+    assert S.top2_gap([0.5, -1.0, 0.25, 0.5]) == 0.0
+    assert S.top2_gap([-np.inf, 2.0, -3.0]) == 5.0
+    assert S.top2_gap([7.0]) == np.inf
+
+
+def test_top2_gap_brute_force_and_margin_meaning():
+    """Against the definition written out (max over the others removed one at a time), and as
+    the greedy near-tie margin: no perturbation of every logit by less than half the gap moves
+    the argmax, and one of half the gap plus a little can."""
+    rng = np.random.default_rng(5)
+    for trial in range(200):
+        V = int(rng.integers(2, 40))
+        l = rng.standard_normal(V).astype(np.float32) * 3
+        if trial % 5 == 0:
+            l[rng.integers(V)] = l.max()           # a repeated maximum
+        j = int(np.argmax(l))
+        brute = float(l[j]) - max(float(l[i]) for i in range(V) if i != j)
+        gap = S.top2_gap(l)
+        assert gap == brute
+        if gap > 0:
+            e = rng.uniform(-1, 1, V) * (0.499 * gap)
+            assert S.argmax(l.astype(np.float64) + e) == j
+            k = max((i for i in range(V) if i != j), key=lambda i: l[i])
+            flip = l.astype(np.float64).copy()
+            flip[j] -= 0.5 * gap + 1e-6
+            flip[k] += 0.5 * gap + 1e-6
+            assert S.argmax(flip) == k
