@@ -369,6 +369,18 @@ typedef struct {
 size_t isd_sample_step_workspace_bytes(int32_t batch, int32_t rows, int32_t vocab, int32_t q_rows);
 isd_status isd_sample_step(const isd_sample_args* a, void* stream);
 
+/* isd_sample_step for callers that cannot allocate device memory or pass a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels and results, with the chunk statistics in a fixed scratch array of 8 MiB that the
+ * library holds on every GPU it runs on until the process ends.  a->workspace must be NULL.
+ * The call allocates nothing: no hipMalloc or hipFree, no allocating library routine.  Every
+ * call on one GPU shares that GPU's scratch, so calls that overlap on one GPU (different
+ * streams, or threads) race; calls in one stream are ordered.  Limit: isd_sample_step_workspace_
+ * bytes(batch, 2N-1, vocab, q_rows) <= 8 MiB (e.g. 64 slots x 7 rows and 448 previous rows at
+ * vocab 151936 need 0.8 MiB).  Errors: ISD_E_ARG (as isd_sample_step, or a non-NULL workspace),
+ * ISD_E_CAPACITY (beyond the scratch size), ISD_E_HIP. */
+isd_status isd_sample_step_noalloc(const isd_sample_args* a, void* stream);
+
 /* Introspective acceptance meter (wiki note, TL;DR and Key claims: the introspective
  * acceptance rate - whether a model accepts, under argmax or sampling, its own previously
  * generated tokens when it re-evaluates them; AR models ~0.98).  With the meter on, every

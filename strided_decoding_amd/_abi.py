@@ -28,7 +28,7 @@ EXPORTS = ("isd_init", "isd_prefill", "isd_step", "isd_step_active", "isd_step_n
            "isd_get_status", "isd_release", "attn_paged_decode_workspace_bytes", "attn_paged_decode",
            "isd_sample_step_workspace_bytes", "isd_sample_step", "isd_version", "isd_profile",
            "isd_profile_report", "isd_gemm", "isd_gemm_splits", "isd_set_graphs", "isd_packed_weight_bytes",
-           "isd_pack_weights", "isd_set_meter")
+           "isd_pack_weights", "isd_set_meter", "isd_sample_step_noalloc")
 
 ISD_GEMM_STORE, ISD_GEMM_STORE_F32, ISD_GEMM_RESID, ISD_GEMM_SWIGLU = 0, 1, 2, 3
 
@@ -137,6 +137,7 @@ def load(path=LIB_PATH):
     lib.isd_sample_step_workspace_bytes.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_int32]
     lib.isd_sample_step_workspace_bytes.restype = C.c_size_t
     lib.isd_sample_step.argtypes = [C.POINTER(SampleArgs), C.c_void_p]
+    lib.isd_sample_step_noalloc.argtypes = [C.POINTER(SampleArgs), C.c_void_p]
     lib.isd_version.restype = C.c_char_p
     lib.isd_gemm.argtypes = [C.POINTER(GemmArgs), C.c_void_p]
     lib.isd_gemm.restype = C.c_int
@@ -151,7 +152,8 @@ def load(path=LIB_PATH):
     lib.isd_profile_report.argtypes = [C.c_void_p, C.POINTER(ProfEntry), C.c_int32, C.POINTER(C.c_int32)]
     for f in ("isd_init", "isd_prefill", "isd_step", "isd_step_active", "isd_step_n", "isd_get_buffers",
               "isd_get_status", "isd_release", "attn_paged_decode", "isd_sample_step", "isd_profile",
-              "isd_profile_report", "isd_set_graphs", "isd_set_meter", "isd_pack_weights"):
+              "isd_profile_report", "isd_set_graphs", "isd_set_meter", "isd_pack_weights",
+              "isd_sample_step_noalloc"):
         getattr(lib, f).restype = C.c_int
     _lib = lib
     return lib

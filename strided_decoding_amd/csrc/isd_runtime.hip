@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <tuple>
 #include <new>
 #include <vector>
@@ -1086,19 +1087,23 @@ size_t isd_sample_step_workspace_bytes(int32_t batch, int32_t rows, int32_t voca
          align_up((size_t)std::max(1, q_rows) * nc * sizeof(ChunkStat));
 }
 
-isd_status isd_sample_step(const isd_sample_args* a, void* stream) {
-  if (!a || !a->slots || !a->logits || !a->tokens || !a->n_commit || !a->n_accept || !a->workspace)
-    return ISD_E_ARG;
+}  // extern "C"
+
+namespace {
+
+// The acceptance step of isd_sample_step with its chunk statistics in `ws` (at least
+// isd_sample_step_workspace_bytes of the arguments).
+isd_status sample_step(const isd_sample_args* a, void* ws, hipStream_t s) {
+  if (!a->slots || !a->logits || !a->tokens || !a->n_commit || !a->n_accept) return ISD_E_ARG;
   if (a->batch < 1 || a->stride_n < 1 || a->stride_n > ISD_MAX_STRIDE || a->vocab < 2 ||
       a->vocab > kStatChunk * 256 || !(a->temperature >= 0.f))
     return ISD_E_ARG;
   if (a->propose != ISD_PROPOSE_SAMPLE && a->propose != ISD_PROPOSE_ARGMAX) return ISD_E_ARG;
   if (a->propose == ISD_PROPOSE_SAMPLE && a->temperature > 0.f && (!a->q_logits || a->q_rows < 1)) return ISD_E_ARG;
   const int R = 2 * a->stride_n - 1, nc = cdiv(a->vocab, kStatChunk);
-  char* w = (char*)a->workspace;
+  char* w = (char*)ws;
   ChunkStat* st = (ChunkStat*)w;
   ChunkStat* qst = (ChunkStat*)(w + align_up((size_t)a->batch * R * nc * sizeof(ChunkStat)));
-  hipStream_t s = (hipStream_t)stream;
   HIP_OK(launch_row_stats(a->logits, a->batch * R, a->vocab, a->temperature, st, s));
   if (a->q_logits && a->q_rows > 0)
     HIP_OK(launch_row_stats(a->q_logits, a->q_rows, a->vocab, a->temperature, qst, s));
@@ -1125,6 +1130,61 @@ isd_status isd_sample_step(const isd_sample_args* a, void* stream) {
   sa.kinds = a->kinds;
   HIP_OK(launch_decide(sa, s));
   return ISD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+isd_status isd_sample_step(const isd_sample_args* a, void* stream) {
+  if (!a || !a->workspace) return ISD_E_ARG;
+  return sample_step(a, a->workspace, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------
+// isd_sample_step_noalloc: the acceptance step with its chunk statistics in a file-scope
+// device array instead of a caller workspace, for callers that cannot allocate.  Every GPU the
+// library runs on holds one copy until the process ends; its address on a device is looked up
+// once (hipGetSymbolAddress, with that device current) and kept.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;   // device -> its copy of `scratch`
+
+isd_status scratch_on_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ISD_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ISD_E_HIP;
+    it = g_scratch_ptr.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return ISD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+isd_status isd_sample_step_noalloc(const isd_sample_args* a, void* stream) {
+  if (!a || a->workspace) return ISD_E_ARG;
+  if (a->batch < 1 || a->stride_n < 1 || a->stride_n > ISD_MAX_STRIDE || a->vocab < 2) return ISD_E_ARG;
+  const size_t need = isd_sample_step_workspace_bytes(a->batch, 2 * a->stride_n - 1, a->vocab, a->q_rows);
+  if (need > kNoAllocScratchBytes) return ISD_E_CAPACITY;
+  void* ws = nullptr;
+  const isd_status st = scratch_on_current_device(&ws);
+  if (st != ISD_OK) return st;
+  // the kernels write every statistic they read (row_stats before decide), so nothing in the
+  // scratch has to start at zero
+  return sample_step(a, ws, (hipStream_t)stream);
 }
 
 }  // extern "C"
