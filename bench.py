@@ -71,7 +71,7 @@ def parse():
 def kernel_model(shape, M, N, ctx_rows, attn_keys):
     """Algorithmic bytes and flops of one launch of each kernel of a decode pass.
 
-    M rows (batch x (2N-1)); ctx_rows: sum over slots of keys in the pages this pass
+    M live rows (2N-1 per A-state slot, N per B-state slot); ctx_rows: sum over slots of keys in the pages this pass
     (L + q_len); attn_keys: sum over live query rows of visible keys.  Weights are read
     once per pass; activations are counted once in and once out.
     """
@@ -378,7 +378,7 @@ def kernel_profile(eng, shape, B, N, steps, n_active=None):
     """Per-op launch counts and durations (HIP events on the launch stream) over `steps` passes,
     with the algorithmic bytes / flops of the same passes."""
     R = 2 * N - 1
-    ctx_rows = attn_keys = 0
+    ctx_rows = attn_keys = live_rows = 0
     eng.profile(True)
     for _ in range(steps):
         for s in eng.slots_host():
@@ -386,11 +386,14 @@ def kernel_profile(eng, shape, B, N, steps, n_active=None):
             if q:
                 ctx_rows += s["L"] + q
                 attn_keys += sum(s["L"] + i + 1 for i in range(q))
+                live_rows += q
         eng.step(n_active)
     rep = eng.profile_report()
     eng.profile(False)
     P = max(1, steps)
-    model = kernel_model(shape, (n_active or B) * R, N, ctx_rows / P, attn_keys / P)
+    # a pass computes its live rows only (packed: 2N-1 per A-state slot, N per B-state slot)
+    kernel_profile.live_rows = live_rows / P
+    model = kernel_model(shape, live_rows / P, N, ctx_rows / P, attn_keys / P)
     kernels = {}
     for name, (n, tot_ms) in rep.items():
         e = {"launches_per_step": n / P, "avg_us": 1e3 * tot_ms / n, "ms_per_step": tot_ms / P}
@@ -431,7 +434,7 @@ def report(args, wl_name, shape, B, N, T, propose, prompt_len, gen, elapsed, st0
     committed = delta(st0, st1, "committed")
     ms = 1e3 * elapsed / args.steps
     ctx_rows = window_ctx_rows(st0, st1, N) or ctx_rows
-    sb = step_bytes(shape, B * (2 * N - 1), ctx_rows)
+    sb = step_bytes(shape, getattr(kernel_profile, "live_rows", B * (2 * N - 1)), ctx_rows)
     live0 = [s["L"] for s in st0 if s["state"] in (1, 2)] or [0]
     live1 = [s["L"] for s in st1 if s["state"] in (1, 2)] or [0]
     per_launch = 1 if args.no_graphs else args.passes_per_launch
@@ -456,6 +459,7 @@ def report(args, wl_name, shape, B, N, T, propose, prompt_len, gen, elapsed, st0
         "projected_tokens_per_s_at_p0.9": args.steps / elapsed * B * tpf_projection(0.9, N),
         "stride_efficiency_at_p0.9": tpf_projection(0.9, N) ** 2 / (2 * N - 1),
         "roofline": roof,
+        "live_rows_per_pass": getattr(kernel_profile, "live_rows", None),
         "kernels": kernels,
     }
 

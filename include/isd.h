@@ -148,16 +148,20 @@ typedef struct {
   int32_t max_pages_per_slot;
   int32_t* free_stack;      /* [n_pages], entries 0 .. n_free-1 */
   int32_t* n_free;          /* [1] */
-  float* logits;            /* logits of the last pass: [max_batch * (2N-1), vocab] fp32;
-                               row b*(2N-1)+i is row i of slot b's block */
+  float* logits;            /* logits of the last pass: [max_batch * (2N-1), vocab] fp32 in the
+                               pass's packed row order: row row_off[b] + i is row i of slot b's
+                               block, i < row_len[b] (the live rows of all slots come first, slot
+                               by slot; the rows after them are dead) */
   int32_t rows_per_slot;    /* 2N-1 */
-  int32_t* row_token;       /* [max_batch*(2N-1)] input token of each row of the last pass */
+  int32_t* row_token;       /* [max_batch*(2N-1)] input token of each packed row of the last pass */
   int32_t* row_pos;         /* [max_batch*(2N-1)] position (-1 for a dead row) */
   void* k_pool;             /* [n_layers][n_pages][Hkv][P][hd] act */
   void* v_pool;             /* [n_layers][n_pages][Hkv][hd][P] act (transposed within a page) */
   void* attn_out;           /* last layer's attention output of the last pass [rows, Hq*hd] act */
   float* prefill_logits;    /* logits of the last isd_prefill call, row i = the last prompt row
                                of its i-th slot [n, vocab] fp32; valid until the next pass */
+  int32_t* row_off;         /* [max_batch] first packed row of each slot's block in the last pass */
+  int32_t* row_len;         /* [max_batch] its live rows: 2N-1 (state A), N (state B) or 0 */
 } isd_buffers;
 
 /* Debug surface of one pass (isd_step's `debug`; NULL = off), for the parity harness: the
@@ -232,7 +236,10 @@ isd_status isd_prefill(isd_ctx* ctx, int32_t n, const int32_t* slots, const int3
  * the first rejection; Agentic Commons, "How Introspective Strided Decoding Works"): assemble
  * the block rows from device state, reserve KV pages, run the causal forward (LoRA on MASK
  * rows when lora_rank > 0), verify / accept / resample / propose, and roll the KV cache back
- * to the committed length.
+ * to the committed length.  The rows are packed on the device: A-state slots 2N-1 rows,
+ * B-state slots N, finished or empty slots none, slot after slot; the projections and the
+ * sampler's statistics skip the rows past the live ones (the pages' continuous batching:
+ * wiki note, TL;DR and Key claims).  A slot's results do not depend on the packing.
  *   tokens   device [max_batch, N] int32 out: tokens committed this pass (-1 padded)
  *   n_commit device [max_batch]    int32 out: number of tokens committed this pass
  *   n_accept device [max_batch]    int32 out: pending tokens accepted this pass

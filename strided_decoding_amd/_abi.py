@@ -85,7 +85,7 @@ class Buffers(C.Structure):
                 ("free_stack", C.c_void_p), ("n_free", C.c_void_p), ("logits", C.c_void_p),
                 ("rows_per_slot", C.c_int32), ("row_token", C.c_void_p), ("row_pos", C.c_void_p),
                 ("k_pool", C.c_void_p), ("v_pool", C.c_void_p), ("attn_out", C.c_void_p),
-                ("prefill_logits", C.c_void_p)]
+                ("prefill_logits", C.c_void_p), ("row_off", C.c_void_p), ("row_len", C.c_void_p)]
 
 
 class Debug(C.Structure):

@@ -190,6 +190,10 @@ struct GemmArgs {
   int lora_r;
   int lora_nseg;
   int lora_seg_end[3];
+  // Optional (tiled kernel, decode): the number of live rows, read on the device.  The live
+  // rows are the first *m_live of the M (the pass's packed rows); the row tiles shrink to
+  // them (the grid still covers M) and rows past them are neither computed nor stored.
+  const int32_t* m_live;
 };
 // TILED4 / TILED3 / TILED2: the tiled kernel with that many waves per workgroup (TILED and
 // AUTO choose it by the grid's fill of the CUs)
@@ -340,6 +344,11 @@ struct StepMeta {            // device buffers of the block / page machinery
   int32_t* zero_words;       // cleared once at init (arrival counters)
   int n_zero_words;
   int32_t* sticky_host;      // pinned host word: the first non-zero slot status (0 = none), or null
+  // decode: slot b's live rows are rows row_off[b] .. row_off[b] + row_len[b] - 1 of the pass
+  // (slots packed in order, B-state slots N rows, A-state 2N-1, others none); *m_live rows in all
+  int32_t* row_off;
+  int32_t* row_len;
+  int32_t* m_live;
 };
 hipError_t launch_init_state(const StepMeta& m, int n_pages, hipStream_t s);
 hipError_t launch_assemble(const StepMeta& m, hipStream_t s);
@@ -382,12 +391,18 @@ struct SampleArgs {
   int meter;                 // 1: commit pending tokens untested, accumulate their acceptance
   double* margins;           // optional [n_slots, 2N]: margin of each decision (-1 past the last)
   int32_t* kinds;            // optional [n_slots, 2N]: ISD_DEC_* of each decision (-1 past the last)
+  const int32_t* row_off;    // optional: first row of slot b (packed pass); null: b * rows_per_slot
 };
-hipError_t launch_row_stats(const float* logits, int rows, int V, float T, ChunkStat* stats, hipStream_t s);
-// Debug record: dst[r, 0:width] = src[rows[r], 0:width] for r < n, zeros when rows[r] is outside
-// [0, n_src) (ld and width in elements of elem_bytes; both multiples of 16 bytes).
+// rows past *m_live (when given) are skipped
+hipError_t launch_row_stats(const float* logits, int rows, int V, float T, ChunkStat* stats, hipStream_t s,
+                            const int32_t* m_live = nullptr);
+// Debug record: dst[r, 0:width] = src[row of rows[r], 0:width] for r < n, zeros when that row is
+// outside [0, n_src) (ld and width in elements of elem_bytes; both multiples of 16 bytes).
+// With row_off / row_len, rows[r] = b R + i names block row i of slot b, which is packed row
+// row_off[b] + i (none when i >= row_len[b]); without, rows[r] is the row itself.
 hipError_t launch_debug_gather(const void* src, size_t ld, const int32_t* rows, int n, int n_src, int width,
-                               int elem_bytes, void* dst, hipStream_t s);
+                               int elem_bytes, void* dst, hipStream_t s, const int32_t* row_off = nullptr,
+                               const int32_t* row_len = nullptr, int R = 1);
 hipError_t launch_decide(const SampleArgs& a, hipStream_t s);
 
 }  // namespace isd

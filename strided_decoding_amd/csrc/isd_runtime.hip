@@ -64,6 +64,7 @@ struct isd_ctx {
   int32_t *page_table = nullptr, *free_stack = nullptr, *n_free = nullptr;
   int32_t *row_tok = nullptr, *row_pos = nullptr, *row_slot = nullptr, *delta_row = nullptr;
   int32_t *mask_rows = nullptr, *ctx_len = nullptr, *last_rows = nullptr, *order = nullptr;
+  int32_t *row_off = nullptr, *row_len = nullptr, *m_live = nullptr;   // packed rows of a decode pass
   AttnItem* items = nullptr;
   float* X = nullptr;
   float* QKV = nullptr;   // the unsplit QKV projection in fp32 (q, k, v are rounded once, after RoPE)
@@ -172,6 +173,9 @@ size_t carve(isd_ctx& x, char* base) {
   x.delta_row = cv.take<int32_t>(x.max_rows);
   x.mask_rows = cv.take<int32_t>(std::max(1, x.n_mask));
   x.ctx_len = cv.take<int32_t>(B);
+  x.row_off = cv.take<int32_t>(B);
+  x.row_len = cv.take<int32_t>(B);
+  x.m_live = cv.take<int32_t>(64);
   x.last_rows = cv.take<int32_t>(B);
   x.order = cv.take<int32_t>(B);
   x.items = cv.take<AttnItem>(x.max_items);
@@ -270,6 +274,9 @@ StepMeta meta(isd_ctx& x) {
   m.zero_words = x.tile_cnt;
   m.n_zero_words = x.n_cnt;
   m.sticky_host = x.sticky_host;
+  m.row_off = x.row_off;
+  m.row_len = x.row_len;
+  m.m_live = x.m_live;
   return m;
 }
 
@@ -420,11 +427,14 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
   const isd_config& c = x.cfg;
   const int d = c.d_model, F = c.d_ffn, Hq = c.n_q_heads, Hkv = c.n_kv_heads, hd = c.head_dim;
   const int nd = dbg ? dbg->n_rows : 0;
-  // debug record of the followed rows: dst slice `idx` of `width` elements per row
+  // decode passes pack their live rows first; the projections skip the rest
+  const int32_t* live = decode ? x.m_live : nullptr;
+  // debug record of the followed rows (block row i of slot b, mapped to its packed row): dst
+  // slice `idx` of `width` elements per row
   auto record = [&](const void* src, int width, int esize, void* dst, int idx) -> hipError_t {
     if (!nd || !dst) return hipSuccess;
     return launch_debug_gather(src, width, dbg->rows, nd, M, width, esize,
-                               (char*)dst + (size_t)idx * nd * width * esize, s);
+                               (char*)dst + (size_t)idx * nd * width * esize, s, x.row_off, x.row_len, x.R);
   };
   if (x.bf) TIMED("embed", launch_embed<bf16>(x.row_tok, (const bf16*)x.embed, x.X, M, d, c.vocab, s));
   else TIMED("embed", launch_embed<float>(x.row_tok, (const float*)x.embed, x.X, M, d, c.vocab, s));
@@ -440,6 +450,7 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
     }
     // QKV projection; with split-K its partials are reduced by rope_append itself
     GemmArgs gq = plan_gemm(x, gargs(x.Xn, d, x.wqkv[l], d, M, x.qkvw, d, EPI_STORE_F32));
+    gq.m_live = live;
     gq.C = x.QKV;
     gq.ldc = x.qkvw;
     if (lora) {
@@ -515,6 +526,7 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
     {
       // O projection + residual, then the FFN input norm of the updated rows
       GemmArgs g = gargs(x.O, x.qd, x.wo[l], x.qd, M, d, x.qd, EPI_RESID);
+      g.m_live = live;
       g.R = x.X;
       g.ldr = d;
       g.norm_g = x.ffn_norm[l];
@@ -530,6 +542,7 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
     // FFN block
     {
       GemmArgs g = gargs(x.Xn, d, x.wg[l], d, M, F, d, EPI_SWIGLU);
+      g.m_live = live;
       g.B1 = x.wu[l];
       g.C = x.H;
       g.ldc = F;
@@ -543,6 +556,7 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
     {
       // down projection + residual, then the next layer's input norm (the final norm last)
       GemmArgs g = gargs(x.H, F, x.wd[l], F, M, d, F, EPI_RESID);
+      g.m_live = live;
       g.R = x.X;
       g.ldr = d;
       g.norm_g = l + 1 < c.n_layers ? x.attn_norm[l + 1] : x.final_norm;
@@ -559,6 +573,7 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
   HIP_OK(record(x.X, d, 4, dbg ? dbg->layer_in : nullptr, c.n_layers));
   HIP_OK(record(x.Xn, d, (int)x.act, dbg ? dbg->final_normed : nullptr, 0));
   GemmArgs g = gargs(x.Xn, d, x.lm_head, d, lm_M, c.vocab, d, EPI_STORE_F32);
+  g.m_live = live;
   g.a_rows = lm_rows;
   g.C = logits_out;
   g.ldc = c.vocab;
@@ -749,9 +764,10 @@ isd_status step_launches(isd_ctx* x, int nb, int32_t* tokens, int32_t* n_commit,
                           /*lora=*/c.lora_rank > 0 && c.stride_n > 1, x->logits[cur], dbg, s);
   if (st != ISD_OK) return st;
   const int prev = cur ^ 1;
-  TIMEDP("row_stats", launch_row_stats(x->logits[cur], M, c.vocab, c.temperature, x->stats[cur], s));
+  TIMEDP("row_stats", launch_row_stats(x->logits[cur], M, c.vocab, c.temperature, x->stats[cur], s, x->m_live));
   SampleArgs a = sargs(*x);
   a.n_slots = nb;
+  a.row_off = x->row_off;
   a.logits = x->logits[cur];
   a.rows_per_slot = x->R;
   a.stats = x->stats[cur];
@@ -896,6 +912,8 @@ isd_status isd_get_buffers(const isd_ctx* x, isd_buffers* out) {
   out->v_pool = x->v_pool;
   out->attn_out = x->O;
   out->prefill_logits = x->logits[x->cur];
+  out->row_off = x->row_off;
+  out->row_len = x->row_len;
   return ISD_OK;
 }
 

@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void assemble_kernel(StepMeta m) {
   if (tid == 0) s_nfree = *m.n_free;
   __syncthreads();
   const int N = m.N, R = 2 * N - 1, P = m.P;
-  int popped = 0;
+  int popped = 0, rows_base = 0;
   for (int g0 = 0; g0 < m.max_batch; g0 += 256) {
     const int b = g0 + tid;
     // slots at or past n_active sit this pass out; a live one there is an error of the caller
@@ -72,35 +72,38 @@ __global__ __launch_bounds__(256) void assemble_kernel(StepMeta m) {
       state = ISD_SLOT_DONE;
       q_len = 0;
     }
+    // packed rows: the slots' blocks back to back in slot order
+    int n_rows;
+    const int roff = rows_base + block_excl_scan(q_len, sh, &n_rows);
+    if (b < m.max_batch) {
+      m.row_off[b] = roff;
+      m.row_len[b] = q_len;
+    }
     if (valid) {
       int32_t* pt = m.page_table + (size_t)b * m.max_pages;
       for (int k = 0; k < grant; ++k) pt[have + k] = m.free_stack[s_nfree - 1 - (popped + off + k)];
       st->n_pages = have + grant;
-      // rows
-      for (int i = 0; i < R; ++i) {
-        const int r = b * R + i;
-        int tok = m.mask_id, pos = -1;
-        if (i < q_len) {
-          pos = L + i;
-          if (i == 0) tok = st->c;
-          else if (state == ISD_SLOT_A && i < N) tok = st->pending[i - 1];
-        }
+      for (int i = 0; i < q_len; ++i) {
+        const int r = roff + i;
+        int tok = m.mask_id;
+        if (i == 0) tok = st->c;
+        else if (state == ISD_SLOT_A && i < N) tok = st->pending[i - 1];
         m.row_tok[r] = tok;
-        m.row_pos[r] = pos;
+        m.row_pos[r] = L + i;
         m.row_slot[r] = b;
         m.delta_row[r] = -1;
       }
       for (int j = 0; j < N - 1; ++j) {
         int r = -1;
-        if (state == ISD_SLOT_A) r = b * R + N + j;
-        else if (state == ISD_SLOT_B) r = b * R + 1 + j;
+        if (state == ISD_SLOT_A) r = roff + N + j;
+        else if (state == ISD_SLOT_B) r = roff + 1 + j;
         m.mask_rows[b * (N - 1) + j] = r;
         if (r >= 0) m.delta_row[r] = b * (N - 1) + j;
       }
       for (int k = 0; k < m.items_per_slot; ++k) {
         AttnItem it;
         it.slot = b;
-        it.row0 = b * R + k * m.q_max;
+        it.row0 = roff + k * m.q_max;
         it.nq = max(0, min(m.q_max, q_len - k * m.q_max));
         it.pos0 = L + k * m.q_max;
         m.items[b * m.items_per_slot + k] = it;
@@ -108,9 +111,20 @@ __global__ __launch_bounds__(256) void assemble_kernel(StepMeta m) {
       m.ctx_len[b] = L + q_len;
     }
     popped += granted;
+    rows_base += n_rows;
+  }
+  // the rows past the live ones (up to the pass's n_active R) are dead: MASK token, no position
+  for (int r = rows_base + tid; r < m.n_active * R; r += 256) {
+    m.row_tok[r] = m.mask_id;
+    m.row_pos[r] = -1;
+    m.row_slot[r] = 0;
+    m.delta_row[r] = -1;
   }
   __syncthreads();
-  if (tid == 0) *m.n_free = s_nfree - popped;
+  if (tid == 0) {
+    *m.n_free = s_nfree - popped;
+    *m.m_live = rows_base;
+  }
 }
 
 // Free the pages beyond ceil(L/P) (all pages of a finished or empty slot), slots taken in
@@ -358,9 +372,16 @@ __global__ void rope_tables_kernel(float* cos_t, float* sin_t, int max_pos, int 
 // Debug record: row r of dst = row rows[r] of src (zeros for an index outside [0, n_src)),
 // copied in 16-byte units.
 __global__ __launch_bounds__(256) void debug_gather_kernel(const char* src, size_t ld_bytes, const int32_t* rows,
-                                                           int n_src, int width_bytes, char* dst) {
+                                                           int n_src, int width_bytes, char* dst,
+                                                           const int32_t* row_off, const int32_t* row_len, int R,
+                                                           int n_slots) {
   const int r = blockIdx.x;
-  const int row = rows[r];
+  int row = rows[r];
+  if (row_off) {                       // block row i of slot b -> its packed row
+    const bool in = row >= 0 && row < n_slots * R;
+    const int b = in ? row / R : 0, i = in ? row % R : 0;
+    row = (in && i < row_len[b]) ? row_off[b] + i : -1;
+  }
   const bool ok = row >= 0 && row < n_src;
   u32x4_t* d = (u32x4_t*)(dst + (size_t)r * width_bytes);
   for (int c = threadIdx.x; c < width_bytes / 16; c += 256)
@@ -427,11 +448,12 @@ hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_debug_gather(const void* src, size_t ld, const int32_t* rows, int n, int n_src, int width,
-                               int elem_bytes, void* dst, hipStream_t s) {
+                               int elem_bytes, void* dst, hipStream_t s, const int32_t* row_off,
+                               const int32_t* row_len, int R) {
   if (n <= 0) return hipSuccess;
   if ((width * elem_bytes) % 16 || (ld * elem_bytes) % 16) return hipErrorInvalidValue;
   hipLaunchKernelGGL(debug_gather_kernel, dim3(n), dim3(256), 0, s, (const char*)src, ld * elem_bytes, rows, n_src,
-                     width * elem_bytes, (char*)dst);
+                     width * elem_bytes, (char*)dst, row_off, row_len, R, n_src / max(1, R));
   return hipGetLastError();
 }
 

@@ -144,7 +144,18 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
   const int kt_per = (a.K / BK) / S;
   const int kbase = sp * kt_per * BK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = nt * TNO, m0 = mt * TM2;
+  // This workgroup's rows: row tile mt of TM2 rows, or, with a live-row count on the device
+  // (a packed decode pass), the live rows split evenly over the n_mt tiles in whole 32-row
+  // blocks.  Only the nblk blocks holding this tile's live rows are multiplied and stored.
+  int th = TM2, m_lim = a.M;
+  if (a.m_live) {
+    m_lim = min(__builtin_amdgcn_readfirstlane(*a.m_live), a.M);
+    th = min(TM2, ((m_lim + n_mt - 1) / n_mt + 31) / 32 * 32);
+  }
+  const int n0 = nt * TNO, m0 = mt * th;
+  if (m0 >= m_lim) return;
+  const int row_lim = min(m_lim, m0 + th);
+  const int nblk = min(7, (row_lim - m0 + 31) / 32);
   const uint16_t* zero = kZeroOperand + lane * 8;
   // stages kt_per .. kt_end-1: the fused LoRA expand (last split only); the stage count is
   // rounded up to whole ring rounds with zero stages (kZeroOperand)
@@ -173,7 +184,7 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
     }
 #pragma unroll
     for (int i = 0; i < kALoads; ++i) {
-      const bool valid = m0 + min(wave + WV * i, AG - 1) * 16 + lrow < a.M;
+      const bool valid = m0 + min(wave + WV * i, AG - 1) * 16 + lrow < row_lim;
       const int srow = valid ? max(sr[i], 0) : 0;   // unused rows: their outputs are never consumed
       const int l = valid ? lr[i] : -1;
       asrc[i] = (const uint16_t*)a.A + (size_t)srow * a.lda + aoff + kbase + chunk * 8;
@@ -253,7 +264,8 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
   wait_vmcnt<PER * (kBDepth - 1)>();                 // A stage 0 and B stage 0 have landed
   __builtin_amdgcn_s_barrier();
 #pragma unroll
-  for (int i = 0; i < 7; ++i) x0[i] = frag(0, 0, i);
+  for (int i = 0; i < 7; ++i)
+    if (i < nblk) x0[i] = frag(0, 0, i);
   wait_lgkm0();
   // One pipeline step per 32-k stage kt: make A stage kt+1 visible, then two halves of 14
   // MFMAs.  One wave per SIMD keeps the matrix unit fed by itself: the MFMAs are interleaved
@@ -277,9 +289,9 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
         const int nslot = (d + kBDepth) % kBRing;     // a constant once the loop is unrolled
 #pragma unroll
         for (int m = 0; m < 14; ++m) {
-          acc[m >> 1][m & 1] = mfma32x32x16(x0[m >> 1], bq[d][m & 1][0], acc[m >> 1][m & 1]);
+          if ((m >> 1) < nblk) acc[m >> 1][m & 1] = mfma32x32x16(x0[m >> 1], bq[d][m & 1][0], acc[m >> 1][m & 1]);
           __builtin_amdgcn_sched_barrier(0);
-          if (m < 7) x1[m] = frag(kt, 1, m);
+          if (m < nblk) x1[m] = frag(kt, 1, m);
           if (m >= 1 && m <= kALoads) {
             const int q = m - 1;
             const uint16_t* src = MODE == kPlainStages ? asrc[q] + ka * BK
@@ -303,9 +315,9 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
         const int kn = kt + 1;                            // past the end: a slot of zeros
 #pragma unroll
         for (int m = 0; m < 14; ++m) {
-          acc[m >> 1][m & 1] = mfma32x32x16(x1[m >> 1], bq[d][m & 1][1], acc[m >> 1][m & 1]);
+          if ((m >> 1) < nblk) acc[m >> 1][m & 1] = mfma32x32x16(x1[m >> 1], bq[d][m & 1][1], acc[m >> 1][m & 1]);
           __builtin_amdgcn_sched_barrier(0);
-          if (m < 7) x0[m] = frag(kn, 0, m);
+          if (m < nblk) x0[m] = frag(kn, 0, m);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -329,7 +341,8 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
   const int wcol = n0 + (DUAL ? 32 : 64) * wave;   // first output column of this wave
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int i0 = 4 * h, nb = h ? 3 : 4, r0 = m0 + 128 * h;
+    const int i0 = 4 * h, nb = h ? min(3, nblk - 4) : min(4, nblk), r0 = m0 + 128 * h;
+    if (nb <= 0) break;                            // no live block in this half (uniform)
     if (h) __syncthreads();                        // the first half has been written out
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -344,7 +357,7 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
     if (DUAL && !PARTIAL) {
       for (int q = lane; q < nb * 32 * 4; q += 64) {
         const int tr = q >> 2, c8 = (q & 3) * 8, row = r0 + tr, col = wcol + c8;
-        if (row >= a.M || col >= a.N) continue;
+        if (row >= row_lim || col >= a.N) continue;
         float g[8], u[8];
         *(f32x4_t*)&g[0] = *(const f32x4_t*)&tile[tr * LD + c8];
         *(f32x4_t*)&g[4] = *(const f32x4_t*)&tile[tr * LD + c8 + 4];
@@ -374,7 +387,7 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
     } else if (!PARTIAL && EPI == EPI_STORE) {
       for (int q = lane; q < nb * 32 * 8; q += 64) {
         const int tr = q >> 3, c8 = (q & 7) * 8, row = r0 + tr, col = wcol + c8;
-        if (row >= a.M || col >= a.N) continue;
+        if (row >= row_lim || col >= a.N) continue;
         float v[8];
         *(f32x4_t*)&v[0] = *(const f32x4_t*)&tile[tr * LD + c8];
         *(f32x4_t*)&v[4] = *(const f32x4_t*)&tile[tr * LD + c8 + 4];
@@ -400,7 +413,7 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
         const int tr = q >> 4, c4 = (q & 15) * 4, row = r0 + tr;
         // SwiGLU partials: columns 0-31 of the tile are gate sums, 32-63 up sums
         const int col = DUAL ? wcol + (c4 & 31) : wcol + c4;
-        if (row >= a.M || col >= a.N) continue;
+        if (row >= row_lim || col >= a.N) continue;
         f32x4_t v = *(const f32x4_t*)&tile[tr * LD + c4];
         if (PARTIAL) {
           float* dst = DUAL ? part + ((size_t)sp * a.M + row) * (2 * (size_t)a.N) + (c4 >> 5) * a.N + col
@@ -647,7 +660,8 @@ template <int EPI>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a, int S, const float* part) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU);
   const size_t ld = DUAL ? 2 * (size_t)a.N : (size_t)a.N;
-  const size_t n4 = (size_t)a.M * a.N / 4;
+  const int m_lim = a.m_live ? min(*a.m_live, a.M) : a.M;       // live rows of a packed pass
+  const size_t n4 = (size_t)m_lim * a.N / 4;
   for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n4; e += (size_t)gridDim.x * blockDim.x) {
     const int row = (int)(e * 4 / a.N), col = (int)(e * 4 % a.N);
     f32x4_t v = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
@@ -672,6 +686,7 @@ constexpr int kMaxSplits = 16;
 __global__ __launch_bounds__(kNormThreads) void splitk_resid_norm_kernel(GemmArgs a, int S, const float* part) {
   __shared__ float sh[kNormThreads / 64];
   const int row = blockIdx.x, tid = threadIdx.x;
+  if (a.m_live && row >= *a.m_live) return;        // a dead row of a packed pass
   const int dr = a.delta_row ? a.delta_row[row] : -1;
   float* R = a.R + (size_t)row * a.ldr;
   const size_t split_stride = (size_t)a.M * a.N;

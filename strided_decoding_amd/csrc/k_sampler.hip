@@ -27,12 +27,13 @@ constexpr int NT = 256;
 constexpr int PER = kStatChunk / NT;   // logits per thread in a chunk
 
 __global__ __launch_bounds__(NT) void row_stats_kernel(const float* logits, int V, float T, ChunkStat* stats,
-                                                       int n_chunks) {
+                                                       int n_chunks, const int32_t* m_live) {
   __shared__ float shm[4], shm2[4];
   __shared__ int sha[4];
   __shared__ double shs[4];
   __shared__ int shbad[4];
   const int row = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  if (m_live && row >= *m_live) return;              // a dead row of a packed pass
   const int c0 = c * kStatChunk, c1 = min(V, c0 + kStatChunk);
   const float* l = logits + (size_t)row * V;
   float v[PER];
@@ -446,7 +447,7 @@ __global__ __launch_bounds__(NT) void decide_kernel(SampleArgs a) {
     }
     return;
   }
-  const int R = a.rows_per_slot, base_row = b * R;
+  const int R = a.rows_per_slot, base_row = a.row_off ? a.row_off[b] : b * R;
   const int L = st->L, t = st->t;
   int ncommit = 0, nacc = 0, nver = 0;
   // debug record: kind and margin of each decision in order (an argmax decision's margin is
@@ -628,10 +629,11 @@ __global__ __launch_bounds__(NT) void decide_kernel(SampleArgs a) {
 
 }  // namespace
 
-hipError_t launch_row_stats(const float* logits, int rows, int V, float T, ChunkStat* stats, hipStream_t s) {
+hipError_t launch_row_stats(const float* logits, int rows, int V, float T, ChunkStat* stats, hipStream_t s,
+                            const int32_t* m_live) {
   if (rows <= 0) return hipSuccess;
   const int nc = (V + kStatChunk - 1) / kStatChunk;
-  hipLaunchKernelGGL(row_stats_kernel, dim3(rows, nc), dim3(NT), 0, s, logits, V, T, stats, nc);
+  hipLaunchKernelGGL(row_stats_kernel, dim3(rows, nc), dim3(NT), 0, s, logits, V, T, stats, nc, m_live);
   return hipGetLastError();
 }
 

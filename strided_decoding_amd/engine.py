@@ -273,13 +273,33 @@ class Engine:
         n = int(self._view(self._buf.n_free, 4, torch.int32, (1,)).item())
         return self._view(self._buf.free_stack, self.cfg.n_pages * 4, torch.int32, (self.cfg.n_pages,))[:n]
 
+    def _slot_rows(self):
+        """Packed row of each slot's block row [max_batch, 2N-1] of the last pass (host int64;
+        rows past a slot's live rows repeat its first row), synchronizes."""
+        torch.cuda.synchronize(self.device)
+        n = self.max_batch * self.R
+        off = self._view(self._buf.row_off, self.max_batch * 4, torch.int32, (self.max_batch,)).cpu().numpy()
+        ln = self._view(self._buf.row_len, self.max_batch * 4, torch.int32, (self.max_batch,)).cpu().numpy()
+        i = np.arange(self.R)[None, :]
+        idx = np.where(i < ln[:, None], off[:, None] + i, off[:, None])
+        return np.clip(idx, 0, n - 1).astype(np.int64)
+
+    def row_offsets(self):
+        """First packed row of each slot's block in the last pass [max_batch] (host int array):
+        a slot's q_row entries name packed rows of the pass that proposed them."""
+        torch.cuda.synchronize(self.device)
+        return self._view(self._buf.row_off, self.max_batch * 4, torch.int32, (self.max_batch,)).cpu().numpy()
+
     def logits(self):
-        """Logits of the last decode pass [max_batch, 2N-1, V] (float32)."""
+        """Logits of the last decode pass per slot block row [max_batch, 2N-1, V] (float32; a
+        copy gathered from the packed rows; rows past a slot's live rows are not meaningful)."""
         b = A.Buffers()          # the logits buffer alternates between passes: query it now
         A.check("isd_get_buffers", self.lib.isd_get_buffers(self.ctx, C.byref(b)))
         V = self.shape.vocab
-        rows = self.max_batch * self.R
-        return self._view(b.logits, rows * V * 4, torch.float32, (self.max_batch, self.R, V))
+        n = self.max_batch * self.R
+        flat = self._view(b.logits, n * V * 4, torch.float32, (n, V))
+        idx = torch.from_numpy(self._slot_rows().reshape(-1)).to(self.device)
+        return flat.index_select(0, idx).view(self.max_batch, self.R, V)
 
     def prefill_logits(self, n):
         """Logits of the last prompt row of each slot of the last isd_prefill call [n, V]
@@ -290,10 +310,15 @@ class Engine:
         return self._view(b.prefill_logits, n * V * 4, torch.float32, (n, V))
 
     def rows(self):
+        """(token, position) of each slot's block rows in the last pass [max_batch, 2N-1]
+        (gathered from the packed rows; -1 positions past a slot's live rows)."""
         n = self.max_batch * self.R
-        tok = self._view(self._buf.row_token, n * 4, torch.int32, (self.max_batch, self.R))
-        pos = self._view(self._buf.row_pos, n * 4, torch.int32, (self.max_batch, self.R))
-        return tok, pos
+        idx = self._slot_rows()
+        ln = self._view(self._buf.row_len, self.max_batch * 4, torch.int32, (self.max_batch,)).cpu().numpy()
+        tok = self._view(self._buf.row_token, n * 4, torch.int32, (n,)).cpu().numpy()[idx]
+        pos = self._view(self._buf.row_pos, n * 4, torch.int32, (n,)).cpu().numpy()[idx]
+        pos = np.where(np.arange(self.R)[None, :] < ln[:, None], pos, -1)
+        return torch.from_numpy(tok), torch.from_numpy(pos)
 
     def kv_pools(self):
         """(K, V) pools: K [L, n_pages, Hkv, P, hd], V [L, n_pages, Hkv, hd, P] (act dtype)."""

@@ -45,8 +45,10 @@ def _rel(a, r):
     return float((np.abs(a - r).max(axis=-1) / np.maximum(np.abs(r).max(axis=-1), 1e-6)).max())
 
 
-def _adopt(dec, model, b, g, committed, rec_logits, R, N, T, propose):
-    """Make the oracle slot equal the GPU's state (cache rebuilt when L differs)."""
+def _adopt(dec, model, b, g, committed, rec_logits, row0, N, T, propose):
+    """Make the oracle slot equal the GPU's state (cache rebuilt when L differs).  rec_logits:
+    the slot's block rows of the pass that proposed its pending tokens, whose first row is the
+    pass's packed row row0 (the GPU's q_row entries are packed rows)."""
     st = dec.slots[b]
     st.committed = list(committed)
     st.n_gen = len(committed) - st.prompt_len
@@ -59,7 +61,7 @@ def _adopt(dec, model, b, g, committed, rec_logits, R, N, T, propose):
             st.pending.append(g[f"pending{j}"])
             qr = g[f"q_row{j}"]
             if qr >= 0 and T > 0 and propose == "sample":
-                st.pending_q.append(sampler.weights_T(rec_logits[qr - b * R], T)[:2])
+                st.pending_q.append(sampler.weights_T(rec_logits[qr - row0], T)[:2])
             else:
                 st.pending_q.append(None)
     if g["L"] != st.L:
@@ -119,6 +121,7 @@ def teacher_forced(shape, w, N, T, propose, prompts, max_new, steps, lora=None, 
         torch.cuda.synchronize()
         g_tok, g_nc, g_na = tok.cpu().numpy(), nc.cpu().numpy(), na.cpu().numpy()
         g_logits = eng.logits().cpu().numpy()
+        g_off = eng.row_offsets()
         gs = eng.slots_host()
         for b in slots:
             if b not in recs:
@@ -160,7 +163,7 @@ def teacher_forced(shape, w, N, T, propose, prompts, max_new, steps, lora=None, 
         for b in slots:
             if b in recs:
                 q_src = g_logits[b] if on_gpu_logits else recs[b].logits
-                _adopt(dec, model, b, gs[b], committed[b], q_src, R, N, T, propose)
+                _adopt(dec, model, b, gs[b], committed[b], q_src, int(g_off[b]), N, T, propose)
     print(f"steps={n_steps} near_ties={near} max_logit_err={max_err:.3g}", flush=True)
     return eng, dec, committed, near
 
