@@ -65,6 +65,9 @@ def parse():
                    help="only summarise a rocprofv3 --kernel-trace csv output directory (no GPU) and exit")
     p.add_argument("--pmc-summary", default=None, metavar="DIR",
                    help="only summarise rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (no GPU) and exit")
+    p.add_argument("--counter-summary", default=None, metavar="DIR",
+                   help="only print the mean of every counter per decode op of a rocprofv3 --pmc run (no GPU) "
+                        "and exit")
     return p.parse_args()
 
 
@@ -113,10 +116,21 @@ def step_bytes(shape, M, ctx_rows):
 
 # Kernel (demangled-name pattern) behind each profiled operation whose traffic can be read from
 # rocprofv3 counters: the decode launches are the most frequent grid of that kernel in a run.
+# o and down run the same kernel with the same grid, in turn (o of a layer, then its down):
+# (period, index) selects every period-th of those dispatches in dispatch order.
 OP_KERNELS = {
     "gemm_gate_up": (r"gemm_bf16_big_kernel<3, false, false, 3>", ("k_gemm.hip",)),
-    "lm_head": (r"gemm_bf16_big_kernel<1, false, false, 4>", ("k_gemm.hip",)),
+    "gemm_qkv": (r"gemm_bf16_big_kernel<1, true, false, 3>", ("k_gemm.hip",)),
+    "gemm_o": (r"gemm_bf16_big_kernel<2, true, false, 4>", ("k_gemm.hip",), (2, 0)),
+    "gemm_down": (r"gemm_bf16_big_kernel<2, true, false, 4>", ("k_gemm.hip",), (2, 1)),
+    "splitk_resid_norm": (r"splitk_resid_norm_kernel", ("k_gemm.hip",)),
+    "rope_append": (r"rope_append_kernel<", ("k_block.hip",)),
+    # the LM head's kernel instance is also the prefill's (fp32) QKV projection: at this
+    # workload the decode LM head is the grid of 2 row tiles x 600 (8-aligned) column tiles of
+    # four-wave workgroups
+    "lm_head": (r"gemm_bf16_big_kernel<1, false, false, 4>", ("k_gemm.hip",), None, 2 * 600 * 256),
     "attention": (r"attn_bf16_kernel<", ("k_attn.hip",)),
+    "attn_combine": (r"attn_combine_kernel", ("k_attn.hip",)),
     "row_stats": (r"row_stats_kernel", ("k_sampler.hip",)),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qwen3_8b_b64.md")
@@ -182,19 +196,49 @@ def trace_summary(root):
     for (name, grid), e in sorted(acc.items(), key=lambda kv: -kv[1][1])[:30]:
         print(f"| `{_short(name)}` | {grid} | {e[0]} | {e[1] / e[0] / 1e3:.1f} | {e[2] / 1e3:.1f} | "
               f"{e[3] / 1e3:.1f} | {100 * e[1] / tot:.1f} |")
+    # decode ops: the most frequent grid of each op's kernel (o and down split by dispatch order)
+    import re
+    print("\n| op | kernel | grid (threads) | dispatches | avg us |")
+    print("|---|---|---|---|---|")
+    for op, (pat, _files, *sel) in OP_KERNELS.items():
+        nth = sel[0] if sel else None
+        per = {}
+        for r in rows:
+            if re.search(pat, _col(r, "Kernel_Name")):
+                ns = int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))
+                per.setdefault(_grid(r), []).append((int(_col(r, "Start_Timestamp")), ns))
+        grid = sel[1] if len(sel) > 1 else (max(per, key=lambda g: len(per[g])) if per else None)
+        if grid not in per:
+            continue
+        v = [ns for _, ns in sorted(per[grid])]
+        if nth:
+            v = v[nth[1]::nth[0]]
+        print(f"| {op} | `{_short(pat)}` | {grid} | {len(v)} | {sum(v) / len(v) / 1e3:.1f} |")
 
 
-def _counter_by_grid(root, counter, pattern):
+def _counter_by_grid(root, counter, pattern, nth=None, grid=None):
+    """(grid, dispatches, mean value) of a counter over the most frequent grid (or the given
+    one) of the kernels matching pattern; nth = (period, index) keeps every period-th dispatch
+    in dispatch order."""
     import re
     per = {}
     for r in _csv_rows(root, "counter_collection.csv"):
         if _col(r, "Counter_Name") != counter or not re.search(pattern, _col(r, "Kernel_Name")):
             continue
-        per.setdefault(_grid(r), []).append(float(_col(r, "Counter_Value")))
+        try:
+            order = int(_col(r, "Dispatch_Id"))
+        except KeyError:
+            order = len(per.get(_grid(r), []))
+        per.setdefault(_grid(r), []).append((order, float(_col(r, "Counter_Value"))))
     if not per:
         raise SystemExit(f"no {counter} records for /{pattern}/ under {root}")
-    grid = max(per, key=lambda g: len(per[g]))
-    v = per[grid]
+    if grid is None:
+        grid = max(per, key=lambda g: len(per[g]))
+    elif grid not in per:
+        raise SystemExit(f"no {counter} records of grid {grid} for /{pattern}/ under {root}")
+    v = [x for _, x in sorted(per[grid])]
+    if nth:
+        v = v[nth[1]::nth[0]]
     return grid, len(v), sum(v) / len(v)
 
 
@@ -220,10 +264,12 @@ def pmc_summary(root):
     print("| op | kernel | grid | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | traffic bytes (calibrated) |")
     print("|---|---|---|---|---|---|---|")
     rec = {}
-    for op, (pat, files) in OP_KERNELS.items():
+    for op, (pat, files, *sel) in OP_KERNELS.items():
+        nth = sel[0] if sel else None
+        grid = sel[1] if len(sel) > 1 else None
         try:
-            g, n, f = _counter_by_grid(os.path.join(root, "fetch_bench"), "FETCH_SIZE", pat)
-            g2, _, w = _counter_by_grid(os.path.join(root, "write_bench"), "WRITE_SIZE", pat)
+            g, n, f = _counter_by_grid(os.path.join(root, "fetch_bench"), "FETCH_SIZE", pat, nth, grid)
+            g2, _, w = _counter_by_grid(os.path.join(root, "write_bench"), "WRITE_SIZE", pat, nth, grid)
         except SystemExit:
             continue
         t = f * 1024 * kf + w * 1024 * kw
@@ -231,6 +277,25 @@ def pmc_summary(root):
                    "source_sha": kernel_source_sha(files)}
         print(f"| {op} | `{pat}` | {g}/{g2} | {n} | {f:.0f} | {w:.0f} | {t:.4g} |")
     print("\n```json\n" + json.dumps({"calibration": {"fetch": kf, "write": kw}, "ops": rec}, indent=1) + "\n```")
+
+
+def counter_summary(root):
+    """Mean value per dispatch of every counter of a rocprofv3 --pmc run, for each decode op of
+    OP_KERNELS (its decode grid, o and down told apart by dispatch order)."""
+    names = sorted({_col(r, "Counter_Name") for r in _csv_rows(root, "counter_collection.csv")})
+    print("| op | grid | dispatches | " + " | ".join(names) + " |")
+    print("|---|---|---|" + "---|" * len(names))
+    for op, (pat, _files, *sel) in OP_KERNELS.items():
+        nth = sel[0] if sel else None
+        grid = sel[1] if len(sel) > 1 else None
+        vals = []
+        try:
+            for c in names:
+                g, n, v = _counter_by_grid(root, c, pat, nth, grid)
+                vals.append(v)
+        except SystemExit:
+            continue
+        print(f"| {op} | {g} | {n} | " + " | ".join(f"{v:.4g}" for v in vals) + " |")
 
 
 def load_traffic(op):
@@ -731,6 +796,8 @@ def main():
         return trace_summary(args.trace_summary)
     if args.pmc_summary:
         return pmc_summary(args.pmc_summary)
+    if args.counter_summary:
+        return counter_summary(args.counter_summary)
     if args.copy_probe_mib:
         return copy_probe(args.copy_probe_mib)
     if args.gpus != 1:
