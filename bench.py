@@ -119,16 +119,17 @@ def step_bytes(shape, M, ctx_rows):
 # o and down run the same kernel with the same grid, in turn (o of a layer, then its down):
 # (period, index) selects every period-th of those dispatches in dispatch order.
 OP_KERNELS = {
-    "gemm_gate_up": (r"gemm_bf16_big_kernel<3, false, false, 3>", ("k_gemm.hip",)),
-    "gemm_qkv": (r"gemm_bf16_big_kernel<1, true, false, 3>", ("k_gemm.hip",)),
-    "gemm_o": (r"gemm_bf16_big_kernel<2, true, false, 4>", ("k_gemm.hip",), (2, 0)),
-    "gemm_down": (r"gemm_bf16_big_kernel<2, true, false, 4>", ("k_gemm.hip",), (2, 1)),
+    "gemm_gate_up": (r"gemm_bf16_big_kernel<3, false, false, 3>", ("gemm_tile.h", "k_gemm_big_swiglu.hip")),
+    "gemm_qkv": (r"gemm_bf16_big_kernel<1, true, false, 3>", ("gemm_tile.h", "k_gemm_big_store_f32.hip")),
+    "gemm_o": (r"gemm_bf16_big_kernel<2, true, false, 4>", ("gemm_tile.h", "k_gemm_big_resid.hip"), (2, 0)),
+    "gemm_down": (r"gemm_bf16_big_kernel<2, true, false, 4>", ("gemm_tile.h", "k_gemm_big_resid.hip"), (2, 1)),
     "splitk_resid_norm": (r"splitk_resid_norm_kernel", ("k_gemm.hip",)),
     "rope_append": (r"rope_append_kernel<", ("k_block.hip",)),
     # the LM head's kernel instance is also the prefill's (fp32) QKV projection: at this
     # workload the decode LM head is the grid of 2 row tiles x 600 (8-aligned) column tiles of
     # four-wave workgroups
-    "lm_head": (r"gemm_bf16_big_kernel<1, false, false, 4>", ("k_gemm.hip",), None, 2 * 600 * 256),
+    "lm_head": (r"gemm_bf16_big_kernel<1, false, false, 4>", ("gemm_tile.h", "k_gemm_big_store_f32.hip"), None,
+                2 * 600 * 256),
     "attention": (r"attn_bf16_kernel<", ("k_attn.hip",)),
     "attn_combine": (r"attn_combine_kernel", ("k_attn.hip",)),
     "row_stats": (r"row_stats_kernel", ("k_sampler.hip",)),
