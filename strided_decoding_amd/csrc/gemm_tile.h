@@ -60,6 +60,13 @@ __device__ __attribute__((aligned(1024))) uint16_t kZeroOperand[512] = {};
 constexpr int kPlainStages = 0, kZeroTail = 1, kLoraTail = 2;
 template <int M> using StageMode = std::integral_constant<int, M>;
 
+// SwiGLU of one output: silu(g) u = g u / (1 + e^-g), with e^-g = 2^(-g log2 e) and the
+// reciprocal taken by the hardware's exp2 and reciprocal instructions (about 1 ulp each: the
+// result is rounded to bf16 where it is stored, and every kernel uses this one formula).
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g)) * u;
+}
+
 template <typename T, int EPI>
 __device__ __forceinline__ void epilogue_store_t(const GemmArgs& a, int row, int col, float v, float v_up) {
   if (row >= a.M || col >= a.N) return;
@@ -77,8 +84,7 @@ __device__ __forceinline__ void epilogue_store_t(const GemmArgs& a, int row, int
   } else if (EPI == EPI_RESID) {
     a.R[(size_t)row * a.ldr + col] += v;
   } else {
-    const float s = v / (1.0f + expf(-v));
-    ((T*)a.C)[(size_t)row * a.ldc + col] = from_f<T>(s * v_up);
+    ((T*)a.C)[(size_t)row * a.ldc + col] = from_f<T>(silu_mul(v, v_up));
   }
 }
 
@@ -290,11 +296,47 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* smem, int u
   // 68 floats) in two halves (row blocks 0-3, then 4-6), then written out in 16-byte chunks.
   // Accumulator register r of block (i, j) in lane l is tile row 32 i + 8 (r/4) + 4 (l/32) + r%4,
   // column 32 j + l%32.  For SwiGLU columns 0-31 are the gate and 32-63 the up product.
-  __syncthreads();                                 // every wave is done with the ring
-  constexpr int LD = 68;
-  float* tile = (float*)smem + (size_t)wave * (128 * LD);
   const int cl = lane & 31;
   const int wcol = n0 + (DUAL ? 32 : 64) * wave;   // first output column of this wave
+  __syncthreads();                                 // every wave is done with the ring
+  if (DUAL && !PARTIAL && !a.delta_row) {
+    // SwiGLU without a delta: the gate and up sums of an output share a lane and a register
+    // index, so the outputs are formed in registers.  Adjacent lanes trade one value so that each
+    // holds two adjacent columns of one row (rows r and r + 1 of a register pair: the even lane
+    // keeps row r, the odd lane row r + 1), the bf16 pairs are staged row-major in this wave's
+    // LDS rows (40 bf16 per row: 16-byte aligned), and each row's 64 bytes leave in 16-byte stores.
+    constexpr int LDW = 20;                        // 32-bit words per staged row
+    uint32_t* st = (uint32_t*)smem + wave * (TM2 * LDW);
+    const bool odd = cl & 1;
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float x0 = silu_mul(acc[i][0][r], acc[i][1][r]);          // row t, column cl
+        const float x1 = silu_mul(acc[i][0][r + 1], acc[i][1][r + 1]);  // row t + 1, column cl
+        const float give = odd ? x0 : x1;
+        const float got = __builtin_bit_cast(
+            float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, give), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+        const uint32_t w = odd ? pack_bf16x2(got, x1) : pack_bf16x2(x0, got);
+        const int t = 32 * i + 8 * (r >> 2) + 4 * khi + (r & 3) + (odd ? 1 : 0);
+        st[t * LDW + (cl >> 1)] = w;
+      }
+    // (one wave's LDS accesses are processed in order: its reads see its writes)
+    for (int q = lane; q < NB * 32 * 4; q += 64) {
+      const int t = q >> 2, c8 = (q & 3) * 8, row = m0 + t, col = wcol + c8;
+      if (row >= row_lim || col >= a.N) continue;
+      const u32x4_t v = *(const u32x4_t*)(st + t * LDW + c8 / 2);
+      uint16_t* dst = (uint16_t*)a.C + (size_t)row * a.ldc + col;
+      if (col + 8 <= a.N) {
+        *(u32x4_t*)dst = v;
+      } else {
+        for (int j = 0; j < 8 && col + j < a.N; ++j) dst[j] = (uint16_t)(v[j >> 1] >> (16 * (j & 1)));
+      }
+    }
+    return;
+  }
+  constexpr int LD = 68;
+  float* tile = (float*)smem + (size_t)wave * (128 * LD);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int i0 = 4 * h, nb = h ? min(3, NB - 4) : min(4, NB), r0 = m0 + 128 * h;
@@ -331,7 +373,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* smem, int u
             w0 += dl[a.delta_off2];
             w1 += dl[a.delta_off2 + 1];
           }
-          pk[j >> 1] = pack_bf16x2(v0 / (1.0f + expf(-v0)) * w0, v1 / (1.0f + expf(-v1)) * w1);
+          pk[j >> 1] = pack_bf16x2(silu_mul(v0, w0), silu_mul(v1, w1));
         }
         uint16_t* dst = (uint16_t*)a.C + (size_t)row * a.ldc + col;
         if (col + 8 <= a.N) {
