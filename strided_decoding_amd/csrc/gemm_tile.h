@@ -6,7 +6,7 @@
 // Tiled kernel (more than 128 rows): one 224 x 64 WV output tile per workgroup of WV = 4, 3
 // or 2 waves, one wave per SIMD, each 224 x 64 = 7 x 2 MFMA tiles (224 accumulators in AGPRs).  224 = 448 / 2
 // makes the decode row count (64 slots x 7 rows) exactly two row tiles.  The activation tile
-// is streamed in 32-wide k stages through a 10-deep LDS ring filled by direct global->LDS
+// is streamed in 32-wide k stages through an 8-deep LDS ring filled by direct global->LDS
 // loads and shared by the waves; each wave loads its own weight operands straight into a
 // 4-stage register ring.  Each 64-byte LDS row keeps its four 16-byte k-chunks XOR-swizzled by
 // (row/4)%4 so that the 16 rows an MFMA operand read touches fall in distinct banks.
@@ -31,7 +31,7 @@ constexpr int BK = 32;            // k per pipeline stage (one MFMA k-step)
 constexpr int TM2 = 224, TN2 = 256;
 constexpr int GROUP_BYTES = 16 * BK * 2;                 // 16 rows x 64 B
 constexpr int AG = TM2 / 16;              // A row groups of 16 rows per tile
-constexpr int kNsA = 10;                  // A ring depth (10 x 14 KB)
+constexpr int kNsA = 8;                   // A ring depth (8 x 14 KB; 6, 7, 9 and 10 measured slower)
 constexpr int kAStage = AG * GROUP_BYTES;
 constexpr int kBRing = 4;                 // B operands: a register ring of this many stages,
 constexpr int kBDepth = kBRing - 1;       // loaded this many stages ahead
