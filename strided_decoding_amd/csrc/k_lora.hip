@@ -95,6 +95,20 @@ __global__ __launch_bounds__(64 * kShrinkWaves) void lora_shrink_kernel(ShrinkAr
     // point where every XCD sees them, and are read back the same way: no cache-wide
     // write-back or invalidation (a device-scope fence costs several microseconds here).
     // Each thread waits for its own stores before the barrier that precedes the arrival.
+    // Why the last workgroup sees every partial (an argument about the ISA's ordering, not the
+    // source-level memory model, in which relaxed atomics alone would not order the data):
+    //  1. a device-scope atomic store is performed at the memory side shared by all XCDs (it
+    //     bypasses the XCD's L2), and s_waitcnt(0) returns only once every store of the
+    //     thread has been acknowledged there, i.e. is visible to any later device-scope load;
+    //  2. the barrier after that wait means thread 0's counter increment (a device-scope atomic
+    //     performed at the same memory side) is issued after all 512 threads' partials are
+    //     visible; the counter's value orders the workgroups of a tile;
+    //  3. the workgroup that reads S - 1 from the counter knows every other workgroup's
+    //     increment happened, hence (2) every other partial is visible; its loads of the
+    //     partials are device-scope atomic loads (no stale L2 or L1 line can serve them) and are
+    //     issued only after the counter's value has returned (s_last through LDS and a barrier).
+    //  The counter is reset by that last workgroup with a device-scope store; the next launch
+    //  of the kernel starts after this one has ended (stream order), so it sees zero.
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
       if (row[i] < a.M)
