@@ -1,16 +1,17 @@
 // Shared pieces of the bf16 projection GEMMs (the packed weight operands, the 32x32x16 MFMA
-// tile, the epilogues) and the tiled kernel for more than 128 rows.
+// tile, the epilogues) and the tiled kernel.
 //
 // bf16 path: the weights are in a packed operand layout (the B operand of one 32x32x16 MFMA
 // is one contiguous kilobyte), so every weight load is a full-rate contiguous 1 KB access.
-// Tiled kernel (more than 128 rows): one 224 x 64 WV output tile per workgroup of WV = 4, 3
+// Tiled kernel (the automatic choice above 32 rows): one 224 x 64 WV output tile per workgroup of WV = 4, 3
 // or 2 waves, one wave per SIMD, each 224 x 64 = 7 x 2 MFMA tiles (224 accumulators in AGPRs).  224 = 448 / 2
-// makes the decode row count (64 slots x 7 rows) exactly two row tiles.  The activation tile
+// makes the decode row count (64 slots x 7 rows) exactly two row tiles; a product of more than
+// 128 rows has at least two row tiles, its rows split evenly in 32-row blocks.  The activation tile
 // is streamed in 32-wide k stages through an 8-deep LDS ring filled by direct global->LDS
 // loads and shared by the waves; each wave loads its own weight operands straight into a
 // 4-stage register ring.  Each 64-byte LDS row keeps its four 16-byte k-chunks XOR-swizzled by
 // (row/4)%4 so that the 16 rows an MFMA operand read touches fall in distinct banks.
-// Skinny kernel (at most 128 rows): workgroups of two waves (one for very wide products), each
+// Skinny kernel (at most 128 rows; the automatic choice up to 32): workgroups of two waves (one for very wide products), each
 // wave streaming 64 weight columns while the pair shares the activation stages.
 // Split-K: split s covers k-stages [s kt, (s+1) kt) and writes fp32 partials that
 // splitk_reduce_kernel sums in split order - no atomics - so every output element has a fixed
@@ -432,8 +433,8 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* smem, int u
   }
 }
 
-// One workgroup: row tile mt of TM2 rows, or, with a live-row count on the device (a packed
-// decode pass), the live rows split evenly over the n_mt tiles in whole 32-row blocks.  The
+// One workgroup: row tile mt of the rows (with a live-row count on the device, a packed decode
+// pass, the live ones) split evenly over the n_mt tiles in whole 32-row blocks.  The
 // tile body is instantiated for every count of live 32-row blocks, so that the blocks past the
 // live rows cost neither an MFMA nor a branch in the pipeline loop (a uniform branch around
 // each MFMA and operand read made the decode launches 10-25 % slower).
@@ -445,11 +446,8 @@ void gemm_bf16_big_kernel(GemmArgs a, int n_mt, int n_units, int S, float* part)
   const int grp = id / (8 * n_mt), rem = id % (8 * n_mt);
   const int mt = rem / 8, unit = grp * 8 + (rem % 8);
   if (unit >= n_units) return;
-  int th = TM2, m_lim = a.M;
-  if (a.m_live) {
-    m_lim = min(__builtin_amdgcn_readfirstlane(*a.m_live), a.M);
-    th = min(TM2, ((m_lim + n_mt - 1) / n_mt + 31) / 32 * 32);
-  }
+  const int m_lim = a.m_live ? min(__builtin_amdgcn_readfirstlane(*a.m_live), a.M) : a.M;
+  const int th = min(TM2, ((m_lim + n_mt - 1) / n_mt + 31) / 32 * 32);
   const int m0 = mt * th;
   if (m0 >= m_lim) return;
   const int row_lim = min(m_lim, m0 + th);

@@ -4,14 +4,15 @@
 //
 // bf16 path: the weights are in a packed operand layout (the B operand of one 32x32x16 MFMA
 // is one contiguous kilobyte), so every weight load is a full-rate contiguous 1 KB access.
-// Tiled kernel (more than 128 rows): one 224 x 64 WV output tile per workgroup of WV = 4, 3
+// Tiled kernel (the automatic choice above 32 rows): one 224 x 64 WV output tile per workgroup of WV = 4, 3
 // or 2 waves, one wave per SIMD, each 224 x 64 = 7 x 2 MFMA tiles (224 accumulators in AGPRs).  224 = 448 / 2
-// makes the decode row count (64 slots x 7 rows) exactly two row tiles.  The activation tile
+// makes the decode row count (64 slots x 7 rows) exactly two row tiles; a product of more than
+// 128 rows has at least two row tiles, its rows split evenly in 32-row blocks.  The activation tile
 // is streamed in 32-wide k stages through an 8-deep LDS ring filled by direct global->LDS
 // loads and shared by the waves; each wave loads its own weight operands straight into a
 // 4-stage register ring.  Each 64-byte LDS row keeps its four 16-byte k-chunks XOR-swizzled by
 // (row/4)%4 so that the 16 rows an MFMA operand read touches fall in distinct banks.
-// Skinny kernel (at most 128 rows): workgroups of two waves (one for very wide products), each
+// Skinny kernel (at most 128 rows; the automatic choice up to 32): workgroups of two waves (one for very wide products), each
 // wave streaming 64 weight columns while the pair shares the activation stages.
 // Split-K: split s covers k-stages [s kt, (s+1) kt) and writes fp32 partials that
 // splitk_reduce_kernel sums in split order - no atomics - so every output element has a fixed
@@ -475,7 +476,11 @@ int big_waves(const GemmArgs& a, int n_mt, int S) {
 
 template <int EPI>
 hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
-  const int n_mt = (a.M + TM2 - 1) / TM2;
+  // at least two row tiles above 128 rows: at 224 rows two tiles of 128 + 96 rows (a smaller
+  // activation stage per CU, twice the workgroups) were 20-30 % faster than one of 224.  Not for
+  // very wide products (the LM head), whose column tiles alone fill the CUs several times over:
+  // there a second row tile only reads the weights twice (+12 % at 224 rows, measured).
+  const int n_mt = std::max((a.M + TM2 - 1) / TM2, a.M > 128 && a.N <= 65536 ? 2 : 1);
   const int S = (a.splits > 1 && a.part) ? a.splits : 1;
   const int WV = big_waves<EPI>(a, n_mt, S);
   const int tno = (EPI == EPI_SWIGLU ? 32 : 64) * WV;
@@ -529,10 +534,11 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
 
 template <int EPI>
 hipError_t launch_path(const GemmArgs& a, hipStream_t s) {
-  // automatic: the skinny kernel up to 64 rows, and up to 128 rows unless the product is so
-  // wide (the LM head) that the tiled kernel's 224-row tiles have work for every CU
+  // automatic: the skinny kernel up to 32 rows (64 for very wide products, the LM head), the
+  // tiled kernel above (measured per decode pass: 16 slots, 112 rows, 7.28 -> 6.49 ms; 8 slots,
+  // 56 rows, 5.59 -> 5.52 ms; at 7 rows the skinny kernel stays ahead)
   const bool skinny = a.path == GEMM_PATH_SKINNY ||
-                      (a.path == GEMM_PATH_AUTO && (a.M <= 64 || (a.M <= kSkinnyMaxRows && a.N <= 65536)));
+                      (a.path == GEMM_PATH_AUTO && (a.M <= 32 || (a.M <= 64 && a.N > 65536)));
   return skinny ? launch_skinny<EPI>(a, s) : launch_big<EPI>(a, s);
 }
 
