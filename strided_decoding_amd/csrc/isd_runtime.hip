@@ -217,7 +217,9 @@ void derive(isd_ctx& x) {
   x.max_dec_rows = c.max_batch * x.R;
   x.max_rows = std::max(x.max_dec_rows, c.max_prefill_tokens);
   x.n_chunks = cdiv(c.vocab, kStatChunk);
-  x.attn_split = attn_split_len(c.max_batch, c.n_kv_heads, c.max_seq_len + 2 * c.stride_n);
+  // (a function of the configuration's sequence length, not of the stride, so that an AR
+  // context and an ISD context of the same model split every row's keys alike)
+  x.attn_split = attn_split_len(c.max_batch, c.n_kv_heads, c.max_seq_len);
   x.max_splits = cdiv(c.max_seq_len + 2 * c.stride_n, x.attn_split);
   const int G = c.n_q_heads / c.n_kv_heads;
   x.ncb = (x.R * G <= 32) ? 2 : 4;
@@ -516,7 +518,9 @@ isd_status forward(isd_ctx& x, int M, int n_items, bool decode, const int32_t* l
         aa.part_ml = x.part_ml;
         aa.part_rows = x.max_dec_rows;
         TIMED("attention", launch_attn_bf16(aa, s));
-        TIMED("attn_combine", launch_attn_combine_bf16(aa, s));
+        // with one split every live row is final in the attention kernel (rows past the live
+        // ones are never read): no merge
+        if (x.max_splits > 1) TIMED("attn_combine", launch_attn_combine_bf16(aa, s));
       } else {
         aa.split = 0;
         TIMED("attention", launch_attn_bf16(aa, s));

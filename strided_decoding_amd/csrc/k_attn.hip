@@ -392,7 +392,9 @@ int attn_split_len(int batch, int n_kv_heads, int max_ctx) {
   // With at least two (slot, KV head) pairs per CU the pairs alone fill the chip: the longest
   // split, so that most rows are final in their first split and skip the merge (measured: the
   // 64-slot pass is 1.2 % faster than with 1024-key splits; 16 slots need the short splits).
-  if ((long long)batch * n_kv_heads >= 512) return 2048;
+  // Contexts a little past 2048 keys take one 2560-key split, so that no row needs the merge
+  // (the pass then launches no combine kernel).
+  if ((long long)batch * n_kv_heads >= 512) return max_ctx > 2048 && max_ctx <= 2560 ? 2560 : 2048;
   // else about kAttnItems (slot, KV head, split) workgroups at the longest context, 128 .. 2048
   // keys each
   constexpr long long kAttnItems = ISD_ATTN_ITEMS;
