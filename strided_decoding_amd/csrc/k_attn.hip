@@ -39,6 +39,27 @@ constexpr float kRescale = 8.f;            // log2 headroom of the softmax refer
 constexpr int kAttnBufs = ISD_ATTN_NBUF;
 
 ISD_DEV u32x4_t ld16(const uint16_t* p) { return *(const u32x4_t*)p; }
+
+// The maximum (sum) of x over lanes l and l ^ 16, and over l and l ^ 32: a register swapped with
+// itself by gfx950's lane-swap instructions (rows of 16 lanes, halves of 32) leaves each lane
+// holding its own value in one result and its partner's in the other (which is which depends on
+// the lane; max and + are symmetric).  No LDS round trip, unlike a generic lane shuffle.
+ISD_DEV float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+ISD_DEV float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+ISD_DEV float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+ISD_DEV float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 ISD_DEV u32x4_t lds16(const uint8_t* p) { return *(const u32x4_t*)p; }
 
 // One workgroup per (item, KV head, context split); wave w handles the 16 query columns
@@ -186,8 +207,7 @@ __global__ __launch_bounds__(64 * NCB) void attn_bf16_kernel(AttnArgs a) {
         sv[4 * b + r] = v;
         mx = fmaxf(mx, v);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = max_xor32(max_xor16(mx));
     const bool raise = mx > m_run + kRescale;      // also the first visible key of the column
     const float m_new = raise ? mx : m_run;
     const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
@@ -203,8 +223,7 @@ __global__ __launch_bounds__(64 * NCB) void attn_bf16_kernel(AttnArgs a) {
         ps += __uint_as_float(pk[w] << 16) + __uint_as_float(pk[w] & 0xffff0000u);
       }
     }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
+    ps = sum_xor32(sum_xor16(ps));
     l_run = l_run * alpha + ps;
     m_run = m_new;
     if (__any(raise)) {
