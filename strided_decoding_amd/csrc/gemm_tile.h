@@ -3,16 +3,18 @@
 //
 // bf16 path: the weights are in a packed operand layout (the B operand of one 32x32x16 MFMA
 // is one contiguous kilobyte), so every weight load is a full-rate contiguous 1 KB access.
-// Tiled kernel (the automatic choice above 32 rows): one 224 x 64 WV output tile per workgroup of WV = 4, 3
-// or 2 waves, one wave per SIMD, each 224 x 64 = 7 x 2 MFMA tiles (224 accumulators in AGPRs).  224 = 448 / 2
-// makes the decode row count (64 slots x 7 rows) exactly two row tiles; a product of more than
-// 128 rows has at least two row tiles, its rows split evenly in 32-row blocks.  The activation tile
-// is streamed in 32-wide k stages through an 8-deep LDS ring filled by direct global->LDS
-// loads and shared by the waves; each wave loads its own weight operands straight into a
-// 4-stage register ring.  Each 64-byte LDS row keeps its four 16-byte k-chunks XOR-swizzled by
-// (row/4)%4 so that the 16 rows an MFMA operand read touches fall in distinct banks.
-// Skinny kernel (at most 128 rows; the automatic choice up to 32): workgroups of two waves (one for very wide products), each
-// wave streaming 64 weight columns while the pair shares the activation stages.
+// Tiled kernel (the automatic choice above 32 rows): one 224 x 64 WV output tile per
+// workgroup of WV = 4, 3 or 2 waves, one wave per SIMD, each 224 x 64 = 7 x 2 MFMA tiles (224
+// accumulators in AGPRs).  224 = 448 / 2 makes the decode row count (64 slots x 7 rows)
+// exactly two row tiles; a product of more than 128 rows has at least two row tiles, its rows
+// split evenly in 32-row blocks.  The activation tile is streamed in 32-wide k stages through
+// an 8-deep LDS ring filled by direct global->LDS loads and shared by the waves; each wave
+// loads its own weight operands straight into a 4-stage register ring.  Each 64-byte LDS row
+// keeps its four 16-byte k-chunks XOR-swizzled by (row/4)%4 so that the 16 rows an MFMA
+// operand read touches fall in distinct banks.
+// Skinny kernel (at most 128 rows; the automatic choice up to 32): workgroups of two waves (one
+// for very wide products), each wave streaming 64 weight columns while the pair shares the
+// activation stages.
 // Split-K: split s covers k-stages [s kt, (s+1) kt) and writes fp32 partials that
 // splitk_reduce_kernel sums in split order - no atomics - so every output element has a fixed
 // accumulation order that depends only on K and the split count, never on the number of rows.
