@@ -97,3 +97,13 @@ def test_attention_32b_head_grouping(batch, lo, hi):
     q_len = np.random.default_rng(batch).integers(0, 8, size=batch).astype(np.int32)
     q_len[0] = 7
     _check(inp, q_len, _run(inp, q_len, n_kv=8), group=8)
+
+
+def test_attention_one_split_past_2048_keys():
+    """64 slots with contexts a little past 2048 keys take a single 2560-key split per (slot, KV
+    head): every row is final in the attention kernel, and each workgroup reloads its window of
+    page ids (128 pages, 2048 keys) once inside its key range."""
+    inp = I.attn_micro(batch=64, ctx_lo=2049, ctx_hi=2560, seed=41)
+    assert int(inp["ctx"].max()) > 2048 + 16
+    q_len = np.random.default_rng(41).integers(1, 8, size=64).astype(np.int32)
+    _check(inp, q_len, _run(inp, q_len))
