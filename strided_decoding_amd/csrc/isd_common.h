@@ -46,6 +46,37 @@ ISD_DEV f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Split-K reduction of fp32 4-vectors: a = sum over s = 0 .. S-1 (1 <= S <= MAXS) of
+// p[s * stride] and, with PAIR, b = the same at p + off, each added in split order starting from
+// zero.  Every load is issued before the first add (one memory round trip instead of S dependent
+// ones); the loads are unconditional, s > S - 1 re-reading split S - 1 (callers choose MAXS as
+// the smallest power of two >= S, so that happens only for other S), and the adds past S are
+// selected away.
+template <int MAXS, bool PAIR>
+ISD_DEV void sum_split_partials(const float* p, size_t stride, int S, size_t off, f32x4_t& a, f32x4_t& b) {
+  f32x4_t ta[MAXS], tb[PAIR ? MAXS : 1];
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s) {
+    const size_t o = (size_t)min(s, S - 1) * stride;
+    ta[s] = *(const f32x4_t*)(p + o);
+    if (PAIR) tb[s] = *(const f32x4_t*)(p + off + o);
+  }
+  a = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  b = a;
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s) {
+    const bool in = s < S;
+    const f32x4_t na = a + ta[s];
+    a = in ? na : a;
+    if (PAIR) {
+      const f32x4_t nb = b + tb[s];
+      b = in ? nb : b;
+    }
+  }
+}
+// The MAXS bucket of a split count: the smallest power of two >= S (S <= 16).
+inline int split_bucket(int S) { return S <= 1 ? 1 : S <= 2 ? 2 : S <= 4 ? 4 : S <= 8 ? 8 : 16; }
+
 // ---------------------------------------------------------------------------------------
 // Wave (64-lane) reductions.
 ISD_DEV float wave_max(float v) {

@@ -10,6 +10,7 @@
 // orders come from block-wide prefix sums, so the page tables are a deterministic function
 // of the slot states.
 #include <algorithm>
+#include <type_traits>
 
 #include "isd_common.h"
 
@@ -283,7 +284,10 @@ __global__ __launch_bounds__(1024) void rmsnorm_kernel(const float* X, const T* 
 // (a RoPE group is 4 elements and their 4 partners half a head away); with split-K partials
 // the projection's reduction (in split order, plus the LoRA delta, rounded to act) happens
 // here, so the QKV projection is never stored.
-template <typename T>
+constexpr int kRopeMaxSplits = 16;   // split-K factor of the QKV projection
+
+// MAXS: the split bucket of a.splits (1 without partials)
+template <typename T, int MAXS>
 __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
   const int hd = a.hd, half = hd / 2, P = a.P, h4 = half / 4;
   const int qd = a.Hq * hd, kd = a.Hkv * hd, width = qd + 2 * kd;
@@ -293,22 +297,35 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
   const size_t split_stride = (size_t)a.rows * width;
   for (size_t it = (size_t)blockIdx.x * blockDim.x + threadIdx.x; it < total; it += (size_t)gridDim.x * blockDim.x) {
     const int r = (int)(it / per_row), w = (int)(it % per_row);
-    const int pos = a.row_pos[r];
+    const int pos = a.row_pos[r], slot = a.row_slot[r];
     const int dr = (a.part && a.delta_row) ? a.delta_row[r] : -1;
     // columns c .. c+3 of row r's projection in fp32 (summed from the split-K partials, or as
     // the unsplit projection stored them): q, k and v are rounded to act once, after RoPE
-    auto load4 = [&](int c, float* v) {
-      f32x4_t acc;
+    // (with PAIR also columns c + off .. c + off + 3 into w; every load of both is issued
+    // before the first add)
+    auto load4 = [&](auto pair, int c, int off, float* v, float* w) {
+      constexpr bool PAIR = decltype(pair)::value;
+      f32x4_t acc, acc2;
       if (a.part) {
-        const float* pr = a.part + (size_t)r * width + c;
-        acc = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-        for (int sp = 0; sp < a.splits; ++sp) acc += *(const f32x4_t*)(pr + sp * split_stride);
-        if (dr >= 0) acc += *(const f32x4_t*)(a.delta + (size_t)dr * a.ldd + c);
+        f32x4_t d = {0.f, 0.f, 0.f, 0.f}, d2 = d;
+        if (dr >= 0) {
+          d = *(const f32x4_t*)(a.delta + (size_t)dr * a.ldd + c);
+          if (PAIR) d2 = *(const f32x4_t*)(a.delta + (size_t)dr * a.ldd + c + off);
+        }
+        sum_split_partials<MAXS, PAIR>(a.part + (size_t)r * width + c, split_stride, a.splits, off, acc, acc2);
+        if (dr >= 0) {
+          acc += d;
+          if (PAIR) acc2 += d2;
+        }
       } else {
         acc = *(const f32x4_t*)(a.qkv + (size_t)r * width + c);
+        if (PAIR) acc2 = *(const f32x4_t*)(a.qkv + (size_t)r * width + c + off);
       }
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) v[jj] = acc[jj];
+      for (int jj = 0; jj < 4; ++jj) {
+        v[jj] = acc[jj];
+        if (PAIR) w[jj] = acc2[jj];
+      }
     };
     if (w < qi + ki) {
       // RoPE group: head h, elements e0 .. e0+3 and their partners e0+half ..
@@ -322,32 +339,35 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
           for (int jj = 0; jj < 4; ++jj) qo[jj] = qo[jj + half] = from_f<T>(0.f);
         continue;
       }
+      // the page id (used by k only) and the rotation are loaded ahead of the projection
+      const int page = a.page_table[(size_t)slot * a.max_pages + pos / P];
+      float cs[4], sn[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        cs[jj] = a.cos_t[(size_t)pos * half + e0 + jj];
+        sn[jj] = a.sin_t[(size_t)pos * half + e0 + jj];
+      }
       float x1[4], x2[4];
       const int c0 = (isq ? 0 : qd) + h * hd + e0;
-      load4(c0, x1);
-      load4(c0 + half, x2);
-      const float* cs = a.cos_t + (size_t)pos * half + e0;
-      const float* sn = a.sin_t + (size_t)pos * half + e0;
+      load4(std::true_type{}, c0, half, x1, x2);
       T* dst = qo;
       if (!isq) {
-        const int page = a.page_table[(size_t)a.row_slot[r] * a.max_pages + pos / P];
         if (page < 0) continue;                // no page (never after a successful reserve)
         dst = (T*)a.k_pool + (((size_t)page * a.Hkv + h) * P + pos % P) * hd + e0;
       }
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const float c = cs[jj], sv = sn[jj];
-        dst[jj] = from_f<T>(x1[jj] * c - x2[jj] * sv);
-        dst[jj + half] = from_f<T>(x2[jj] * c + x1[jj] * sv);
+        dst[jj] = from_f<T>(x1[jj] * cs[jj] - x2[jj] * sn[jj]);
+        dst[jj + half] = from_f<T>(x2[jj] * cs[jj] + x1[jj] * sn[jj]);
       }
     } else {
       // V: dims d0 .. d0+3 of KV head h, written into the page's transposed layout
       if (pos < 0) continue;
       const int j = w - qi - ki;
       const int h = j / (hd / 4), d0 = (j % (hd / 4)) * 4;
+      const int page = a.page_table[(size_t)slot * a.max_pages + pos / P];
       float v[4];
-      load4(qd + kd + h * hd + d0, v);
-      const int page = a.page_table[(size_t)a.row_slot[r] * a.max_pages + pos / P];
+      load4(std::false_type{}, qd + kd + h * hd + d0, 0, v, v);
       if (page < 0) continue;
       T* vp = (T*)a.v_pool + (((size_t)page * a.Hkv + h) * hd + d0) * P + pos % P;
 #pragma unroll
@@ -440,10 +460,16 @@ hipError_t launch_rmsnorm(const float* X, const T* g, T* Y, int rows, int d, flo
 template <typename T>
 hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
-  if (a.hd % 8) return hipErrorInvalidValue;
+  if (a.hd % 8 || (a.part && (a.splits < 1 || a.splits > kRopeMaxSplits))) return hipErrorInvalidValue;
   const size_t items = (size_t)a.rows * ((a.Hq + a.Hkv) * (a.hd / 8) + a.Hkv * (a.hd / 4));
   const unsigned blocks = (unsigned)std::min<size_t>((items + 255) / 256, 4096);
-  hipLaunchKernelGGL(rope_append_kernel<T>, dim3(blocks), dim3(256), 0, s, a);
+  switch (a.part ? split_bucket(a.splits) : 1) {
+    case 1: hipLaunchKernelGGL((rope_append_kernel<T, 1>), dim3(blocks), dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((rope_append_kernel<T, 2>), dim3(blocks), dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((rope_append_kernel<T, 4>), dim3(blocks), dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((rope_append_kernel<T, 8>), dim3(blocks), dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((rope_append_kernel<T, 16>), dim3(blocks), dim3(256), 0, s, a); break;
+  }
   return hipGetLastError();
 }
 

@@ -283,8 +283,10 @@ __global__ __launch_bounds__(64 * WV) void gemm_bf16_skinny_kernel(GemmArgs a, i
   }
 }
 
-// Sum the split-K partials in split order and apply the epilogue.
-template <int EPI>
+constexpr int kMaxSplits = 16;
+
+// Sum the split-K partials in split order and apply the epilogue (MAXS: the split bucket).
+template <int EPI, int MAXS>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a, int S, const float* part) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU);
   const size_t ld = DUAL ? 2 * (size_t)a.N : (size_t)a.N;
@@ -292,12 +294,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a, int S, c
   const size_t n4 = (size_t)m_lim * a.N / 4;
   for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n4; e += (size_t)gridDim.x * blockDim.x) {
     const int row = (int)(e * 4 / a.N), col = (int)(e * 4 % a.N);
-    f32x4_t v = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < S; ++s) {
-      const float* pr = part + ((size_t)s * a.M + row) * ld;
-      v += *(const f32x4_t*)(pr + col);
-      if (DUAL) u += *(const f32x4_t*)(pr + a.N + col);
-    }
+    f32x4_t v, u;
+    sum_split_partials<MAXS, DUAL>(part + (size_t)row * ld + col, (size_t)a.M * ld, S, a.N, v, u);
 #pragma unroll
     for (int j = 0; j < 4; ++j) epilogue_store_t<bf16, EPI>(a, row, col + j, v[j], u[j]);
   }
@@ -310,7 +308,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a, int S, c
 // both paths give the same normalized row for the same residual row.
 constexpr int kNormThreads = 1024;
 constexpr int kNormMaxGroups = 2;         // rows up to 8192 wide
-constexpr int kMaxSplits = 16;
+template <int MAXS>
 __global__ __launch_bounds__(kNormThreads) void splitk_resid_norm_kernel(GemmArgs a, int S, const float* part) {
   __shared__ float sh[kNormThreads / 64];
   const int row = blockIdx.x, tid = threadIdx.x;
@@ -326,10 +324,13 @@ __global__ __launch_bounds__(kNormThreads) void splitk_resid_norm_kernel(GemmArg
     const int c = 4 * (tid + kNormThreads * k);
     rv[k] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     if (c < a.N) {
-      f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-      for (int s = 0; s < S; ++s) v += *(const f32x4_t*)(prow + s * split_stride + c);
-      if (dr >= 0) v += *(const f32x4_t*)(a.delta + (size_t)dr * a.ldd + c);
-      const f32x4_t r = *(const f32x4_t*)(R + c) + v;
+      const f32x4_t rin = *(const f32x4_t*)(R + c);
+      f32x4_t dv = {0.f, 0.f, 0.f, 0.f};
+      if (dr >= 0) dv = *(const f32x4_t*)(a.delta + (size_t)dr * a.ldd + c);
+      f32x4_t v, unused;
+      sum_split_partials<MAXS, false>(prow + c, split_stride, S, 0, v, unused);
+      if (dr >= 0) v += dv;
+      const f32x4_t r = rin + v;
       *(f32x4_t*)(R + c) = r;
       rv[k] = r;
 #pragma unroll
@@ -418,13 +419,21 @@ hipError_t finish(const GemmArgs& a, int S, hipStream_t s) {
   if (S > 1 && a.keep_part) return hipSuccess;       // the consumer reduces the partials
   const bool norm = EPI == EPI_RESID && a.norm_out;
   if (S > 1) {
-    if (norm) {
-      hipLaunchKernelGGL(splitk_resid_norm_kernel, dim3(a.M), dim3(kNormThreads), 0, s, a, S, (const float*)a.part);
-      return hipGetLastError();
-    }
     const size_t n4 = (size_t)a.M * a.N / 4;
     const int blocks = (int)std::min<size_t>((n4 + 255) / 256, 4096);
-    hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3(blocks), dim3(256), 0, s, a, S, (const float*)a.part);
+    const float* part = (const float*)a.part;
+#define ISD_REDUCE(B)                                                                                   \
+  if (norm)                                                                                             \
+    hipLaunchKernelGGL(splitk_resid_norm_kernel<B>, dim3(a.M), dim3(kNormThreads), 0, s, a, S, part); \
+  else                                                                                                  \
+    hipLaunchKernelGGL((splitk_reduce_kernel<EPI, B>), dim3(blocks), dim3(256), 0, s, a, S, part);
+    switch (split_bucket(S)) {
+      case 2: ISD_REDUCE(2) break;
+      case 4: ISD_REDUCE(4) break;
+      case 8: ISD_REDUCE(8) break;
+      default: ISD_REDUCE(16) break;
+    }
+#undef ISD_REDUCE
     return hipGetLastError();
   }
   if (norm) return launch_rmsnorm<bf16>(a.R, (const bf16*)a.norm_g, (bf16*)a.norm_out, a.M, a.N, a.norm_eps, s);
