@@ -33,6 +33,10 @@ ISD_DEV uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
 }
 
+// Cache-policy operand of a direct global->LDS load with the nt (non-temporal) bit: data read
+// once per pass, which should not displace cached lines.
+constexpr int kCachePolicyNT = 2;
+
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;   // MFMA operand (8 bf16)
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;     // 16x16 MFMA accumulator
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;  // 16-byte load unit

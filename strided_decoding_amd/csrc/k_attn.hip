@@ -142,7 +142,9 @@ __global__ __launch_bounds__(64 * NCB) void attn_bf16_kernel(AttnArgs a) {
         const int e = (lane & 1) ^ ((dim >> 3) & 1);
         src = vbase + (size_t)(i < 4 ? pg0 : pg1) * page_elems + (size_t)dim * 16 + e * 8;
       }
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(st + j * 1024), 16, 0, 0);
+      // non-temporal: every K/V byte is read once per pass, so it should not displace cached
+      // lines (measured 88.6 -> 80.4 us per launch at 64 slots, contexts ~2000)
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(st + j * 1024), 16, 0, kCachePolicyNT);
     }
   };
 

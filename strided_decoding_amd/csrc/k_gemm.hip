@@ -162,8 +162,10 @@ __global__ __launch_bounds__(64 * WV) void gemm_bf16_skinny_kernel(GemmArgs a, i
       for (int kk = 0; kk < 2; ++kk) {
         const int lk = ls - (DUAL ? j * lp.per : 0);
         const uint16_t* l = (MODE == kLoraTail && lk >= 0 && lk < (DUAL ? lp.per : lp.n)) ? lwsrc[j] + (2 * lk + kk) * 512 : zero;
+        // weights non-temporal (streamed once; measured -6 % per decode pass at 1 slot)
         __builtin_amdgcn_global_load_lds((const void*)(live ? wsrc[j] + (2 * kt + kk) * 512 : l),
-                                         (lds_void*)(st + (2 * MT + 2 * NB * wave + 2 * j + kk) * 1024), 16, 0, 0);
+                                         (lds_void*)(st + (2 * MT + 2 * NB * wave + 2 * j + kk) * 1024), 16, 0,
+                                         kCachePolicyNT);
       }
   };
   f32x16_t acc[MT][NB];
