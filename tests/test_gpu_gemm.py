@@ -136,6 +136,42 @@ def test_gemm_residual_with_fused_rmsnorm(splits):
     _check(y.float().cpu().numpy().ravel(), yref.ravel())
 
 
+@pytest.mark.parametrize("M", [7, 200])
+@pytest.mark.parametrize("S,K", [(3, 1536), (5, 1280), (6, 1536), (12, 1536), (16, 2048)])
+def test_gemm_split_counts(M, S, K):
+    """Split counts that are not powers of two, and the largest (16), on the skinny (7 rows) and
+    tiled (200 rows) kernels: the ordered reductions (plain, the SwiGLU pair, residual + RMSNorm)
+    issue the split loads together in a group of the next power of two, the slots past S
+    re-reading the last split and left out of the sum."""
+    from strided_decoding_amd import gemm
+    print(f"gemm splits S={S} M={M} K={K}", flush=True)
+    N = 512
+    X = _rand((M, K), 60 + S, 1.0)
+    W = _rand((N, K), 61, 0.05)
+    W2 = _rand((N, K), 62, 0.05)
+    Wp, W2p = _pk(W), _pk(W2)
+    Y = gemm(X, Wp, "store_f32", splits=S)
+    torch.cuda.synchronize()
+    ref = X.double() @ W.double().T
+    assert (Y.double() - ref).abs().max().item() <= 1e-4 * ref.abs().max().item()
+    H = gemm(X, Wp, "swiglu", W2=W2p, splits=S)
+    torch.cuda.synchronize()
+    rows, cols = _pick(M, N, 300, 63)
+    g, u = _ref(X, W, rows, cols), _ref(X, W2, rows, cols)
+    _check(H.float().cpu().numpy()[rows, cols], g / (1 + np.exp(-g)) * u)
+    R0 = _rand((M, N), 64, 1.0, torch.float32)
+    R = R0.clone()
+    gn = (1.0 + 0.1 * _rand((N,), 65, 1.0, torch.float32)).to(torch.bfloat16)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    gemm(X, Wp, "resid", R=R, splits=S, norm_g=gn, norm_out=y, norm_eps=1e-6)
+    torch.cuda.synchronize()
+    Rref = R0.double() + ref
+    assert (R.double() - Rref).abs().max().item() <= 1e-4 * Rref.abs().max().item()
+    Rg = R.double().cpu().numpy()
+    yref = Rg / np.sqrt((Rg ** 2).mean(axis=1, keepdims=True) + 1e-6) * gn.double().cpu().numpy()
+    _check(y.float().cpu().numpy().ravel(), yref.ravel())
+
+
 SKINNY_ROWS = [1, 7, 28, 32, 33, 56, 64, 65, 112, 128]
 
 
