@@ -294,45 +294,67 @@ __global__ __launch_bounds__(64 * NCB) void attn_bf16_kernel(AttnArgs a) {
 
 // Merge the split partials of each row in ascending split order (the row at position p uses
 // splits 0 .. ceil((p+1)/split)-1; rows with p < split were written by the attention kernel);
-// dead rows (position -1) are written as zeros.  Thread t of a row's block handles 16 dims of
-// head t / 8.
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+// dead rows (position -1) are written as zeros.  Workgroup (row, y), thread x handles item
+// t = 256 y + x of the row: dims 4 (t % 32) .. +3 of head t / 32.  Every split's (m, l) and
+// output slice is loaded before the first use, in groups of G splits (G = 4, 8 or 16, the
+// smallest that holds the row's splits, at most 16; a group's slots past the row's last split
+// re-read it and are left out), so a row with up to 16 splits costs one memory round trip.
+// The weights and sums follow the split order: M = max of the maxima, w_s = exp2(m_s - M)
+// (zero for a split with no visible key), O = sum_s w_s O_s / sum_s w_s l_s.
+constexpr int kMergeThreads = 256;
+template <int G>
+ISD_DEV f32x4_t merge_splits(const AttnArgs& a, size_t e0, size_t stride, int ns, int d4, float& inv) {
+  float2 ml[G];
+  f32x4_t po[G];
+  auto load_group = [&](int s0, bool with_o) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const size_t e = e0 + (size_t)min(s0 + i, ns - 1) * stride;
+      ml[i] = *(const float2*)(a.part_ml + e * 2);
+      if (with_o) po[i] = *(const f32x4_t*)(a.part_o + e * HD + 4 * d4);
+    }
+  };
+  float M = kNegInf;
+  for (int s0 = 0; s0 < ns; s0 += G) {
+    load_group(s0, ns <= G);   // a single group: the outputs come with the maxima
+#pragma unroll
+    for (int i = 0; i < G; ++i) M = fmaxf(M, ml[i].x);   // repeats of the last split: same maximum
+  }
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += G) {
+    if (ns > G) load_group(s0, true);
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const bool in = s0 + i < ns;
+      const float w = (ml[i].x == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ml[i].x - M);
+      const float nl = L + w * ml[i].y;
+      const f32x4_t na = acc + w * po[i];
+      L = in ? nl : L;
+      acc = in ? na : acc;
+    }
+  }
+  inv = L > 0.f ? 1.f / L : 0.f;
+  return acc;
+}
+
+__global__ __launch_bounds__(kMergeThreads) void attn_combine_kernel(AttnArgs a) {
   const int row = blockIdx.x;
   const int pos = a.row_pos[row];
   if (pos >= 0 && pos < a.split) return;                     // written by the attention kernel
+  const int t = blockIdx.y * kMergeThreads + threadIdx.x;
+  if (t >= a.Hq * (HD / 4)) return;
+  const int head = t / (HD / 4), d4 = t % (HD / 4);
   const size_t stride = (size_t)a.part_rows * a.Hq;          // between splits
-  for (int t = threadIdx.x; t < a.Hq * 8; t += blockDim.x) {
-    const int head = t >> 3, sub = t & 7;
-    f32x4_t acc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    float inv = 0.f;
-    if (pos >= 0) {
-      const int ns = pos / a.split + 1;
-      const size_t e0 = (size_t)row * a.Hq + head;
-      float M = kNegInf;
-      // unrolled by 8 (the loads of eight splits issued together); the sums stay in split order
-#pragma unroll 8
-      for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, a.part_ml[(e0 + sp * stride) * 2]);
-      float L = 0.f;
-#pragma unroll 8
-      for (int sp = 0; sp < ns; ++sp) {
-        const size_t e = e0 + sp * stride;
-        const float2 ml = *(const float2*)(a.part_ml + e * 2);
-        const float w = (ml.x == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
-        L += w * ml.y;
-        const f32x4_t* po = (const f32x4_t*)(a.part_o + e * HD + 16 * sub);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] += w * po[j];
-      }
-      inv = L > 0.f ? 1.f / L : 0.f;
-    }
-    u32x4_t* out = (u32x4_t*)((uint16_t*)a.out + (size_t)row * a.Hq * HD + (size_t)head * HD + 16 * sub);
-    out[0] = (u32x4_t){pack_bf16x2(acc[0][0] * inv, acc[0][1] * inv), pack_bf16x2(acc[0][2] * inv, acc[0][3] * inv),
-                       pack_bf16x2(acc[1][0] * inv, acc[1][1] * inv), pack_bf16x2(acc[1][2] * inv, acc[1][3] * inv)};
-    out[1] = (u32x4_t){pack_bf16x2(acc[2][0] * inv, acc[2][1] * inv), pack_bf16x2(acc[2][2] * inv, acc[2][3] * inv),
-                       pack_bf16x2(acc[3][0] * inv, acc[3][1] * inv), pack_bf16x2(acc[3][2] * inv, acc[3][3] * inv)};
-  }
+  const size_t e0 = (size_t)row * a.Hq + head;
+  const int ns = pos >= 0 ? pos / a.split + 1 : 0;           // the same for the whole workgroup
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  float inv = 0.f;
+  if (ns > 8) acc = merge_splits<16>(a, e0, stride, ns, d4, inv);
+  else if (ns > 4) acc = merge_splits<8>(a, e0, stride, ns, d4, inv);
+  else if (ns > 0) acc = merge_splits<4>(a, e0, stride, ns, d4, inv);
+  uint2* out = (uint2*)((uint16_t*)a.out + (size_t)row * a.Hq * HD + (size_t)head * HD + 4 * d4);
+  *out = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv));
 }
 
 // fp32 path: one wave per (row, query head); keys 0 .. pos streamed from the pages with a
@@ -449,7 +471,8 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_attn_combine_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.n_rows), dim3(256), 0, s, a);
+  const int per_row = (a.Hq * (HD / 4) + kMergeThreads - 1) / kMergeThreads;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.n_rows, per_row), dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
 
