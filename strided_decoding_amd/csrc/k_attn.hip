@@ -76,6 +76,15 @@ __global__ __launch_bounds__(64 * NCB) void attn_bf16_kernel(AttnArgs a) {
   const size_t q_stride = (size_t)a.Hq * HD;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   if (it.nq <= 0) return;
+  // Page ids of the key range, lane l holding logical pages win + l and win + 64 + l (a window
+  // of 128 pages, 2048 keys: a whole context split; longer ranges reload it), read out with
+  // readlane: no memory access inside the KV pipeline besides its own loads.  The first window
+  // is loaded together with the context length (clamped to the table row, not to the context:
+  // entries past the context are never read out).
+  const int32_t* pt = a.page_table + (size_t)it.slot * a.max_pages;
+  int win = a.split ? (split * a.split) >> 4 : 0;
+  int pid0 = pt[min(win + lane, a.max_pages - 1)];
+  int pid1 = pt[min(win + 64 + lane, a.max_pages - 1)];
   const int ctx = a.ctx_len[it.slot];
   const int key_hi = min(ctx, it.pos0 + it.nq);
   int k_begin = 0, k_end = key_hi;
@@ -95,15 +104,16 @@ __global__ __launch_bounds__(64 * NCB) void attn_bf16_kernel(AttnArgs a) {
   const uint16_t* qsrc =
       (const uint16_t*)a.q + (size_t)(it.row0 + (qvalid ? qp : 0)) * q_stride + (size_t)(kvh * G + qh) * HD + g * 8;
 
-  // Page ids of the key range, lane l holding logical pages win + l and win + 64 + l (a window
-  // of 128 pages, 2048 keys: a whole context split; longer ranges reload it), read out with
-  // readlane: no memory access inside the KV pipeline besides its own loads.
-  const int32_t* pt = a.page_table + (size_t)it.slot * a.max_pages;
   const int last_page = (k_end - 1) >> 4;
-  int win = k_begin >> 4;
-  int pid0 = pt[min(win + lane, last_page)];
-  int pid1 = pt[min(win + 64 + lane, last_page)];
-  wait_vmcnt<0>();
+  // this wave's Q goes out now (4 direct loads into the last ring slot), the page ids are
+  // waited for with only those loads left in flight
+  {
+    uint8_t* qs = ring + (NBUF - 1) * kBlockBytes + wave * 4096;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      __builtin_amdgcn_global_load_lds((const void*)(qsrc + ks * 32), (lds_void*)(qs + ks * 1024), 16, 0, 0);
+  }
+  wait_vmcnt<4>();
   auto page_of = [&](int pg) -> int {
     if (pg >= win + 128) {
       wait_vmcnt<0>();
@@ -242,12 +252,6 @@ __global__ __launch_bounds__(64 * NCB) void attn_bf16_kernel(AttnArgs a) {
   // also tells that every wave is done with block blk-1, whose slot is refilled next.
   const int nblk = (k_end - k_begin + 31) >> 5;
   const int pro = min(NBUF - 1, nblk);
-  {
-    uint8_t* qs = ring + (NBUF - 1) * kBlockBytes + wave * 4096;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      __builtin_amdgcn_global_load_lds((const void*)(qsrc + ks * 32), (lds_void*)(qs + ks * 1024), 16, 0, 0);
-  }
   for (int blk = 0; blk < pro; ++blk) issue(blk);
   if (pro >= 3) wait_vmcnt<3 * PW>();                // this wave's Q has landed
   else if (pro == 2) wait_vmcnt<2 * PW>();

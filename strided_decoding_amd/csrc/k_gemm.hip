@@ -314,8 +314,19 @@ template <int MAXS>
 __global__ __launch_bounds__(kNormThreads) void splitk_resid_norm_kernel(GemmArgs a, int S, const float* part) {
   __shared__ float sh[kNormThreads / 64];
   const int row = blockIdx.x, tid = threadIdx.x;
-  if (a.m_live && row >= *a.m_live) return;        // a dead row of a packed pass
+  // the live-row count, the row's delta index and this thread's norm weights are loaded
+  // together, ahead of the row's data (one memory round trip before the partials, none after
+  // the reduction)
+  const int live = a.m_live ? *a.m_live : a.M;
   const int dr = a.delta_row ? a.delta_row[row] : -1;
+  const bf16* g = (const bf16*)a.norm_g;
+  float gv[kNormMaxGroups][4];
+#pragma unroll
+  for (int k = 0; k < kNormMaxGroups; ++k)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)   // (clamped, not branched: every load goes out at once)
+      gv[k][j] = to_f(g[min(4 * (tid + kNormThreads * k) + j, a.N - 1)]);
+  if (row >= live) return;                          // a dead row of a packed pass
   float* R = a.R + (size_t)row * a.ldr;
   const size_t split_stride = (size_t)a.M * a.N;
   const float* prow = part + (size_t)row * a.N;
@@ -341,14 +352,13 @@ __global__ __launch_bounds__(kNormThreads) void splitk_resid_norm_kernel(GemmArg
   }
   const float tot = block_sum_1024(ss, sh);
   const float denom = sqrtf(tot / (float)a.N + a.norm_eps);
-  const bf16* g = (const bf16*)a.norm_g;
   bf16* y = (bf16*)a.norm_out + (size_t)row * a.N;
 #pragma unroll
   for (int k = 0; k < kNormMaxGroups; ++k) {
     const int c = 4 * (tid + kNormThreads * k);
     if (c < a.N) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) y[c + j] = from_f<bf16>((rv[k][j] / denom) * to_f(g[c + j]));
+      for (int j = 0; j < 4; ++j) y[c + j] = from_f<bf16>((rv[k][j] / denom) * gv[k][j]);
     }
   }
 }
