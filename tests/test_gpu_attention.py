@@ -107,3 +107,12 @@ def test_attention_one_split_past_2048_keys():
     assert int(inp["ctx"].max()) > 2048 + 16
     q_len = np.random.default_rng(41).integers(1, 8, size=64).astype(np.int32)
     _check(inp, q_len, _run(inp, q_len))
+
+
+def test_attention_merge_of_many_splits():
+    """Two slots with contexts of 3000..4096 keys take 128-key splits: rows span 24..32 splits,
+    so the merge runs its multi-group path (16 splits a group, the maxima of every group
+    first); ragged query lengths put rows of one block on both sides of a split boundary."""
+    inp = I.attn_micro(batch=2, ctx_lo=3000, ctx_hi=4096, seed=43)
+    q_len = np.array([7, 5], np.int32)
+    _check(inp, q_len, _run(inp, q_len))
