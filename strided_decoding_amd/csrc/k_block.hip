@@ -263,6 +263,11 @@ __global__ __launch_bounds__(1024) void rmsnorm_kernel(const float* X, const T* 
   __shared__ float sh[16];
   const int r = blockIdx.x, tid = threadIdx.x;
   const float* x = X + (size_t)r * d;
+  // this thread's weights of the first 4096 columns, loaded ahead of the reduction (loaded
+  // after it, each would wait behind the stores of the previous ones)
+  float g0[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) g0[j] = to_f(g[min(4 * tid + j, d - 1)]);
   float ss = 0.f;
   for (int c = 4 * tid; c < d; c += 4096) {
     const f32x4_t v = *(const f32x4_t*)(x + c);
@@ -272,7 +277,13 @@ __global__ __launch_bounds__(1024) void rmsnorm_kernel(const float* X, const T* 
   const float tot = block_sum_1024(ss, sh);
   const float denom = sqrtf(tot / (float)d + eps);
   T* y = Y + (size_t)r * d;
-  for (int c = 4 * tid; c < d; c += 4096) {
+  if (4 * tid < d) {
+    const int c = 4 * tid;
+    const f32x4_t v = *(const f32x4_t*)(x + c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[c + j] = from_f<T>((v[j] / denom) * g0[j]);
+  }
+  for (int c = 4 * tid + 4096; c < d; c += 4096) {
     const f32x4_t v = *(const f32x4_t*)(x + c);
 #pragma unroll
     for (int j = 0; j < 4; ++j) y[c + j] = from_f<T>((v[j] / denom) * to_f(g[c + j]));
